@@ -1,0 +1,163 @@
+"""Plain fp64 CPU oracle for the selective-SSM scan (ctypes over ssm_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the package smoke check
+and by the benchmark's CPU-baseline leg, never by the product path.  It shares
+no code with the HIP implementation; both sides receive the same seeded inputs
+from the `workloads` module.
+
+The arithmetic lives in ssm_oracle.c, which cites the passages it follows
+(page "Mamba 논문 리뷰: Selective State Space Models로 Transformer를 넘어서",
+sections 2.2, 3.1, 3.3 and 3.4).  This wrapper only widens inputs to fp64,
+lays them out densely and calls the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+import time
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_BUILD = os.path.join(_HERE, "_build")
+
+_dp = ctypes.POINTER(ctypes.c_double)
+
+
+class _Args(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+        ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+        ("x", _dp), ("delta", _dp), ("A", _dp), ("Bm", _dp), ("Cm", _dp),
+        ("Dskip", _dp), ("z", _dp), ("delta_bias", _dp), ("h0", _dp),
+        ("y", _dp), ("hT", _dp),
+    ]
+
+
+def lib_path(mutant: int = 0, out_dir: str | None = None) -> str:
+    d = out_dir or _BUILD
+    name = "liboracle.so" if mutant == 0 else f"liboracle_mutant{mutant}.so"
+    return os.path.join(d, name)
+
+
+def build(mutant: int = 0, out_dir: str | None = None) -> str:
+    """Compile the oracle with gcc (no fast-math: IEEE fp64 throughout)."""
+    out = lib_path(mutant, out_dir)
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-fno-fast-math",
+           "-ffp-contract=off", f"-DORACLE_MUTANT={int(mutant)}", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+class Oracle:
+    """Handle on one compiled oracle library (the real one, or a test mutant)."""
+
+    def __init__(self, path: str):
+        self.path = path
+        self._lib = ctypes.CDLL(path)
+        self._lib.oracle_scan_f64.argtypes = [ctypes.POINTER(_Args), ctypes.c_int]
+        self._lib.oracle_scan_f64.restype = ctypes.c_int
+        self._lib.oracle_assoc_scan_f64.argtypes = [ctypes.POINTER(_Args)]
+        self._lib.oracle_assoc_scan_f64.restype = ctypes.c_int
+        self._lib.oracle_softplus_vec.argtypes = [_dp, _dp, ctypes.c_int64]
+        self._lib.oracle_softplus_vec.restype = None
+        self._lib.oracle_mutant_id.restype = ctypes.c_int
+        self.mutant = self._lib.oracle_mutant_id()
+
+    # -- helpers -------------------------------------------------------------
+    @staticmethod
+    def _f64(a):
+        if a is None:
+            return None
+        if hasattr(a, "detach"):  # torch tensor (CPU): widen exactly
+            a = a.detach().cpu().to(dtype=__import__("torch").float64).numpy()
+        return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+    @staticmethod
+    def _ptr(a):
+        return None if a is None else a.ctypes.data_as(_dp)
+
+    def _pack(self, x, delta, A, B, C, D, z, delta_bias, h0, want_state):
+        x, delta, A, B, C = (self._f64(t) for t in (x, delta, A, B, C))
+        D, z, delta_bias, h0 = (self._f64(t) for t in (D, z, delta_bias, h0))
+        bsz, L, dim = x.shape
+        N = A.shape[1]
+        assert delta.shape == x.shape and A.shape == (dim, N)
+        assert B.shape == (bsz, L, N) and C.shape == (bsz, L, N)
+        assert D is None or D.shape == (dim,)
+        assert z is None or z.shape == x.shape
+        assert delta_bias is None or delta_bias.shape == (dim,)
+        assert h0 is None or h0.shape == (bsz, dim, N)
+        y = np.zeros((bsz, L, dim), dtype=np.float64)
+        hT = np.zeros((bsz, dim, N), dtype=np.float64) if want_state else None
+        keep = (x, delta, A, B, C, D, z, delta_bias, h0, y, hT)
+        args = _Args(bsz, L, dim, N, *(self._ptr(t) for t in keep))
+        return args, keep, y, hT
+
+    # -- entry points --------------------------------------------------------
+    def scan(self, x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
+             threads: int | None = None, timing: dict | None = None):
+        """Sequential fp64 scan.  Returns (y, hT) as float64 numpy arrays.
+        If `timing` is a dict, the wall time of the C call alone (inputs already
+        widened to fp64) and the thread count are stored in it."""
+        args, keep, y, hT = self._pack(x, delta, A, B, C, D, z, delta_bias, h0, True)
+        nt = threads if threads is not None else (os.cpu_count() or 1)
+        t0 = time.perf_counter()
+        rc = self._lib.oracle_scan_f64(ctypes.byref(args), int(nt))
+        t1 = time.perf_counter()
+        if rc != 0:
+            raise RuntimeError("oracle_scan_f64 failed")
+        if timing is not None:
+            timing["seconds"] = t1 - t0
+            timing["threads"] = int(nt)
+        del keep
+        return y, hT
+
+    def assoc_scan(self, x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None):
+        """Associative-scan twin (log-depth prefix over (a, b) pairs); small inputs."""
+        args, keep, y, hT = self._pack(x, delta, A, B, C, D, z, delta_bias, h0, True)
+        rc = self._lib.oracle_assoc_scan_f64(ctypes.byref(args))
+        if rc != 0:
+            raise RuntimeError("oracle_assoc_scan_f64 failed")
+        del keep
+        return y, hT
+
+    def softplus(self, v):
+        v = self._f64(v)
+        out = np.empty_like(v)
+        self._lib.oracle_softplus_vec(self._ptr(v), self._ptr(out), v.size)
+        return out
+
+
+_lock = threading.Lock()
+_default: Oracle | None = None
+
+
+def get(rebuild: bool = False) -> Oracle:
+    """The oracle, building it with gcc on first use if it is not built."""
+    global _default
+    with _lock:
+        if _default is None or rebuild:
+            path = lib_path()
+            if rebuild or not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+                build()
+            _default = Oracle(path)
+        return _default
+
+
+def scan(*args, **kw):
+    return get().scan(*args, **kw)
+
+
+def assoc_scan(*args, **kw):
+    return get().assoc_scan(*args, **kw)
+
+
+def softplus(v):
+    return get().softplus(v)

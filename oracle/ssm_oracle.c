@@ -1,0 +1,257 @@
+/*
+ * Plain fp64 CPU oracle for the Mamba selective-SSM scan forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the tests, the package's smoke check and the CPU
+ * baseline leg of the benchmark use it.  It shares no code, header, table or
+ * constant with the HIP implementation.
+ *
+ * What it computes (page "Mamba 논문 리뷰: Selective State Space Models로
+ * Transformer를 넘어서", youngju.dev):
+ *   - discretisation, section 2.2: Abar = exp(delta * A) per (d, n); the
+ *     input term is the Euler form delta * B * x that the section 3.3
+ *     selective_scan listing materialises as deltaB * x (the ZOH form of the
+ *     same section is not used; see the readings in the design notes);
+ *   - recurrence and readout, section 2.2: h_t = Abar h_{t-1} + Bbar x_t,
+ *     y_t = C h_t, with the state updated before it is read (section 3.3);
+ *   - selection, section 3.1: delta_t = softplus(raw delta + bias), B_t and
+ *     C_t given per token;
+ *   - block, section 3.4: skip term D * x and the SiLU(z) output gate
+ *     y <- y * z * sigmoid(z).
+ * Shapes follow the section 3.3 contract: x, delta, z are (B, L, D); A is
+ * (D, N); B and C are (B, L, N); D and delta_bias are (D); the state h0/hT is
+ * (B, D, N).  All arrays are dense row-major fp64 holding exactly the values
+ * the device receives (bf16/fp32 widened without rounding).
+ *
+ * Build-time mutations (ORACLE_MUTANT=k, k>0) exist only so the test suite
+ * can show that its closed-form pins catch plausible mistakes; the default
+ * build (k=0) is the oracle.
+ *
+ * Parity pins: every function here is pinned by closed forms in
+ * tests/test_oracle.py (softplus special values, A=0 cumulative sum,
+ * geometric series, L=1 by hand, brute-force unrolled sum, associative twin,
+ * chunk chaining, causality, linearity, gate and readout special cases).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+typedef struct {
+  int64_t batch, seqlen, dim, dstate;
+  const double *x, *delta, *A, *Bm, *Cm;
+  const double *Dskip;      /* NULL: no skip term   */
+  const double *z;          /* NULL: no gate        */
+  const double *delta_bias; /* NULL: zero bias      */
+  const double *h0;         /* NULL: zero state     */
+  double *y;                /* (B, L, D) out        */
+  double *hT;               /* NULL or (B, D, N)    */
+} oracle_args;
+
+/* softplus(v) = log(1 + e^v), written in the overflow-free form
+ * max(v, 0) + log1p(exp(-|v|)) (page youngju.dev, section 3.1). */
+double oracle_softplus(double v) {
+#if ORACLE_MUTANT == 1
+  return fmax(v, 0.0) + log1p(exp(-v)); /* |v| slip */
+#elif ORACLE_MUTANT == 2
+  return log(1.0 + exp(v)) * 0.999;                    /* scaled softplus */
+#else
+  return fmax(v, 0.0) + log1p(exp(-fabs(v)));
+#endif
+}
+
+/* z * sigmoid(z): the SiLU gate of the block (youngju.dev, section 3.4). */
+static double silu(double z) {
+#if ORACLE_MUTANT == 3
+  return 1.0 / (1.0 + exp(-z)); /* sigmoid instead of SiLU */
+#else
+  return z / (1.0 + exp(-z));
+#endif
+}
+
+/* One independent chain: batch row b, channel d, all N states, t = 0..L-1. */
+static void scan_channel(const oracle_args *a, int64_t b, int64_t d, double *h) {
+  const int64_t L = a->seqlen, D = a->dim, N = a->dstate;
+  for (int64_t n = 0; n < N; ++n) h[n] = a->h0 ? a->h0[(b * D + d) * N + n] : 0.0;
+#if ORACLE_MUTANT == 4
+  for (int64_t n = 0; n < N; ++n) h[n] = 0.0; /* initial state ignored */
+#endif
+  for (int64_t t = 0; t < L; ++t) {
+    const int64_t i = (b * L + t) * D + d; /* (b, t, d) */
+    const double *Bt = a->Bm + (b * L + t) * N;
+    const double *Ct = a->Cm + (b * L + t) * N;
+#if ORACLE_MUTANT == 5
+    const double v = a->delta[i]; /* bias dropped */
+#else
+    const double v = a->delta[i] + (a->delta_bias ? a->delta_bias[d] : 0.0);
+#endif
+    const double dt = oracle_softplus(v);
+#if ORACLE_MUTANT == 13
+    const double xt = a->x[(b * D + d) * L + t]; /* x read as (B, D, L) */
+#else
+    const double xt = a->x[i];
+#endif
+#if ORACLE_MUTANT == 6
+    double yv = 0.0; /* readout before the update */
+    for (int64_t n = 0; n < N; ++n) yv += Ct[n] * h[n];
+#endif
+    for (int64_t n = 0; n < N; ++n) {
+#if ORACLE_MUTANT == 7
+      const double abar = exp(-dt * a->A[d * N + n]); /* wrong sign of A */
+#elif ORACLE_MUTANT == 8
+      const double abar = exp(dt * a->A[d * N + (N - 1 - n)]); /* A row reversed */
+#else
+      const double abar = exp(dt * a->A[d * N + n]);
+#endif
+#if ORACLE_MUTANT == 9
+      const double bx = dt * Ct[n] * xt; /* B and C swapped */
+#elif ORACLE_MUTANT == 10
+      const double bx = Bt[n] * xt; /* delta missing from the input term */
+#else
+      const double bx = dt * Bt[n] * xt;
+#endif
+      h[n] = abar * h[n] + bx;
+    }
+#if ORACLE_MUTANT != 6
+    double yv = 0.0;
+#if ORACLE_MUTANT == 9
+    for (int64_t n = 0; n < N; ++n) yv += Bt[n] * h[n];
+#elif ORACLE_MUTANT == 14
+    for (int64_t n = 0; n + 1 < N; ++n) yv += Ct[n] * h[n]; /* last state not read out */
+#else
+    for (int64_t n = 0; n < N; ++n) yv += Ct[n] * h[n];
+#endif
+#endif
+#if ORACLE_MUTANT == 11
+    if (a->Dskip) yv += a->Dskip[d]; /* skip term without x */
+#else
+    if (a->Dskip) yv += a->Dskip[d] * xt;
+#endif
+#if ORACLE_MUTANT == 12
+    if (a->z) yv += silu(a->z[i]); /* gate added, not multiplied */
+#else
+    if (a->z) yv *= silu(a->z[i]);
+#endif
+    a->y[i] = yv;
+  }
+  if (a->hT)
+    for (int64_t n = 0; n < N; ++n) a->hT[(b * D + d) * N + n] = h[n];
+}
+
+typedef struct {
+  const oracle_args *a;
+  int64_t first, last; /* chain range [first, last) over b * D + d */
+  int status;
+} worker_t;
+
+static void *worker(void *p) {
+  worker_t *w = (worker_t *)p;
+  double *h = (double *)malloc(sizeof(double) * (size_t)w->a->dstate);
+  if (!h) { w->status = -1; return NULL; }
+  for (int64_t c = w->first; c < w->last; ++c) scan_channel(w->a, c / w->a->dim, c % w->a->dim, h);
+  free(h);
+  w->status = 0;
+  return NULL;
+}
+
+/* Sequential-in-time fp64 scan.  Chains (b, d) are independent, so they are
+ * spread over `nthreads` POSIX threads; each chain is still one plain loop
+ * over t in increasing order and over n in increasing order.
+ * Returns 0, or -1 on bad arguments / allocation failure. */
+int oracle_scan_f64(const oracle_args *a, int nthreads) {
+  if (!a || !a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->y) return -1;
+  if (a->batch < 0 || a->seqlen < 0 || a->dim < 0 || a->dstate <= 0) return -1;
+  const int64_t chains = a->batch * a->dim;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if (chains < nthreads) nthreads = chains > 0 ? (int)chains : 1;
+  worker_t ws[256];
+  pthread_t th[256];
+  int started = 0, rc = 0;
+  for (int k = 0; k < nthreads; ++k) {
+    ws[k].a = a;
+    ws[k].first = chains * k / nthreads;
+    ws[k].last = chains * (k + 1) / nthreads;
+    ws[k].status = 0;
+  }
+  for (int k = 1; k < nthreads; ++k) {
+    if (pthread_create(&th[k], NULL, worker, &ws[k]) != 0) { rc = -1; break; }
+    started = k;
+  }
+  worker(&ws[0]);
+  for (int k = 1; k <= started; ++k) pthread_join(th[k], NULL);
+  if (rc) {
+    /* run any chains whose thread could not be started on this thread */
+    for (int k = started + 1; k < nthreads; ++k) worker(&ws[k]);
+  }
+  for (int k = 0; k < nthreads; ++k)
+    if (ws[k].status) return -1;
+  return 0;
+}
+
+/* The same result through the parallel associative scan the explainer page
+ * (allinfo.ai.kr, "쉽게 이해하기" and key insights) names for selective SSMs.
+ * The operator is not printed on the pages; it follows from the recurrence:
+ * the step h -> a h + b composes as (a1, b1) then (a2, b2) = (a1 a2, a2 b1 + b2).
+ * Per chain (b, d, n) this builds the (a_t, b_t) sequence, runs a log-depth
+ * inclusive Hillis-Steele scan with that operator, applies the prefix to h0,
+ * and reads out.  Single-threaded, O(L log L) per chain: small inputs only. */
+int oracle_assoc_scan_f64(const oracle_args *a) {
+  if (!a || !a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->y) return -1;
+  const int64_t Bn = a->batch, L = a->seqlen, D = a->dim, N = a->dstate;
+  double *pa = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+  double *pb = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+  double *qa = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+  double *qb = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+  double *hs = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * (size_t)N);
+  if (!pa || !pb || !qa || !qb || !hs) { free(pa); free(pb); free(qa); free(qb); free(hs); return -1; }
+  for (int64_t b = 0; b < Bn; ++b)
+    for (int64_t d = 0; d < D; ++d) {
+      for (int64_t n = 0; n < N; ++n) {
+        for (int64_t t = 0; t < L; ++t) {
+          const int64_t i = (b * L + t) * D + d;
+          const double dt = oracle_softplus(a->delta[i] + (a->delta_bias ? a->delta_bias[d] : 0.0));
+          pa[t] = exp(dt * a->A[d * N + n]);
+          pb[t] = dt * a->Bm[(b * L + t) * N + n] * a->x[i];
+        }
+        for (int64_t off = 1; off < L; off <<= 1) {
+          for (int64_t t = 0; t < L; ++t) {
+            if (t >= off) { /* (pa[t-off], pb[t-off]) then (pa[t], pb[t]) */
+              qa[t] = pa[t - off] * pa[t];
+              qb[t] = pa[t] * pb[t - off] + pb[t];
+            } else {
+              qa[t] = pa[t];
+              qb[t] = pb[t];
+            }
+          }
+          memcpy(pa, qa, sizeof(double) * (size_t)L);
+          memcpy(pb, qb, sizeof(double) * (size_t)L);
+        }
+        const double h0 = a->h0 ? a->h0[(b * D + d) * N + n] : 0.0;
+        for (int64_t t = 0; t < L; ++t) hs[t * N + n] = pa[t] * h0 + pb[t];
+        if (a->hT) a->hT[(b * D + d) * N + n] = L > 0 ? hs[(L - 1) * N + n] : h0;
+      }
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t i = (b * L + t) * D + d;
+        double yv = 0.0;
+        for (int64_t n = 0; n < N; ++n) yv += a->Cm[(b * L + t) * N + n] * hs[t * N + n];
+        if (a->Dskip) yv += a->Dskip[d] * a->x[i];
+        if (a->z) yv *= a->z[i] / (1.0 + exp(-a->z[i]));
+        a->y[i] = yv;
+      }
+    }
+  free(pa); free(pb); free(qa); free(qb); free(hs);
+  return 0;
+}
+
+/* Elementwise softplus over an array (used by the pins on its own). */
+void oracle_softplus_vec(const double *v, double *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_softplus(v[i]);
+}
+
+int oracle_mutant_id(void) { return ORACLE_MUTANT; }

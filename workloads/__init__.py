@@ -1,0 +1,162 @@
+"""Seeded synthetic inputs for the selective-scan workloads, and the error metric.
+
+This module is shared by the oracle side and the HIP side of every test and
+benchmark.  It holds input recipes only (shapes, distributions, seeds) and the
+comparison metric; none of the scan's arithmetic lives here.
+
+Recipe (the five workloads; every tensor is synthetic, no dataset or weights):
+  * x, z, B, C, raw delta ~ N(0, 1);
+  * delta_bias[d] = softplus^-1(u) = log(expm1(u)), u log-uniform on [1e-3, 1e-1],
+    so softplus(raw + bias) starts around u;
+  * A[d, n] = -(n + 1) (the S4D-real diagonal of the Mamba block, page
+    youngju.dev section 3.4: A = -exp(A_log), A_log = log(1..N));
+  * D = 1, or D ~ N(1, 0.1) where noted; h0 = 0, or ~ N(0, 0.1) for decode;
+  * bf16 tensors are fp32 draws rounded to nearest-even by torch.
+Seeds: numpy PCG64 seeded from SeedSequence([20261203, workload_index, *extra]),
+one spawned stream per tensor in the fixed order x, delta, B, C, z, u, D, h0.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+ROOT_SEED = 20261203
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    index: int
+    name: str
+    batch: int
+    seqlen: int
+    dim: int
+    dstate: int
+    dtype: torch.dtype
+    gate: bool
+    d_noise: bool          # D ~ N(1, 0.1) instead of ones
+    final_state: bool      # the workload asks for hT
+    chunks: int = 1        # run as `chunks` calls passing the state along
+    steps: int = 0         # decode: number of successive L=1 steps (0 = not decode)
+    h0_std: float = 0.0    # decode: initial state ~ N(0, h0_std)
+
+    @property
+    def elems(self) -> int:
+        """B*L*D*N scan elements of the whole workload."""
+        L = self.steps if self.steps else self.seqlen
+        return self.batch * L * self.dim * self.dstate
+
+    def describe(self) -> str:
+        return (f"{self.name}: B={self.batch} L={self.seqlen} D={self.dim} N={self.dstate} "
+                f"{str(self.dtype).replace('torch.', '')} gate={self.gate}"
+                + (f" chunks={self.chunks}" if self.chunks > 1 else "")
+                + (f" steps={self.steps}" if self.steps else ""))
+
+
+WORKLOADS = [
+    Workload(0, "tiny_fp32_B1_L256_D64_N16", 1, 256, 64, 16, torch.float32,
+             gate=False, d_noise=False, final_state=True),
+    Workload(1, "mamba130m_B8_L2048_D1536_N16", 8, 2048, 1536, 16, torch.bfloat16,
+             gate=True, d_noise=False, final_state=True),
+    Workload(2, "mamba1p4b_B4_L8192_D4096_N16", 4, 8192, 4096, 16, torch.bfloat16,
+             gate=True, d_noise=True, final_state=True),
+    Workload(3, "longctx_B1_L262144_D1536_N16", 1, 262144, 1536, 16, torch.bfloat16,
+             gate=True, d_noise=False, final_state=True, chunks=32),
+    Workload(4, "decode_B256_D5120_N16_x128", 256, 1, 5120, 16, torch.bfloat16,
+             gate=True, d_noise=True, final_state=True, steps=128, h0_std=0.1),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def _streams(index: int, extra=()):
+    ss = np.random.SeedSequence([ROOT_SEED, int(index), *[int(e) for e in extra]])
+    return [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(8)]
+
+
+def _cast(a: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dtype)
+
+
+def make_params(w: Workload, dim: int | None = None, dstate: int | None = None, *,
+                seed_extra=()):
+    """Per-channel parameters: A (D,N), D (D), delta_bias (D), all fp32."""
+    dim = dim or w.dim
+    N = dstate or w.dstate
+    g = _streams(w.index, seed_extra)
+    u = np.exp(g[5].uniform(math.log(1e-3), math.log(1e-1), size=dim))
+    bias = np.log(np.expm1(u))
+    A = -np.tile(np.arange(1, N + 1, dtype=np.float64), (dim, 1))
+    Dsk = g[6].normal(1.0, 0.1, size=dim) if w.d_noise else np.ones(dim)
+    return {
+        "A": torch.from_numpy(A.astype(np.float32)),
+        "D": torch.from_numpy(Dsk.astype(np.float32)),
+        "delta_bias": torch.from_numpy(bias.astype(np.float32)),
+    }
+
+
+def make_inputs(w: Workload, *, batch: int | None = None, seqlen: int | None = None,
+                dim: int | None = None, dstate: int | None = None, seed_extra=()):
+    """Seeded CPU tensors for one call of the workload (optionally resized).
+
+    Returns a dict with x, delta, B, C, z (or None), A, D, delta_bias, h0 (or None).
+    """
+    bsz = batch or w.batch
+    L = seqlen or (1 if w.steps else w.seqlen)
+    dim = dim or w.dim
+    N = dstate or w.dstate
+    g = _streams(w.index, seed_extra)
+    f32 = np.float32
+    x = g[0].standard_normal((bsz, L, dim), dtype=f32)
+    delta = g[1].standard_normal((bsz, L, dim), dtype=f32)
+    Bm = g[2].standard_normal((bsz, L, N), dtype=f32)
+    Cm = g[3].standard_normal((bsz, L, N), dtype=f32)
+    z = g[4].standard_normal((bsz, L, dim), dtype=f32) if w.gate else None
+    h0 = None
+    if w.h0_std > 0:
+        h0 = torch.from_numpy((g[7].standard_normal((bsz, dim, N)) * w.h0_std).astype(f32))
+    out = {
+        "x": _cast(x, w.dtype), "delta": _cast(delta, w.dtype),
+        "B": _cast(Bm, w.dtype), "C": _cast(Cm, w.dtype),
+        "z": _cast(z, w.dtype) if z is not None else None,
+        "h0": h0,
+    }
+    out.update(make_params(w, dim, N, seed_extra=seed_extra))
+    return out
+
+
+def make_decode_step(w: Workload, step: int, *, batch: int | None = None, dim: int | None = None):
+    """Fresh per-step tensors (x, delta, B, C, z) of a decode workload, L = 1."""
+    bsz = batch or w.batch
+    dim = dim or w.dim
+    N = w.dstate
+    g = _streams(w.index, (1000 + int(step),))
+    f32 = np.float32
+    return {
+        "x": _cast(g[0].standard_normal((bsz, 1, dim), dtype=f32), w.dtype),
+        "delta": _cast(g[1].standard_normal((bsz, 1, dim), dtype=f32), w.dtype),
+        "B": _cast(g[2].standard_normal((bsz, 1, N), dtype=f32), w.dtype),
+        "C": _cast(g[3].standard_normal((bsz, 1, N), dtype=f32), w.dtype),
+        "z": _cast(g[4].standard_normal((bsz, 1, dim), dtype=f32), w.dtype) if w.gate else None,
+    }
+
+
+def tolerance(dtype: torch.dtype) -> float:
+    """Max floored relative error allowed: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs."""
+    return 1e-4 if dtype == torch.float32 else 2e-2
+
+
+def rel_err(got, ref) -> float:
+    """max_i |g_i - r_i| / max(|r_i|, rms(r)): relative error floored at the RMS of the
+    reference so that entries near zero do not blow it up."""
+    g = np.asarray(got, dtype=np.float64).ravel()
+    r = np.asarray(ref, dtype=np.float64).ravel()
+    if r.size == 0:
+        return 0.0
+    rms = math.sqrt(float(np.mean(r * r)))
+    den = np.maximum(np.abs(r), rms if rms > 0 else 1e-300)
+    e = np.abs(g - r) / den
+    if not np.all(np.isfinite(g)):
+        return math.inf
+    return float(np.max(e))
