@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Throughput of the selective-SSM scan forward pass on one MI355X.
+
+One step = one ssm_scan_fwd over the Mamba-1.4B-shaped layer (B=4, L=8192,
+D=4096, N=16, bf16 x/delta/z/B/C/y, fp32 state, SiLU gate, final state
+returned), inputs resident in HBM.  Prints one JSON line on stdout.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+The metric is scan elements per second, B*L*D*N / step time, in GElem/s.  The
+roofline object reports the algorithmic HBM bytes of one launch (every input
+read once, y and hT written once) over the launch's average duration, timed
+with HIP events on the stream the kernel runs on, against the MI355X peak of
+8 TB/s.  The CPU baseline times the fp64 oracle on a bounded slice of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w) -> int:
+    """Bytes one call must move at minimum: x, delta, z read and y written
+    (B,L,D each), B and C read (B,L,N), A (D,N), D and delta_bias (D) read,
+    h0 read / hT written (B,D,N fp32) where the workload uses them."""
+    es = 2 if "bfloat16" in str(w.dtype) else 4
+    L = w.seqlen if not w.steps else 1
+    bld = w.batch * L * w.dim
+    bln = w.batch * L * w.dstate
+    n = (3 if w.gate else 2) * bld * es + bld * es  # x, delta, (z) in; y out
+    n += 2 * bln * es + w.dim * w.dstate * 4 + 2 * w.dim * 4
+    if w.final_state:
+        n += w.batch * w.dim * w.dstate * 4
+    if w.h0_std > 0:
+        n += w.batch * w.dim * w.dstate * 4
+    return n
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources, so stored traffic counters can be matched to
+    the kernel build they were measured on."""
+    csrc = os.path.join(HERE, "mamba_selective_scan_06_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(HERE, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, max_threads=16):
+    """The fp64 oracle on all batch rows and the first D/4 channels of the
+    workload (full sequence), threaded over independent channels."""
+    import oracle
+    import torch
+    dsub = max(1, w.dim // 4)
+    sub = {k: v for k, v in inp.items()}
+    for k in ("x", "delta", "z"):
+        if sub[k] is not None:
+            sub[k] = sub[k][:, :, :dsub].contiguous()
+    for k in ("D", "delta_bias"):
+        sub[k] = sub[k][:dsub].contiguous()
+    sub["A"] = sub["A"][:dsub].contiguous()
+    if sub.get("h0") is not None:
+        sub["h0"] = sub["h0"][:, :dsub].contiguous()
+    threads = max(1, min(os.cpu_count() or 1, max_threads))
+    timing = {}
+    oracle.scan(sub["x"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"], sub["delta_bias"],
+                sub.get("h0"), threads=threads, timing=timing)
+    elems = w.batch * w.seqlen * dsub * w.dstate
+    del torch
+    return {
+        "value": round(elems / timing["seconds"] / 1e9, 4),
+        "unit": "GElem/s",
+        "cores": timing["threads"],
+        "kind": "oracle",
+        "sample": f"B={w.batch} L={w.seqlen} D={dsub} (channels 0..{dsub - 1}) N={w.dstate}, "
+                  f"{elems} elements, {timing['seconds']:.2f} s fp64 on {timing['threads']} threads",
+    }
+
+
+def main():
+    import workloads
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=workloads.WORKLOADS[2].name, choices=list(workloads.BY_NAME))
+    ap.add_argument("--variant", default="auto")
+    ap.add_argument("--time-splits", type=int, default=0)
+    ap.add_argument("--generic-a", action="store_true", help="never take the structured-decay path")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the scan shards by batch or "
+              "channel with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mamba_selective_scan_06_amd as ssm
+
+    w = workloads.BY_NAME[args.workload]
+    if w.steps or w.chunks > 1:
+        print("bench.py times single-call workloads; the chunked and decode workloads are parity cases",
+              file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    log(f"workload {w.describe()}")
+    t0 = time.time()
+    inp = workloads.make_inputs(w)
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+    d1 = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+    # a second copy of the token tensors: alternating between the two keeps the
+    # previous step's inputs out of the 256 MB last-level cache
+    d2 = dict(d1)
+    for k in ("x", "delta", "z", "B", "C"):
+        if d1[k] is not None:
+            d2[k] = d1[k].clone()
+    sets = [d1, d2]
+    y = [torch.empty_like(d1["x"]) for _ in sets]
+    hT = [torch.empty(w.batch, w.dim, w.dstate, dtype=torch.float32, device=dev) for _ in sets]
+    a0 = ssm.make_args(d1["x"], d1["delta"], d1["A"], d1["B"], d1["C"], d1["D"], d1["z"], d1["delta_bias"],
+                       d1["h0"], hT[0], y[0], None, args.variant, args.time_splits, args.generic_a)
+    nbytes = ssm.workspace_bytes(a0)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
+    a0.workspace = None if ws is None else ws.data_ptr()
+    a0.workspace_bytes = nbytes
+    plan = ssm.plan(a0)
+    log(f"plan {plan}, workspace {nbytes} B")
+
+    def step(i):
+        s = sets[i % 2]
+        ssm.scan_fwd(s["x"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], s["delta_bias"], s["h0"],
+                     out=y[i % 2], final_state_out=hT[i % 2], workspace=ws, variant=args.variant,
+                     time_splits=args.time_splits, generic_a=args.generic_a)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    log(f"timed {args.steps} steps in {elapsed * 1e3:.2f} ms; per-launch ms median {np.median(kern_ms):.4f}")
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    elems = w.elems
+    value = elems / (ms_per_step * 1e-3) / 1e9
+    kern_avg_s = float(np.mean(kern_ms)) * 1e-3
+    alg = algorithmic_bytes(w)
+    achieved = alg / kern_avg_s / 1e9
+    traffic = stored_traffic(w.name)
+    out = {
+        "metric": "scan GElem/s (B*L*D*N) + % HBM roofline, B4 L8192 D4096 N16 bf16",
+        "value": round(value, 2),
+        "unit": "GElem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
+            "io_dtype": str(w.dtype).replace("torch.", ""), "gate": w.gate, "final_state": w.final_state,
+            "plan": {"variant": plan[0], "time_splits": plan[1], "generic_a": args.generic_a},
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "scan_nsplit_kernel" if plan[0] == "nsplit" else f"scan_{plan[0]}_kernel",
+            "kernel_avg_us": round(kern_avg_s * 1e6, 2),
+            "algorithmic_bytes": alg,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+        log(f"cpu baseline {out['cpu_baseline']['value']} GElem/s on {out['cpu_baseline']['cores']} threads")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,121 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective-SSM scan library.
+ *
+ * The operation (page "Mamba 논문 리뷰: Selective State Space Models로
+ * Transformer를 넘어서", youngju.dev):
+ *   section 3.1  delta_t = softplus(raw_delta_t + delta_bias)   (selection)
+ *   section 2.2  Abar = exp(delta A)                            (discretisation)
+ *   section 3.3  Bbar x = delta B_t x_t  (Euler input term of the listing)
+ *   section 2.2  h_t = Abar o h_{t-1} + Bbar x_t, y_t = C_t . h_t
+ *   section 3.4  y_t += D x_t, then y_t *= SiLU(z_t)             (block)
+ * per batch row b, channel d and state n, with a diagonal fp32 state of size N
+ * per channel.  Tensor contract of the section 3.3 listing: x, delta (B, L, D);
+ * A (D, N); B, C (B, L, N); plus D, z and delta_bias of the block.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; every tensor
+ *     is dense, row-major, with the last index fastest.  The library never
+ *     allocates, frees or retains them, and keeps no global mutable state.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without synchronising.  Argument errors are detected on
+ *     the host before any HIP call and nothing is enqueued; faults during
+ *     execution surface at the caller's next synchronisation.
+ *   - Return value: SSM_OK (0) or a negative SSM_ERR_* code.
+ */
+#ifndef SSM_SCAN_H_
+#define SSM_SCAN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_SCAN_ABI_VERSION 1
+
+/* Element type of x, delta, B, C, z and y.  A, D, delta_bias, h0, hT are
+ * always fp32, and all arithmetic (state, accumulation) is fp32. */
+typedef enum ssm_dtype { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype;
+
+enum ssm_status {
+  SSM_OK = 0,
+  SSM_ERR_NULL = -1,      /* a required pointer (args, x, delta, A, B, C, y) is NULL      */
+  SSM_ERR_SHAPE = -2,     /* an extent is negative, or an element count overflows int64   */
+  SSM_ERR_DSTATE = -3,    /* dstate N outside 1..64                                       */
+  SSM_ERR_DTYPE = -4,     /* dtype not one of ssm_dtype                                   */
+  SSM_ERR_ALIGN = -5,     /* a tensor base address is not 16-byte aligned                 */
+  SSM_ERR_ALIAS = -6,     /* y overlaps an input, or hT overlaps an input other than h0   */
+  SSM_ERR_WORKSPACE = -7, /* time_splits > 1 asked for but workspace is NULL or too small */
+  SSM_ERR_LAUNCH = -8,    /* the HIP launch failed (hipGetLastError after the launch)     */
+  SSM_ERR_VARIANT = -9,   /* variant / flags / time_splits not valid for this problem     */
+};
+
+/* Kernel family (SSM_VARIANT_AUTO picks one from the problem shape). */
+enum ssm_variant {
+  SSM_VARIANT_AUTO = 0,
+  SSM_VARIANT_NSPLIT = 1, /* 4 waves share 64 channels, each wave owns N/4 states (N % 4 == 0) */
+  SSM_VARIANT_LANE = 2,   /* one lane owns one channel and all N states; any N <= 64           */
+  SSM_VARIANT_DECODE = 3, /* seqlen == 1 only: N/4 lanes per channel (N % 4 == 0)              */
+};
+
+/* Option bits. */
+enum ssm_flags {
+  /* Never take the structured-A fast path (decay of state n computed as the
+   * (n+1)-th power of the decay of state 0 when A[d,n] == (n+1) A[d,0] holds
+   * exactly for a channel block); every Abar is then its own exp. */
+  SSM_FLAG_GENERIC_A = 1,
+};
+
+typedef struct ssm_scan_args {
+  int64_t batch;   /* B >= 0                                                     */
+  int64_t seqlen;  /* L >= 0                                                     */
+  int64_t dim;     /* D >= 0: channels                                           */
+  int64_t dstate;  /* N, 1..64                                                   */
+  int32_t dtype;   /* ssm_dtype of x, delta, B, C, z, y                          */
+  int32_t flags;   /* ssm_flags bits                                             */
+  const void *x;           /* (B, L, D) input                          required */
+  const void *delta;       /* (B, L, D) raw step size, before bias and softplus, required */
+  const float *A;          /* (D, N) fp32, used as given (normally < 0)        required */
+  const void *B;           /* (B, L, N) input matrix per token                 required */
+  const void *C;           /* (B, L, N) output matrix per token                required */
+  const float *D;          /* (D) skip weight; NULL = no skip term                     */
+  const void *z;           /* (B, L, D) gate input; NULL = no gate                     */
+  const float *delta_bias; /* (D); NULL = zero bias                                    */
+  const float *h0;         /* (B, D, N) initial state; NULL = zeros                    */
+  float *hT;               /* (B, D, N) final state out; NULL = not returned; may equal h0 (in place) */
+  void *y;                 /* (B, L, D) output, same dtype as x                required */
+  void *workspace;         /* device scratch for time splitting; may be NULL           */
+  int64_t workspace_bytes; /* size of workspace in bytes                               */
+  int32_t variant;         /* ssm_variant; 0 = automatic                               */
+  int32_t time_splits;     /* segments per sequence: 0 = automatic, 1 = none, >1 = that many (NSPLIT only) */
+} ssm_scan_args;
+
+/* Forward selective scan, y (and optionally hT) from the inputs above.
+ * With seqlen == 0, y is empty and hT (if given) receives h0 (or zeros).
+ * With batch == 0 or dim == 0 there is nothing to compute and SSM_OK is
+ * returned.  When time splitting is used (automatic or requested), segment
+ * summaries go to `workspace`; with automatic splitting and no (or too small)
+ * workspace the call runs unsplit instead.  Deterministic: the same inputs
+ * give bitwise the same outputs. */
+int ssm_scan_fwd(const ssm_scan_args *args, void *stream);
+
+/* Bytes of workspace ssm_scan_fwd would use for these arguments with a
+ * workspace available (0 if the chosen path needs none).  Host-only; makes no
+ * HIP call.  Returns a negative SSM_ERR_* code for invalid arguments. */
+int64_t ssm_scan_workspace_bytes(const ssm_scan_args *args);
+
+/* The kernel family and number of time segments ssm_scan_fwd would use, as
+ * variant * 65536 + time_splits.  Host-only.  Negative on invalid arguments. */
+int64_t ssm_scan_plan(const ssm_scan_args *args);
+
+/* Static, human-readable text for a status code. */
+const char *ssm_scan_strerror(int code);
+
+/* SSM_SCAN_ABI_VERSION of the loaded library. */
+int ssm_scan_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H_ */

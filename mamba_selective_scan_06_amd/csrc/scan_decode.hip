@@ -1,0 +1,114 @@
+// DECODE family (seqlen == 1): one recurrent step per (b, d), the O(1)-per-token
+// inference update of the fixed-size state (page youngju.dev "Mamba 논문 리뷰",
+// section 6 comparison table; recurrence of section 2.2).
+//
+// The step is bound by the state traffic (read h0, write hT: 8 bytes per
+// state against ~0.3 bytes of token input), so the layout is chosen for
+// perfectly coalesced 16-byte state accesses: Q = N/4 consecutive lanes share
+// one channel and each owns 4 consecutive states (one float4 of h0/hT/A).  The
+// per-channel scalars (softplus, gate) are recomputed by the Q lanes of a
+// channel; the readout sum over n is reduced across them with lane shuffles.
+// h0 and hT may be the same buffer: every lane reads its own states before
+// writing them.
+#include "device_common.hpp"
+#include "scan_internal.hpp"
+
+namespace ssm {
+namespace {
+
+template <typename S>
+__device__ __forceinline__ void load4(const S* p, float out[4]);
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, float out[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+}
+template <>
+__device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float out[4]) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  out[0] = __uint_as_float(v.x << 16); out[1] = __uint_as_float(v.x & 0xffff0000u);
+  out[2] = __uint_as_float(v.y << 16); out[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
+template <typename S, int Q>
+__global__ __launch_bounds__(256) void scan_decode_kernel(
+    const S* __restrict__ x, const S* __restrict__ dl, const float* __restrict__ A,
+    const S* __restrict__ Bm, const S* __restrict__ Cm, const float* __restrict__ Dsk,
+    const S* __restrict__ z, const float* __restrict__ bias, const float* h0, float* hT,
+    S* __restrict__ y, int64_t D) {
+  constexpr int N = 4 * Q;
+  constexpr int CH = 256 / Q;  // channels per block
+  const int64_t b = blockIdx.y;
+  const int q = threadIdx.x % Q;
+  const int64_t dq = static_cast<int64_t>(blockIdx.x) * CH + threadIdx.x / Q;
+  const bool active = dq < D;
+  const int64_t d = active ? dq : D - 1;  // inactive lanes read a valid channel, write nothing
+  const int64_t i = b * D + d;              // (b, t=0, d) and (b, d) share this index
+
+  const float xv = to_f32(x[i]);
+  const float dt = softplus_f32(to_f32(dl[i]) + (bias ? bias[d] : 0.0f));
+  const float u = dt * xv;
+
+  float a[4], hv[4], Bv[4], Cv[4];
+  {
+    const float4 av = *reinterpret_cast<const float4*>(A + d * N + 4 * q);
+    a[0] = av.x; a[1] = av.y; a[2] = av.z; a[3] = av.w;
+  }
+  if (h0) {
+    const float4 hv4 = *reinterpret_cast<const float4*>(h0 + i * N + 4 * q);
+    hv[0] = hv4.x; hv[1] = hv4.y; hv[2] = hv4.z; hv[3] = hv4.w;
+  } else {
+    hv[0] = hv[1] = hv[2] = hv[3] = 0.0f;
+  }
+  load4<S>(Bm + b * N + 4 * q, Bv);
+  load4<S>(Cm + b * N + 4 * q, Cv);
+  float acc = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float ab = fast_exp2(dt * (a[k] * kLog2e));
+    hv[k] = __builtin_fmaf(ab, hv[k], u * Bv[k]);
+    acc = __builtin_fmaf(Cv[k], hv[k], acc);
+  }
+  // Sum the Q partial readouts of this channel (lanes q = 0..Q-1 are adjacent).
+#pragma unroll
+  for (int off = 1; off < Q; off <<= 1) acc += __shfl_xor(acc, off, 64);
+  if (active) {
+    if (hT) *reinterpret_cast<float4*>(hT + i * N + 4 * q) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+    if (q == 0) {
+      if (Dsk) acc = __builtin_fmaf(Dsk[d], xv, acc);
+      if (z) acc *= silu_f32(to_f32(z[i]));
+      store_elem(y + i, acc);
+    }
+  }
+}
+
+template <typename S, int Q>
+hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
+  constexpr int CH = 256 / Q;
+  dim3 grid(static_cast<unsigned>((p.dim + CH - 1) / CH), static_cast<unsigned>(p.batch));
+  hipLaunchKernelGGL((scan_decode_kernel<S, Q>), grid, dim3(256), 0, stream,
+                     static_cast<const S*>(p.x), static_cast<const S*>(p.delta), p.A,
+                     static_cast<const S*>(p.B), static_cast<const S*>(p.C), p.D,
+                     static_cast<const S*>(p.z), p.delta_bias, p.h0, p.hT, static_cast<S*>(p.y), p.dim);
+  return hipGetLastError();
+}
+
+template <typename S>
+hipError_t launch_decode_s(const Problem& p, hipStream_t stream) {
+  switch (p.dstate) {
+    case 4: return launch_decode_t<S, 1>(p, stream);
+    case 8: return launch_decode_t<S, 2>(p, stream);
+    case 16: return launch_decode_t<S, 4>(p, stream);
+    case 32: return launch_decode_t<S, 8>(p, stream);
+    case 64: return launch_decode_t<S, 16>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const Problem& p, hipStream_t stream) {
+  return p.dtype == 0 ? launch_decode_s<float>(p, stream) : launch_decode_s<uint16_t>(p, stream);
+}
+
+}  // namespace ssm

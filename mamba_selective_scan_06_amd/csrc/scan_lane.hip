@@ -1,0 +1,114 @@
+// LANE family: one lane owns one channel (b, d) and all N of its states in
+// fp32 registers, and walks t = 0..L-1 in order.  Every decay is its own exp
+// (no assumption on A).  B_t and C_t are the same for the 64 channels of a
+// wave, so they are read through the scalar unit (s_load into SGPRs) and
+// broadcast to the vector ALU for free.
+//
+// Per token and channel (page youngju.dev "Mamba 논문 리뷰"):
+//   delta = softplus(raw + bias)                       section 3.1
+//   h_n  <- exp(delta A[d,n]) h_n + (delta x) B_t[n]   sections 2.2 and 3.3
+//   y     = sum_n C_t[n] h_n + D[d] x                  sections 2.2 and 3.4
+//   y    *= SiLU(z)                                    section 3.4
+#include "device_common.hpp"
+#include "scan_internal.hpp"
+
+namespace ssm {
+namespace {
+
+template <typename S, int NMAX>
+__global__ __launch_bounds__(64) void scan_lane_kernel(
+    const S* __restrict__ x, const S* __restrict__ dl, const float* __restrict__ A,
+    const S* __restrict__ Bm, const S* __restrict__ Cm, const float* __restrict__ Dsk,
+    const S* __restrict__ z, const float* __restrict__ bias, const float* h0, float* hT,
+    S* __restrict__ y, int64_t L, int64_t D, int N) {
+  const int64_t b = blockIdx.y;
+  const int64_t d0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int lane = threadIdx.x;
+  const bool active = d0 + lane < D;
+  // Inactive lanes read channel D-1 (always valid) and never write.
+  const uint32_t lo = active ? lane : static_cast<uint32_t>(D - 1 - d0);
+  const int64_t d = d0 + lo;
+
+  float A2[NMAX], h[NMAX];
+#pragma unroll
+  for (int n = 0; n < NMAX; ++n) {
+    if (n < N) {
+      A2[n] = A[d * N + n] * kLog2e;
+      h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0f;
+    } else {
+      A2[n] = 0.0f;
+      h[n] = 0.0f;
+    }
+  }
+  const float bs = bias ? bias[d] : 0.0f;
+  const float Dd = Dsk ? Dsk[d] : 0.0f;
+  const bool has_d = Dsk != nullptr;
+  const bool has_z = z != nullptr;
+
+  for (int64_t t = 0; t < L; ++t) {
+    const int64_t row = (b * L + t) * D + d0;  // wave-uniform base of (b, t, d0)
+    const float xv = to_f32(x[row + lo]);
+    const float dt = softplus_f32(to_f32(dl[row + lo]) + bs);
+    const float u = dt * xv;
+    const S* Bt = Bm + (b * L + t) * N;  // wave-uniform
+    const S* Ct = Cm + (b * L + t) * N;
+    float acc = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NMAX; ++n) {
+      if (n < N) {
+        const float a = fast_exp2(dt * A2[n]);
+        h[n] = __builtin_fmaf(a, h[n], u * to_f32(Bt[n]));
+        acc = __builtin_fmaf(to_f32(Ct[n]), h[n], acc);
+      }
+    }
+    if (has_d) acc = __builtin_fmaf(Dd, xv, acc);
+    if (has_z) acc *= silu_f32(to_f32(z[row + lo]));
+    if (active) store_elem(y + row + lane, acc);
+  }
+  if (hT && active) {
+#pragma unroll
+    for (int n = 0; n < NMAX; ++n)
+      if (n < N) hT[(b * D + d) * N + n] = h[n];
+  }
+}
+
+template <typename S, int NMAX>
+hipError_t launch_lane_t(const Problem& p, hipStream_t stream) {
+  dim3 grid(static_cast<unsigned>((p.dim + 63) / 64), static_cast<unsigned>(p.batch));
+  hipLaunchKernelGGL((scan_lane_kernel<S, NMAX>), grid, dim3(64), 0, stream,
+                     static_cast<const S*>(p.x), static_cast<const S*>(p.delta), p.A,
+                     static_cast<const S*>(p.B), static_cast<const S*>(p.C), p.D,
+                     static_cast<const S*>(p.z), p.delta_bias, p.h0, p.hT, static_cast<S*>(p.y),
+                     p.seqlen, p.dim, static_cast<int>(p.dstate));
+  return hipGetLastError();
+}
+
+template <typename S>
+hipError_t launch_lane_s(const Problem& p, hipStream_t stream) {
+  if (p.dstate <= 8) return launch_lane_t<S, 8>(p, stream);
+  if (p.dstate <= 16) return launch_lane_t<S, 16>(p, stream);
+  if (p.dstate <= 32) return launch_lane_t<S, 32>(p, stream);
+  return launch_lane_t<S, 64>(p, stream);
+}
+
+// seqlen == 0: the final state is the initial state (or zeros).
+__global__ __launch_bounds__(256) void state_copy_kernel(const float* h0, float* hT, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) hT[i] = h0 ? h0[i] : 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_lane(const Problem& p, hipStream_t stream) {
+  return p.dtype == 0 ? launch_lane_s<float>(p, stream) : launch_lane_s<uint16_t>(p, stream);
+}
+
+hipError_t launch_state_copy(const Problem& p, hipStream_t stream) {
+  const int64_t n = p.batch * p.dim * p.dstate;
+  if (!p.hT || n == 0 || p.hT == p.h0) return hipSuccess;
+  hipLaunchKernelGGL(state_copy_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+                     p.h0, p.hT, n);
+  return hipGetLastError();
+}
+
+}  // namespace ssm

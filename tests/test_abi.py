@@ -1,0 +1,124 @@
+"""The C ABI on the CPU: the library loads, exports what the header declares,
+and rejects bad arguments on the host before any HIP call (no GPU needed).
+
+Pointers below are fake, 16-byte aligned addresses: every call here either
+fails validation or is a host-only query, so nothing is ever dereferenced.
+"""
+import ctypes
+import re
+
+import pytest
+
+import mamba_selective_scan_06_amd as ssm
+
+FAKE = 0x7F0000000000  # aligned, never dereferenced
+
+
+def _header_functions():
+    text = open(ssm.HEADER_PATH).read()
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char \*)\s*(ssm_scan_\w+)\s*\(", text, re.M)))
+
+
+def _args(**kw):
+    a = ssm.ScanArgs()
+    a.batch, a.seqlen, a.dim, a.dstate = kw.pop("shape", (2, 64, 128, 16))
+    a.dtype = kw.pop("dtype", 1)
+    base = FAKE
+    for name in ("x", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0", "hT", "y"):
+        setattr(a, name, kw.pop(name, base))
+        base += 1 << 32  # disjoint 4 GiB windows
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_library_loads_and_exports_header_symbols():
+    L = ssm.lib()
+    declared = _header_functions()
+    assert set(declared) == set(ssm.EXPORTS), declared
+    for name in declared:
+        assert hasattr(L, name), f"{name} not exported"
+    assert L.ssm_scan_abi_version() == 1
+
+
+def test_strerror_covers_codes():
+    for code in range(0, -10, -1):
+        assert ssm.strerror(code) and ssm.strerror(code) != "unknown status code"
+    assert ssm.strerror(-99) == "unknown status code"
+
+
+def _fwd(a):
+    return ssm.lib().ssm_scan_fwd(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("mut,code", [
+    (dict(shape=(-1, 8, 8, 16)), -2),
+    (dict(shape=(1, 8, 8, 0)), -3),
+    (dict(shape=(1, 8, 8, 65)), -3),
+    (dict(dtype=7), -4),
+    (dict(shape=(70000, 8, 8, 16)), -2),
+    (dict(shape=(2**40, 2**20, 2**20, 16)), -2),
+    (dict(x=0), -1), (dict(delta=0), -1), (dict(A=0), -1), (dict(B=0), -1), (dict(C=0), -1), (dict(y=0), -1),
+    (dict(x=FAKE + 2), -5), (dict(z=FAKE + 8), -5), (dict(hT=FAKE + 4), -5),
+    (dict(flags=2), -9), (dict(variant=9), -9), (dict(time_splits=-1), -9),
+    (dict(variant=3), -9),  # decode needs seqlen == 1
+    (dict(variant=2, time_splits=4), -9),  # splitting is NSPLIT only
+    (dict(shape=(2, 64, 128, 12), variant=1), -9),  # NSPLIT needs N in {4,8,16,32,64}
+])
+def test_invalid_arguments_rejected_on_host(mut, code):
+    assert _fwd(_args(**mut)) == code
+
+
+def test_null_args_struct():
+    assert ssm.lib().ssm_scan_fwd(None, None) == -1
+
+
+def test_aliasing_rejected():
+    a = _args()
+    a.y = a.x  # y over an input
+    assert _fwd(a) == -6
+    a = _args()
+    a.hT = a.A  # hT over A
+    assert _fwd(a) == -6
+    a = _args()
+    a.hT = a.h0 + 16  # partial overlap with h0
+    assert _fwd(a) == -6
+    a = _args()
+    a.y = a.hT
+    assert _fwd(a) == -6
+
+
+def test_time_splits_without_workspace_rejected():
+    a = _args(time_splits=4)
+    assert _fwd(a) == -7
+
+
+def test_empty_problems_are_noops():
+    # batch or dim zero: nothing is read or written, even with NULL pointers
+    a = _args(shape=(0, 64, 128, 16), x=0, y=0)
+    assert _fwd(a) == 0
+    a = _args(shape=(2, 64, 0, 16), x=0, y=0)
+    assert _fwd(a) == 0
+
+
+def test_plan_and_workspace_queries():
+    lib = ssm.lib()
+    # the benchmark layer: 64 channel blocks x 4 batch rows x 4 waves fills the GPU unsplit
+    a = _args(shape=(4, 8192, 4096, 16))
+    assert ssm.plan(a) == ("nsplit", 1)
+    assert lib.ssm_scan_workspace_bytes(ctypes.byref(a)) == 0
+    # long context with few channels splits time when a workspace is given
+    a = _args(shape=(1, 8192, 1536, 16))
+    nbytes = lib.ssm_scan_workspace_bytes(ctypes.byref(a))
+    assert nbytes > 0
+    assert ssm.plan(a) == ("nsplit", 1)  # no workspace: runs unsplit
+    a.workspace, a.workspace_bytes = FAKE + (64 << 32), nbytes
+    v, s = ssm.plan(a)
+    assert v == "nsplit" and s == 16
+    # in-place state update never splits
+    a.hT = a.h0
+    assert ssm.plan(a) == ("nsplit", 1)
+    # decode and the lane fallback
+    assert ssm.plan(_args(shape=(256, 1, 5120, 16))) == ("decode", 1)
+    assert ssm.plan(_args(shape=(2, 64, 128, 12))) == ("lane", 1)
+    assert ssm.plan(_args(shape=(2, 64, 128, 16), variant=2)) == ("lane", 1)
