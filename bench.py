@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--time-splits", type=int, default=0)
     ap.add_argument("--generic-a", action="store_true", help="never take the structured-decay path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="instead of the scan, copy a MIB-MiB buffer `steps` times (calibrates the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -129,6 +131,20 @@ def main():
 
     import torch
     import mamba_selective_scan_06_amd as ssm
+
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t) / max(args.steps, 1)
+        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                          "seconds_per_copy": dt, "GBps": 2 * n * 4 / dt / 1e9}), flush=True)
+        return
 
     w = workloads.BY_NAME[args.workload]
     if w.steps or w.chunks > 1:

@@ -32,7 +32,7 @@ UNITS = [("api.cpp", [], "api"), ("nsplit_dispatch.cpp", [], "nsplit_dispatch"),
 SOURCES = sorted({u[0] for u in UNITS})
 HEADERS = ["device_common.hpp", "scan_internal.hpp", "scan_nsplit_impl.hpp"]
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-command-line-argument", f"-I{os.path.join(ROOT, 'include')}"]
 

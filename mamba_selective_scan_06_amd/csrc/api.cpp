@@ -35,10 +35,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool nsplit_ok(int64_t n) { return n == 4 || n == 8 || n == 16 || n == 32 || n == 64; }
 
-// The NSPLIT kernels index inside one batch row with 32-bit offsets.
+// The NSPLIT kernels address one batch row of a tensor through a buffer
+// descriptor with 32-bit byte offsets: every row must stay below 2 GiB.
 bool row_fits_32(const ssm_scan_args* a) {
-  const int64_t lim = INT32_MAX;
-  return a->seqlen <= lim / (a->dim > 0 ? a->dim : 1) && a->seqlen <= lim / (a->dstate > 0 ? a->dstate : 1);
+  const int64_t lim = (int64_t{1} << 31) - 1;
+  const int64_t es = a->dtype == SSM_DTYPE_F32 ? 4 : 2;
+  const int64_t dmax = (a->dim > a->dstate ? a->dim : a->dstate) * es;
+  return dmax > 0 && a->seqlen <= lim / dmax;
 }
 
 struct Plan {

@@ -22,13 +22,30 @@
 //      channels: widening, softplus, u = delta x, the decay terms, D x and
 //      SiLU(z).  It publishes (decay terms, u) to LDS.
 //   S  scan phase: every wave advances its K states through the 16 tokens,
-//      reading the shared per-token terms from LDS and B_t, C_t through the
-//      scalar unit (wave-uniform s_load, SGPR operands), and writes its
-//      partial readout sum_{n in wave} C_t[n] h_n to LDS.
+//      reading the shared per-token terms from LDS, and writes its partial
+//      readout sum_{n in wave} C_t[n] h_n to LDS.
 //   Y  the owner wave adds the 4 partial sums, D x, applies the gate, rounds
 //      once and stores y_t for its tokens.
-// Inputs of the owner phase are prefetched NS_PF tiles ahead into a register
-// ring (one wave per SIMD cannot hide HBM latency by switching waves).
+//
+// Memory.  All loads are raw buffer loads over one batch row of a tensor with
+// the whole byte offset in the VGPR offset (the part the range check covers),
+// so loads past the row end return 0 and prefetching past the end of the
+// sequence is safe.  Stores of y go through a descriptor covering exactly the
+// segment, and a lane whose store must not happen gets an offset past it.
+// Every input a tile needs (x, delta, z of the owned tokens, and this wave's
+// slices of B_t and C_t for all 16 tokens) is loaded NS_PF tiles ahead into a
+// register ring; one wave per SIMD cannot hide HBM latency by switching waves,
+// and every iteration issues the same memory operations, so each wait covers
+// only the oldest tile.
+//
+// B_t and C_t are the same for all 64 channels of a wave.  A tile's slices
+// are loaded so that every 16-lane row of the wave holds the same 16 words,
+// and each value is consumed straight from its lane with a DPP row broadcast
+// (row_newbcast) as the first operand of the multiply that uses it: no LDS
+// traffic, no scalar registers, no extra instruction.  The compiler folds the
+// broadcast into v_mul_f32 for the input term; for the readout's
+// fused multiply-add it does not, so v_fmac_f32_dpp is written out (see
+// readout_dpp below).
 //
 // Structured decays.  When A[d, n] == (n+1) A[d, 0] holds exactly for every
 // channel of the block (the S4D-real diagonal of section 3.4, A = -(1..N)),
@@ -59,316 +76,481 @@ constexpr int NS_T = kNsplitTile;  // tokens per tile
 constexpr int NS_OWN = NS_T / 4;   // tokens owned by each wave per tile
 constexpr int NS_PF = 4;           // prefetch depth in tiles (register ring slots)
 
-// Raw (undecoded) form of one wave's K-element slice of a B_t or C_t row:
-// fp32 values, bf16 pairs packed in 32-bit words, or a single bf16.
-template <typename S, int K>
-struct RowSlice {
-  static constexpr bool kF32 = sizeof(S) == 4;
-  static constexpr int kWords = kF32 ? K : (K == 1 ? 1 : K / 2);
-  uint32_t v[kWords];
+// Word 3 of a raw buffer descriptor on the gfx9 family: 32-bit data format.
+constexpr int kRawBufferFlags = 0x00020000;
 
-  // p: wave-uniform pointer to the first element (the loads become s_load).
-  __device__ __forceinline__ void load(const S* p) {
-    if constexpr (kF32) {
-      const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-#pragma unroll
-      for (int k = 0; k < K; ++k) v[k] = q[k];
-    } else if constexpr (K == 1) {
-      v[0] = static_cast<uint32_t>(p[0]);
-    } else {
-      const uint32_t* q = reinterpret_cast<const uint32_t*>(p);  // even element offset
-#pragma unroll
-      for (int k = 0; k < kWords; ++k) v[k] = q[k];
-    }
-  }
-  __device__ __forceinline__ float get(int k) const {
-    if constexpr (kF32) return __uint_as_float(v[k]);
-    else if constexpr (K == 1) return __uint_as_float(v[0] << 16);
-    else return (k & 1) ? __uint_as_float(v[k >> 1] & 0xffff0000u) : __uint_as_float(v[k >> 1] << 16);
-  }
-};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buf(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRawBufferFlags);
+}
+
+// Offset that fails the range check of every descriptor used here (each
+// covers less than 2 GiB).
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+
+// One element's raw bits (bf16 zero-extended, or fp32) at byte offset `off`,
+// 0 past the buffer end.  The whole offset is in the VGPR operand: on this GPU
+// family the range check covers the VGPR and immediate offsets only.
+template <typename S>
+__device__ __forceinline__ uint32_t load_bits(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(S) == 4)
+    return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0);
+  else
+    return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, 0);
+}
 
 template <typename S>
-struct Ring {
-  S xr[NS_PF][NS_OWN];
-  S dr[NS_PF][NS_OWN];
-  S zr[NS_PF][NS_OWN];
+__device__ __forceinline__ float bits_to_f32(uint32_t v) {
+  if constexpr (sizeof(S) == 4) return __uint_as_float(v);
+  else return __uint_as_float(v << 16);
+}
+
+// Broadcast lane LANE of every 16-lane row to the whole row.
+template <int LANE>
+__device__ __forceinline__ float row_bcast(float v) {
+  static_assert(LANE >= 0 && LANE < 16, "row lane");
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + LANE, 0xf, 0xf, true));
+}
+
+// Readout terms with the C value broadcast from a lane of each 16-lane row:
+// acc (+)= bcast_L0(c0) h0 + bcast_L1(c1) h1 + ...  The compiler does not fuse
+// a DPP move into v_fmac, so these are written out, up to four terms per
+// block.  A DPP source written by a VALU instruction needs two wait states
+// before the read, and the compiler's hazard checks do not see inside inline
+// asm, so every block starts with s_nop 1.
+#define SSM_DPP_TERM(OP, A, C, H, L) OP " %" #A ", %" #C ", %" #H " row_newbcast:%c" #L " row_mask:0xf bank_mask:0xf\n\t"
+template <bool FIRST, int L0>
+__device__ __forceinline__ float readout1(float acc, float c0, float h0) {
+  if constexpr (FIRST) {
+    asm("s_nop 1\n\t" SSM_DPP_TERM("v_mul_f32_dpp", 0, 1, 2, 3) : "=&v"(acc) : "v"(c0), "v"(h0), "n"(L0));
+  } else {
+    asm("s_nop 1\n\t" SSM_DPP_TERM("v_fmac_f32_dpp", 0, 1, 2, 3) : "+v"(acc) : "v"(c0), "v"(h0), "n"(L0));
+  }
+  return acc;
+}
+template <bool FIRST, int L0, int L1>
+__device__ __forceinline__ float readout2(float acc, float c0, float c1, float h0, float h1) {
+  if constexpr (FIRST) {
+    asm("s_nop 1\n\t" SSM_DPP_TERM("v_mul_f32_dpp", 0, 1, 3, 5) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 2, 4, 6)
+        : "=&v"(acc) : "v"(c0), "v"(c1), "v"(h0), "v"(h1), "n"(L0), "n"(L1));
+  } else {
+    asm("s_nop 1\n\t" SSM_DPP_TERM("v_fmac_f32_dpp", 0, 1, 3, 5) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 2, 4, 6)
+        : "+v"(acc) : "v"(c0), "v"(c1), "v"(h0), "v"(h1), "n"(L0), "n"(L1));
+  }
+  return acc;
+}
+template <bool FIRST, int L0, int L1, int L2, int L3>
+__device__ __forceinline__ float readout4(float acc, float c0, float c1, float c2, float c3, float h0, float h1,
+                                          float h2, float h3) {
+  if constexpr (FIRST) {
+    asm("s_nop 1\n\t" SSM_DPP_TERM("v_mul_f32_dpp", 0, 1, 5, 9) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 2, 6, 10)
+            SSM_DPP_TERM("v_fmac_f32_dpp", 0, 3, 7, 11) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 4, 8, 12)
+        : "=&v"(acc) : "v"(c0), "v"(c1), "v"(c2), "v"(c3), "v"(h0), "v"(h1), "v"(h2), "v"(h3),
+          "n"(L0), "n"(L1), "n"(L2), "n"(L3));
+  } else {
+    asm("s_nop 1\n\t" SSM_DPP_TERM("v_fmac_f32_dpp", 0, 1, 5, 9) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 2, 6, 10)
+            SSM_DPP_TERM("v_fmac_f32_dpp", 0, 3, 7, 11) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 4, 8, 12)
+        : "+v"(acc) : "v"(c0), "v"(c1), "v"(c2), "v"(c3), "v"(h0), "v"(h1), "v"(h2), "v"(h3),
+          "n"(L0), "n"(L1), "n"(L2), "n"(L3));
+  }
+  return acc;
+}
+#undef SSM_DPP_TERM
+
+// Where this wave's slice of one B_t or C_t row lives in the ring.  A row-load
+// fills 16 lanes with TPL consecutive tokens of WB words each (the same in all
+// four rows of the wave); a tile takes NLD = WB row-loads per tensor.
+template <typename S, int K>
+struct BCLayout {
+  static constexpr bool kF32 = sizeof(S) == 4;
+  static constexpr bool kPairs = !kF32 && K >= 2;   // bf16 pairs in 32-bit words
+  static constexpr int WB = kF32 ? K : (K >= 2 ? K / 2 : 1);
+  static constexpr int TPL = 16 / WB;
+  static constexpr int NLD = NS_T / TPL;
+  static_assert(WB <= 16 && 16 % WB == 0, "slice must fit one 16-lane row");
+  // lane holding element k of token j (j inside the tile), and its row-load
+  static constexpr int load_of(int j) { return j / TPL; }
+  static constexpr int lane_of(int j, int k) { return (j % TPL) * WB + (kPairs ? k / 2 : (kF32 ? k : 0)); }
+  static constexpr bool odd_half(int k) { return kPairs && (k & 1); }
 };
 
 struct Smem {
-  float E[NS_T][4][64];  // decay terms: chain start per wave (structured) or delta in slot 0
-  float U[NS_T][64];     // u = delta * x
-  float P[NS_T][4][64];  // partial readouts per wave
-  float sd[4][64];       // per-wave partial sums of delta (STATE_ONLY)
+  float E[2][NS_T][4][64];  // decay terms: chain start per scan wave (structured) or delta in slot 0
+  float U[2][NS_T][64];     // u = delta * x
+  float P[2][NS_T][4][64];  // partial readouts per scan wave
 };
+constexpr int kSmemBytes = static_cast<int>(sizeof(Smem));
 
-// Everything a segment run needs besides the tensors.  Token indices and the
-// element offsets inside one batch row are 32-bit (the planner only sends
-// problems with L*D and L*N below 2^31 here), so uniform index arithmetic and
-// bounds tests stay on the scalar unit.
+// Uniform facts of one segment run plus the lane's identity.  Token indices
+// and byte offsets inside one batch row are 32-bit (the planner only sends rows
+// below 2 GiB here).
 struct SegCtx {
-  int32_t t_begin, t_end;  // token range of the segment, uniform
-  uint32_t D, d0;          // channels, first channel of the block, uniform
-  int w, lane;
-  uint32_t lo;             // lane offset used for loads (clamped for inactive lanes)
-  bool active;
+  int32_t t_begin, t_end;  // token range of the segment
+  int32_t ntiles;          // tiles in the segment, rounded up to a multiple of NS_PF
+  uint32_t D, d0;          // channels, first channel of the block
+  int w, lane;             // wave (0..7) and lane
+  bool active;             // lane's channel < D
   float A2_0, bias_d, D_d;
 };
 
-// Tokens per B/C pipeline stage (4 stages per tile; two stages live at once).
-constexpr int NS_Q = 4;
-
+// ---- owner waves (4..7): per-token scalars, loads of x/delta/z, y -----------
+// Owner wave o handles the tokens j = 4i + o (i < NS_OWN) of every tile for all
+// 64 channels.  In the iteration that the scan waves spend on tile k, it
+// computes the shared terms of tile k+1 into the other LDS buffer and finishes
+// tile k-1 from the partial readouts the scan waves left there.
 template <typename S, int K, bool STATE_ONLY, bool STRUCT, bool GATE>
-__device__ __forceinline__ void run_segment(Smem& sm, const S* __restrict__ xb, const S* __restrict__ db,
-                                            const S* __restrict__ Bb, const S* __restrict__ Cb,
-                                            const S* __restrict__ zb, S* __restrict__ yb, float (&h)[K],
-                                            const float (&A2)[K], const SegCtx& c, float& dsum) {
-  constexpr int N = 4 * K;
+__device__ __forceinline__ void owner_loop(Smem& sm, __amdgpu_buffer_rsrc_t bx, __amdgpu_buffer_rsrc_t bdl,
+                                           __amdgpu_buffer_rsrc_t bz, __amdgpu_buffer_rsrc_t by,
+                                           const SegCtx& c, float& dsum) {
+  constexpr uint32_t ES = sizeof(S);
   constexpr bool kLoadZ = !STATE_ONLY && GATE;
-  using Slice = RowSlice<S, K>;
-  Ring<S> rg;
-  const int32_t t_last = c.t_end - 1;
+  const int o = c.w - 4;
+  const uint32_t xo = (c.d0 + c.lane) * ES;
+  const uint32_t yo = (c.d0 + c.lane) * ES;
 
-  // Owner-phase loads of the tile at t0 into ring slot `slot`.  Tokens past the
-  // segment end are clamped to its last token: the loads stay in bounds and
-  // unconditional (so the compiler can wait on exactly the older ones), and the
-  // values are never used.
+  uint32_t xr[NS_PF][NS_OWN], dr[NS_PF][NS_OWN], zr[NS_PF][NS_OWN];
+  float keep_dx[NS_PF][NS_OWN], keep_g[NS_PF][NS_OWN];
+
   auto load_tile = [&](auto slot_c, int32_t t0) {
     constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
     for (int i = 0; i < NS_OWN; ++i) {
-      int32_t t = t0 + 4 * i + c.w;
-      t = t < t_last ? t : t_last;
-      const uint32_t row = static_cast<uint32_t>(t) * c.D + c.d0;  // wave-uniform
-      rg.xr[slot][i] = xb[row + c.lo];
-      rg.dr[slot][i] = db[row + c.lo];
-      if constexpr (kLoadZ) rg.zr[slot][i] = zb[row + c.lo];
+      // x, delta and z share one layout, so one offset serves all three
+      const uint32_t off = xo + static_cast<uint32_t>(t0 + 4 * i + o) * c.D * ES;
+      xr[slot][i] = load_bits<S>(bx, off);
+      dr[slot][i] = load_bits<S>(bdl, off);
+      if constexpr (kLoadZ) zr[slot][i] = load_bits<S>(bz, off);
     }
   };
 
-  // B_t, C_t slices of this wave for tokens t0 .. t0+NS_Q-1 (clamped).
-  auto load_stage = [&](int32_t t0, Slice (&Bs)[NS_Q], Slice (&Cs)[NS_Q]) {
-#pragma unroll
-    for (int j = 0; j < NS_Q; ++j) {
-      int32_t t = t0 + j;
-      t = t < t_last ? t : t_last;
-      const uint32_t off = static_cast<uint32_t>(t) * N + c.w * K;
-      Bs[j].load(Bb + off);
-      if constexpr (!STATE_ONLY) Cs[j].load(Cb + off);
-    }
-  };
-
-  // Stage 0 of the current tile, loaded one stage ahead of use.
-  Slice Bcur[NS_Q], Ccur[NS_Q];
-  load_stage(c.t_begin, Bcur, Ccur);
-
-  // One tile of 16 tokens.  Tokens past the segment end (last tile only) are
-  // given the neutral step (decay 1, input 0): the states pass through them
-  // unchanged, so the scan phase needs no bounds tests; their y is not stored.
-  auto process_tile = [&](auto slot_c, int32_t t0) {
+  // shared terms of the tile at t0 (ring slot `slot`) into LDS buffer `buf`
+  auto compute_tile = [&](auto slot_c, int buf, int32_t t0) {
     constexpr int slot = decltype(slot_c)::value;
-    float keep_dx[NS_OWN], keep_g[NS_OWN];
-    // ---- O: per-token scalar work, once per (t, d), by the owner wave -----
 #pragma unroll
     for (int i = 0; i < NS_OWN; ++i) {
-      const int j = 4 * i + c.w;
-      keep_dx[i] = 0.0f;
-      keep_g[i] = 0.0f;
+      const int j = 4 * i + o;
+      float e0 = 1.0f, e1 = 1.0f, e2 = 1.0f, e3 = 1.0f, u = 0.0f;  // neutral step
+      if constexpr (!STRUCT) e0 = 0.0f;                           // delta = 0: exp(0 * A) = 1
+      float dx = 0.0f, g = 0.0f;
       if (t0 + j < c.t_end) {  // wave-uniform
-        const float xv = to_f32(rg.xr[slot][i]);
-        const float dt = softplus_f32(to_f32(rg.dr[slot][i]) + c.bias_d);
+        const float xv = bits_to_f32<S>(xr[slot][i]);
+        const float dt = softplus_f32(bits_to_f32<S>(dr[slot][i]) + c.bias_d);
         if constexpr (STATE_ONLY) {
           dsum += dt;
         } else {
-          keep_dx[i] = c.D_d * xv;
-          if constexpr (GATE) keep_g[i] = silu_f32(to_f32(rg.zr[slot][i]));
+          dx = c.D_d * xv;
+          if constexpr (GATE) g = silu_f32(bits_to_f32<S>(zr[slot][i]));
         }
         if constexpr (STRUCT) {
           const float r = fast_exp2(dt * c.A2_0);
           float rk = r;  // r^K by squaring (K is a power of two)
 #pragma unroll
           for (int q = 1; q < K; q <<= 1) rk *= rk;
-          float e = r;
-          sm.E[j][0][c.lane] = e;
-          e *= rk; sm.E[j][1][c.lane] = e;
-          e *= rk; sm.E[j][2][c.lane] = e;
-          e *= rk; sm.E[j][3][c.lane] = e;
+          e0 = r;
+          e1 = e0 * rk;
+          e2 = e1 * rk;
+          e3 = e2 * rk;
         } else {
-          sm.E[j][0][c.lane] = dt;
+          e0 = dt;
         }
-        sm.U[j][c.lane] = dt * xv;
+        u = dt * xv;
+      }
+      sm.E[buf][j][0][c.lane] = e0;
+      if constexpr (STRUCT) {
+        sm.E[buf][j][1][c.lane] = e1;
+        sm.E[buf][j][2][c.lane] = e2;
+        sm.E[buf][j][3][c.lane] = e3;
+      }
+      sm.U[buf][j][c.lane] = u;
+      keep_dx[slot][i] = dx;
+      keep_g[slot][i] = g;
+    }
+  };
+
+  // finish the tile at t0 (its keep values in slot `slot`) from LDS buffer `buf`
+  auto finish_tile = [&](auto slot_c, int buf, int32_t t0) {
+    constexpr int slot = decltype(slot_c)::value;
+#pragma unroll
+    for (int i = 0; i < NS_OWN; ++i) {
+      const int j = 4 * i + o;
+      float yv = ((sm.P[buf][j][0][c.lane] + sm.P[buf][j][1][c.lane]) + sm.P[buf][j][2][c.lane]) +
+                 sm.P[buf][j][3][c.lane];
+      yv += keep_dx[slot][i];
+      if constexpr (GATE) yv *= keep_g[slot][i];
+      // by covers exactly the segment's tokens: tokens before it (the tile
+      // "before the first" finished in the first iteration) and lanes past D
+      // are sent out of range; tokens after it fail the range check.
+      const int32_t tr = t0 + j - c.t_begin;
+      const uint32_t off = (c.active && tr >= 0) ? yo + static_cast<uint32_t>(tr) * c.D * ES : kOutOfRange;
+      if constexpr (sizeof(S) == 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), by, static_cast<int>(off), 0, 0);
       } else {
-        if constexpr (STRUCT) {
-          sm.E[j][0][c.lane] = 1.0f;
-          sm.E[j][1][c.lane] = 1.0f;
-          sm.E[j][2][c.lane] = 1.0f;
-          sm.E[j][3][c.lane] = 1.0f;
-        } else {
-          sm.E[j][0][c.lane] = 0.0f;  // exp(0 * A) = 1
-        }
-        sm.U[j][c.lane] = 0.0f;
-      }
-    }
-    __syncthreads();
-    // ---- S: every wave advances its K states through the tile -------------
-#pragma unroll
-    for (int q = 0; q < NS_T / NS_Q; ++q) {
-      // next stage: the rest of this tile, then stage 0 of the next tile
-      Slice Bnext[NS_Q], Cnext[NS_Q];
-      load_stage(t0 + (q + 1) * NS_Q, Bnext, Cnext);
-#pragma unroll
-      for (int jj = 0; jj < NS_Q; ++jj) {
-        const int j = q * NS_Q + jj;
-        const float u = sm.U[j][c.lane];
-        float acc = 0.0f;
-        if constexpr (STRUCT) {
-          float a = sm.E[j][c.w][c.lane];
-          const float r = sm.E[j][0][c.lane];
-#pragma unroll
-          for (int k = 0; k < K; ++k) {
-            if (k > 0) a *= r;
-            h[k] = __builtin_fmaf(a, h[k], u * Bcur[jj].get(k));
-            if constexpr (!STATE_ONLY) acc = __builtin_fmaf(Ccur[jj].get(k), h[k], acc);
-          }
-        } else {
-          const float dt = sm.E[j][0][c.lane];
-#pragma unroll
-          for (int k = 0; k < K; ++k) {
-            const float a = fast_exp2(dt * A2[k]);
-            h[k] = __builtin_fmaf(a, h[k], u * Bcur[jj].get(k));
-            if constexpr (!STATE_ONLY) acc = __builtin_fmaf(Ccur[jj].get(k), h[k], acc);
-          }
-        }
-        if constexpr (!STATE_ONLY) sm.P[j][c.w][c.lane] = acc;
-      }
-#pragma unroll
-      for (int jj = 0; jj < NS_Q; ++jj) {
-        Bcur[jj] = Bnext[jj];
-        Ccur[jj] = Cnext[jj];
-      }
-    }
-    __syncthreads();
-    // ---- Y: the owner wave finishes and stores its tokens ------------------
-    if constexpr (!STATE_ONLY) {
-#pragma unroll
-      for (int i = 0; i < NS_OWN; ++i) {
-        const int j = 4 * i + c.w;
-        const int32_t t = t0 + j;
-        if (t < c.t_end) {  // wave-uniform
-          float yv = ((sm.P[j][0][c.lane] + sm.P[j][1][c.lane]) + sm.P[j][2][c.lane]) + sm.P[j][3][c.lane];
-          yv += keep_dx[i];
-          if constexpr (GATE) yv *= keep_g[i];
-          if (c.active) store_elem(yb + (static_cast<uint32_t>(t) * c.D + c.d0 + c.lane), yv);
-        }
+        __hip_bfloat16 hb = __float2bfloat16(yv);
+        __builtin_amdgcn_raw_buffer_store_b16(__bfloat16_as_ushort(hb), by, static_cast<int>(off), 0, 0);
       }
     }
   };
 
-  // Prime the ring, then consume tile k from slot k % NS_PF and refill it with
-  // tile k + NS_PF.  Slots are compile-time constants (unrolled by NS_PF).
   static_assert(NS_PF == 4, "the ring code below is written for 4 slots");
-  load_tile(std::integral_constant<int, 0>{}, c.t_begin + 0 * NS_T);
-  load_tile(std::integral_constant<int, 1>{}, c.t_begin + 1 * NS_T);
-  load_tile(std::integral_constant<int, 2>{}, c.t_begin + 2 * NS_T);
-  load_tile(std::integral_constant<int, 3>{}, c.t_begin + 3 * NS_T);
-  for (int32_t tl = c.t_begin; tl < c.t_end; tl += NS_PF * NS_T) {
-    auto step = [&](auto slot_c) {
-      const int32_t t0 = tl + decltype(slot_c)::value * NS_T;
-      if (t0 < c.t_end) {  // workgroup-uniform
-        process_tile(slot_c, t0);
-        load_tile(slot_c, t0 + NS_PF * NS_T);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  load_tile(I0{}, c.t_begin + 0 * NS_T);
+  load_tile(I1{}, c.t_begin + 1 * NS_T);
+  load_tile(I2{}, c.t_begin + 2 * NS_T);
+  load_tile(I3{}, c.t_begin + 3 * NS_T);
+  compute_tile(I0{}, 0, c.t_begin);
+  load_tile(I0{}, c.t_begin + NS_PF * NS_T);
+  __syncthreads();
+  // iteration k (tile k scanned meanwhile): compute tile k+1, finish tile k-1
+  for (int32_t k0 = 0; k0 < c.ntiles; k0 += NS_PF) {
+    auto step = [&](auto kc, auto next_c, auto prev_c) {
+      constexpr int kk = decltype(kc)::value;  // k0 + kk is the tile being scanned
+      const int32_t tk = c.t_begin + (k0 + kk) * NS_T;
+      compute_tile(next_c, (kk + 1) & 1, tk + NS_T);
+      load_tile(next_c, tk + NS_T + NS_PF * NS_T);
+      if constexpr (!STATE_ONLY) finish_tile(prev_c, (kk + 1) & 1, tk - NS_T);
+      __syncthreads();
+    };
+    // ring slot of tile m is m % 4; k0 is a multiple of 4
+    step(I0{}, I1{}, I3{});
+    step(I1{}, I2{}, I0{});
+    step(I2{}, I3{}, I1{});
+    step(I3{}, I0{}, I2{});
+  }
+  // the last scanned tile (ntiles-1 has slot 3)
+  if constexpr (!STATE_ONLY) finish_tile(I3{}, (c.ntiles - 1) & 1, c.t_begin + (c.ntiles - 1) * NS_T);
+}
+
+// ---- scan waves (0..3): the recurrence ---------------------------------------
+template <typename S, int K, bool STATE_ONLY, bool STRUCT>
+__device__ __forceinline__ void scan_loop(Smem& sm, __amdgpu_buffer_rsrc_t bB, __amdgpu_buffer_rsrc_t bC,
+                                          float (&h)[K], const float (&A2)[K], const SegCtx& c) {
+  constexpr int N = 4 * K;
+  constexpr uint32_t ES = sizeof(S);
+  using BL = BCLayout<S, K>;
+  constexpr int NLD = BL::NLD;
+  uint32_t bq[NS_PF][NLD], cq[NS_PF][NLD];
+  const int k16 = c.lane & 15;
+  const uint32_t bco =
+      ((k16 / BL::WB) * N + c.w * K + (BL::kPairs ? 2 * (k16 % BL::WB) : (BL::kF32 ? k16 % BL::WB : 0))) * ES;
+
+  auto load_tile = [&](auto slot_c, int32_t t0) {
+    constexpr int slot = decltype(slot_c)::value;
+    const uint32_t base = bco + static_cast<uint32_t>(t0) * (N * ES);
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+      const int off = static_cast<int>(base + q * BL::TPL * N * ES);  // q part folds into the immediate
+      bq[slot][q] = BL::kPairs || BL::kF32 ? __builtin_amdgcn_raw_buffer_load_b32(bB, off, 0, 0)
+                                           : __builtin_amdgcn_raw_buffer_load_b16(bB, off, 0, 0);
+      if constexpr (!STATE_ONLY)
+        cq[slot][q] = BL::kPairs || BL::kF32 ? __builtin_amdgcn_raw_buffer_load_b32(bC, off, 0, 0)
+                                             : __builtin_amdgcn_raw_buffer_load_b16(bC, off, 0, 0);
+    }
+  };
+
+  auto scan_tile = [&](auto slot_c, int buf) {
+    constexpr int slot = decltype(slot_c)::value;
+    float Blo[NLD], Bhi[NLD], Clo[NLD], Chi[NLD];
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+      if constexpr (BL::kF32) {
+        Blo[q] = __uint_as_float(bq[slot][q]);
+        Bhi[q] = 0.0f;
+      } else {
+        Blo[q] = __uint_as_float(bq[slot][q] << 16);
+        Bhi[q] = BL::kPairs ? __uint_as_float(bq[slot][q] & 0xffff0000u) : 0.0f;
+      }
+    }
+    auto token = [&](auto j_c) {
+      constexpr int j = decltype(j_c)::value;
+      constexpr int q = BL::load_of(j);
+      if constexpr (!STATE_ONLY && j % BL::TPL == 0) {
+        if constexpr (BL::kF32) {
+          Clo[q] = __uint_as_float(cq[slot][q]);
+          Chi[q] = 0.0f;
+        } else {
+          Clo[q] = __uint_as_float(cq[slot][q] << 16);
+          Chi[q] = BL::kPairs ? __uint_as_float(cq[slot][q] & 0xffff0000u) : 0.0f;
+        }
+      }
+      const float u = sm.U[buf][j][c.lane];
+      float hv[K];
+      float a = STRUCT ? sm.E[buf][j][c.w][c.lane] : 0.0f;
+      const float r = STRUCT ? sm.E[buf][j][0][c.lane] : 0.0f;
+      const float dt = STRUCT ? 0.0f : sm.E[buf][j][0][c.lane];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        if constexpr (STRUCT) {
+          if (k > 0) a *= r;
+        } else {
+          a = fast_exp2(dt * A2[k]);
+        }
+        const float bsrc = BL::odd_half(k) ? Bhi[q] : Blo[q];
+        float bk;
+        switch (BL::lane_of(j, k)) {  // compile-time constant after unrolling
+#define SSM_BCAST_CASE(L) case L: bk = row_bcast<L>(bsrc); break;
+          SSM_BCAST_CASE(0) SSM_BCAST_CASE(1) SSM_BCAST_CASE(2) SSM_BCAST_CASE(3)
+          SSM_BCAST_CASE(4) SSM_BCAST_CASE(5) SSM_BCAST_CASE(6) SSM_BCAST_CASE(7)
+          SSM_BCAST_CASE(8) SSM_BCAST_CASE(9) SSM_BCAST_CASE(10) SSM_BCAST_CASE(11)
+          SSM_BCAST_CASE(12) SSM_BCAST_CASE(13) SSM_BCAST_CASE(14) SSM_BCAST_CASE(15)
+#undef SSM_BCAST_CASE
+          default: bk = 0.0f;
+        }
+        h[k] = __builtin_fmaf(a, h[k], bk * u);
+        hv[k] = h[k];
+      }
+      if constexpr (!STATE_ONLY) {
+        auto csrc = [&](int k) { return BL::odd_half(k) ? Chi[q] : Clo[q]; };
+        float acc = 0.0f;
+        if constexpr (K == 1) {
+          acc = readout1<true, BL::lane_of(j, 0)>(acc, csrc(0), hv[0]);
+        } else if constexpr (K == 2) {
+          acc = readout2<true, BL::lane_of(j, 0), BL::lane_of(j, 1)>(acc, csrc(0), csrc(1), hv[0], hv[1]);
+        } else {
+          auto chunk = [&](auto g_c) {
+            constexpr int g = decltype(g_c)::value;
+            acc = readout4<g == 0, BL::lane_of(j, 4 * g), BL::lane_of(j, 4 * g + 1), BL::lane_of(j, 4 * g + 2),
+                           BL::lane_of(j, 4 * g + 3)>(acc, csrc(4 * g), csrc(4 * g + 1), csrc(4 * g + 2),
+                                                      csrc(4 * g + 3), hv[4 * g], hv[4 * g + 1], hv[4 * g + 2],
+                                                      hv[4 * g + 3]);
+          };
+          chunk(std::integral_constant<int, 0>{});
+          if constexpr (K >= 8) chunk(std::integral_constant<int, 1>{});
+          if constexpr (K >= 12) chunk(std::integral_constant<int, 2>{});
+          if constexpr (K >= 16) chunk(std::integral_constant<int, 3>{});
+        }
+        sm.P[buf][j][c.w][c.lane] = acc;
       }
     };
-    step(std::integral_constant<int, 0>{});
-    step(std::integral_constant<int, 1>{});
-    step(std::integral_constant<int, 2>{});
-    step(std::integral_constant<int, 3>{});
+    [&]<int... js>(std::integer_sequence<int, js...>) {
+      (token(std::integral_constant<int, js>{}), ...);
+    }(std::make_integer_sequence<int, NS_T>{});
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  load_tile(I0{}, c.t_begin + 0 * NS_T);
+  load_tile(I1{}, c.t_begin + 1 * NS_T);
+  load_tile(I2{}, c.t_begin + 2 * NS_T);
+  load_tile(I3{}, c.t_begin + 3 * NS_T);
+  __syncthreads();
+  for (int32_t k0 = 0; k0 < c.ntiles; k0 += NS_PF) {
+    auto step = [&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
+      scan_tile(kc, kk & 1);
+      load_tile(kc, c.t_begin + (k0 + kk + NS_PF) * NS_T);
+      __syncthreads();
+    };
+    step(I0{});
+    step(I1{});
+    step(I2{});
+    step(I3{});
   }
 }
 
 template <typename S, int K, bool STATE_ONLY, bool GATE>
-__global__ __launch_bounds__(256, 1) void scan_nsplit_kernel(
+__global__ __launch_bounds__(512, 1) void scan_nsplit_kernel(
     const S* __restrict__ x, const S* __restrict__ dl, const float* __restrict__ A,
     const S* __restrict__ Bm, const S* __restrict__ Cm, const float* __restrict__ Dsk,
     const S* __restrict__ z, const float* __restrict__ bias, const float* h0, float* hT,
     S* __restrict__ y, float* __restrict__ ws_state, float* __restrict__ ws_dsum,
     int32_t L, int32_t D, int32_t seg_len, int splits, int flags) {
   constexpr int N = 4 * K;
-  __shared__ Smem sm;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   SegCtx c;
   c.w = wave_id();
   c.lane = threadIdx.x & 63;
+  const int sw = c.w & 3;  // scan wave index of this lane's states (owners shadow it)
   const int64_t b = blockIdx.y;
   const int s = blockIdx.z;
   c.D = static_cast<uint32_t>(D);
   c.d0 = blockIdx.x * 64u;
   c.active = c.d0 + c.lane < c.D;
-  c.lo = c.active ? c.lane : c.D - 1 - c.d0;
-  const int64_t d = c.d0 + c.lo;  // inactive lanes shadow channel D-1 and write nothing
+  const uint32_t lo = c.active ? c.lane : c.D - 1 - c.d0;
+  const int64_t d = c.d0 + lo;  // inactive lanes shadow channel D-1 for per-channel reads
   c.t_begin = s * seg_len;
   c.t_end = (c.t_begin + seg_len < L) ? c.t_begin + seg_len : L;
+  const int32_t nt = (c.t_end - c.t_begin + NS_T - 1) / NS_T;
+  c.ntiles = (nt + NS_PF - 1) / NS_PF * NS_PF;
 
   float A2[K];
 #pragma unroll
-  for (int k = 0; k < K; ++k) A2[k] = A[d * N + c.w * K + k] * kLog2e;
+  for (int k = 0; k < K; ++k) A2[k] = A[d * N + sw * K + k] * kLog2e;
   const float a0 = A[d * N];
   c.A2_0 = a0 * kLog2e;
 
   // Structured-decay test for the whole block: A[d, n] == (n+1) A[d, 0] exactly.
   bool ok = !(flags & kFlagGenericA);
 #pragma unroll
-  for (int k = 0; k < K; ++k) ok = ok && (A[d * N + c.w * K + k] == static_cast<float>(c.w * K + k + 1) * a0);
+  for (int k = 0; k < K; ++k) ok = ok && (A[d * N + sw * K + k] == static_cast<float>(sw * K + k + 1) * a0);
   const bool structured = __syncthreads_and(ok ? 1 : 0) != 0;
 
   c.bias_d = bias ? bias[d] : 0.0f;
   c.D_d = Dsk ? Dsk[d] : 0.0f;
 
-  float h[K];
-  if constexpr (STATE_ONLY) {
-#pragma unroll
-    for (int k = 0; k < K; ++k) h[k] = 0.0f;
-  } else {
-#pragma unroll
-    for (int k = 0; k < K; ++k) h[k] = h0 ? h0[(b * D + d) * N + c.w * K + k] : 0.0f;
-    // Carry in the summaries of the segments before this one.
-    for (int j = 0; j < s; ++j) {
-      const int64_t seg = b * splits + j;
-      const float sdl = ws_dsum[seg * D + d];
-#pragma unroll
-      for (int k = 0; k < K; ++k)
-        h[k] = __builtin_fmaf(fast_exp2(A2[k] * sdl), h[k], ws_state[(seg * D + d) * N + c.w * K + k]);
-    }
-  }
-
-  // Base pointers of this batch row; offsets inside a row are 32-bit.
+  // Buffer views of this batch row; byte offsets inside a row are 32-bit.
   const int64_t rowD = b * static_cast<int64_t>(L) * D, rowN = b * static_cast<int64_t>(L) * N;
-  const S* xb = x + rowD;
-  const S* db = dl + rowD;
-  const S* zb = z ? z + rowD : x + rowD;  // never read without a gate
-  const S* Bb = Bm + rowN;
-  const S* Cb = Cm + rowN;
-  S* yb = y + rowD;
+  const uint32_t bytesD = static_cast<uint32_t>(static_cast<int64_t>(L) * D * sizeof(S));
+  const uint32_t bytesN = static_cast<uint32_t>(static_cast<int64_t>(L) * N * sizeof(S));
 
   float dsum = 0.0f;
-  if (structured)
-    run_segment<S, K, STATE_ONLY, true, GATE>(sm, xb, db, Bb, Cb, zb, yb, h, A2, c, dsum);
-  else
-    run_segment<S, K, STATE_ONLY, false, GATE>(sm, xb, db, Bb, Cb, zb, yb, h, A2, c, dsum);
+  float h[K];
+  if (c.w >= 4) {
+    const __amdgpu_buffer_rsrc_t bx = make_buf(x + rowD, bytesD);
+    const __amdgpu_buffer_rsrc_t bdl = make_buf(dl + rowD, bytesD);
+    const __amdgpu_buffer_rsrc_t bz = make_buf(z ? z + rowD : x + rowD, bytesD);  // never read without a gate
+    const __amdgpu_buffer_rsrc_t by = make_buf(
+        y + rowD + static_cast<int64_t>(c.t_begin) * D,
+        static_cast<uint32_t>(static_cast<int64_t>(c.t_end - c.t_begin) * D * sizeof(S)));
+    if (structured)
+      owner_loop<S, K, STATE_ONLY, true, GATE>(sm, bx, bdl, bz, by, c, dsum);
+    else
+      owner_loop<S, K, STATE_ONLY, false, GATE>(sm, bx, bdl, bz, by, c, dsum);
+  } else {
+    if constexpr (STATE_ONLY) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) h[k] = 0.0f;
+    } else {
+#pragma unroll
+      for (int k = 0; k < K; ++k) h[k] = h0 ? h0[(b * D + d) * N + sw * K + k] : 0.0f;
+      // Carry in the summaries of the segments before this one.
+      for (int j = 0; j < s; ++j) {
+        const int64_t seg = b * splits + j;
+        const float sdl = ws_dsum[seg * D + d];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+          h[k] = __builtin_fmaf(fast_exp2(A2[k] * sdl), h[k], ws_state[(seg * D + d) * N + sw * K + k]);
+      }
+    }
+    const __amdgpu_buffer_rsrc_t bB = make_buf(Bm + rowN, bytesN);
+    const __amdgpu_buffer_rsrc_t bC = make_buf(Cm + rowN, bytesN);
+    if (structured)
+      scan_loop<S, K, STATE_ONLY, true>(sm, bB, bC, h, A2, c);
+    else
+      scan_loop<S, K, STATE_ONLY, false>(sm, bB, bC, h, A2, c);
+  }
 
   if constexpr (STATE_ONLY) {
-    const int64_t seg = b * splits + s;
-    if (c.active) {
-#pragma unroll
-      for (int k = 0; k < K; ++k) ws_state[(seg * D + d) * N + c.w * K + k] = h[k];
-    }
-    sm.sd[c.w][c.lane] = dsum;
+    // per-channel sum of delta: owner partials through LDS (reusing E)
     __syncthreads();
-    if (c.w == 0 && c.active)
-      ws_dsum[seg * D + d] = ((sm.sd[0][c.lane] + sm.sd[1][c.lane]) + sm.sd[2][c.lane]) + sm.sd[3][c.lane];
-  } else {
-    if (hT && c.active && s == splits - 1) {
+    float* sdv = &sm.E[0][0][0][0];
+    if (c.w >= 4) sdv[(c.w - 4) * 64 + c.lane] = dsum;
+    __syncthreads();
+    const int64_t seg = b * splits + s;
+    if (c.w < 4 && c.active) {
 #pragma unroll
-      for (int k = 0; k < K; ++k) hT[(b * D + d) * N + c.w * K + k] = h[k];
+      for (int k = 0; k < K; ++k) ws_state[(seg * D + d) * N + sw * K + k] = h[k];
+    }
+    if (c.w == 0 && c.active)
+      ws_dsum[seg * D + d] = ((sdv[c.lane] + sdv[64 + c.lane]) + sdv[128 + c.lane]) + sdv[192 + c.lane];
+  } else {
+    if (hT && c.w < 4 && c.active && s == splits - 1) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) hT[(b * D + d) * N + sw * K + k] = h[k];
     }
   }
 }
@@ -377,7 +559,7 @@ template <typename S, int K, bool STATE_ONLY, bool GATE>
 void launch_one(const Problem& p, hipStream_t stream, unsigned nseg) {
   const unsigned nb = static_cast<unsigned>((p.dim + 63) / 64);
   hipLaunchKernelGGL((scan_nsplit_kernel<S, K, STATE_ONLY, GATE>), dim3(nb, static_cast<unsigned>(p.batch), nseg),
-                     dim3(256), 0, stream, static_cast<const S*>(p.x), static_cast<const S*>(p.delta), p.A,
+                     dim3(512), kSmemBytes, stream, static_cast<const S*>(p.x), static_cast<const S*>(p.delta), p.A,
                      static_cast<const S*>(p.B), static_cast<const S*>(p.C), p.D, static_cast<const S*>(p.z),
                      p.delta_bias, p.h0, p.hT, static_cast<S*>(p.y), p.ws_state, p.ws_dsum,
                      static_cast<int32_t>(p.seqlen), static_cast<int32_t>(p.dim), static_cast<int32_t>(p.seg_len),
