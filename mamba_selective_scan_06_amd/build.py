@@ -30,7 +30,7 @@ UNITS = [("api.cpp", [], "api"), ("nsplit_dispatch.cpp", [], "nsplit_dispatch"),
     ("nsplit_inst.hip", [f"-DNSPLIT_S={s}", f"-DNSPLIT_K={k}"], f"nsplit_{'f32' if s == 'float' else 'bf16'}_k{k}")
     for s, k in NSPLIT_INST]
 SOURCES = sorted({u[0] for u in UNITS})
-HEADERS = ["device_common.hpp", "scan_internal.hpp", "scan_nsplit_impl.hpp"]
+HEADERS = ["buffer_io.hpp", "device_common.hpp", "scan_internal.hpp", "scan_nsplit_impl.hpp"]
 
 COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -47,12 +47,34 @@ def _compile(unit) -> str:
     return out
 
 
+def _device_asm(unit) -> str:
+    """gfx950 assembly of one NSPLIT unit, for the DPP hazard check."""
+    src, defs, name = unit
+    out = os.path.join(OBJ, name + ".s")
+    cmd = [HIPCC, *COMMON, *defs, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {name}:\n{r.stdout}\n{r.stderr}")
+    return out
+
+
 def build(jobs: int | None = None, verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
+    """Compile every source, check the NSPLIT device code for the DPP hazard
+    that inline asm hides from the compiler, and link the shared library;
+    returns its path."""
+    from . import dpp_hazard_check
+
     os.makedirs(OBJ, exist_ok=True)
     jobs = jobs or min(len(UNITS), os.cpu_count() or 1, 16)
+    asm_units = [u for u in UNITS if u[0] == "nsplit_inst.hip"]
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, UNITS))
+        listings = list(ex.map(_device_asm, asm_units))
+    problems = []
+    for path in listings:
+        problems += dpp_hazard_check.check_file(path)
+    if problems:
+        raise RuntimeError("VALU -> DPP hazard in generated code:\n" + "\n".join(problems[:20]))
     tmp = LIB + f".tmp{os.getpid()}"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -66,6 +66,7 @@
 
 #include <type_traits>
 
+#include "buffer_io.hpp"
 #include "device_common.hpp"
 #include "scan_internal.hpp"
 
@@ -75,34 +76,6 @@ namespace nsplit_detail {
 constexpr int NS_T = kNsplitTile;  // tokens per tile
 constexpr int NS_OWN = NS_T / 4;   // tokens owned by each wave per tile
 constexpr int NS_PF = 4;           // prefetch depth in tiles (register ring slots)
-
-// Word 3 of a raw buffer descriptor on the gfx9 family: 32-bit data format.
-constexpr int kRawBufferFlags = 0x00020000;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buf(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRawBufferFlags);
-}
-
-// Offset that fails the range check of every descriptor used here (each
-// covers less than 2 GiB).
-constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
-
-// One element's raw bits (bf16 zero-extended, or fp32) at byte offset `off`,
-// 0 past the buffer end.  The whole offset is in the VGPR operand: on this GPU
-// family the range check covers the VGPR and immediate offsets only.
-template <typename S>
-__device__ __forceinline__ uint32_t load_bits(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  if constexpr (sizeof(S) == 4)
-    return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0);
-  else
-    return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, 0);
-}
-
-template <typename S>
-__device__ __forceinline__ float bits_to_f32(uint32_t v) {
-  if constexpr (sizeof(S) == 4) return __uint_as_float(v);
-  else return __uint_as_float(v << 16);
-}
 
 // Broadcast lane LANE of every 16-lane row to the whole row.
 template <int LANE>
@@ -116,44 +89,59 @@ __device__ __forceinline__ float row_bcast(float v) {
 // a DPP move into v_fmac, so these are written out, up to four terms per
 // block.  A DPP source written by a VALU instruction needs two wait states
 // before the read, and the compiler's hazard checks do not see inside inline
-// asm, so every block starts with s_nop 1.
+// asm.  The sources are the C words of the tile's register ring, widened by
+// VALU once per row-load (every TPL tokens): the first block after a widening
+// starts with s_nop 1 (NOP), the others read registers written at least one
+// whole block earlier.  The build's hazard check of the generated code
+// verifies this for every instantiation.
 #define SSM_DPP_TERM(OP, A, C, H, L) OP " %" #A ", %" #C ", %" #H " row_newbcast:%c" #L " row_mask:0xf bank_mask:0xf\n\t"
-template <bool FIRST, int L0>
+// Each block is emitted with or without the leading s_nop 1.
+#define SSM_READOUT_ASM(NOP, BODY, ...)   \
+  do {                                    \
+    if constexpr (NOP)                    \
+      asm("s_nop 1\n\t" BODY __VA_ARGS__); \
+    else                                  \
+      asm(BODY __VA_ARGS__);              \
+  } while (0)
+template <bool FIRST, bool NOP, int L0>
 __device__ __forceinline__ float readout1(float acc, float c0, float h0) {
   if constexpr (FIRST) {
-    asm("s_nop 1\n\t" SSM_DPP_TERM("v_mul_f32_dpp", 0, 1, 2, 3) : "=&v"(acc) : "v"(c0), "v"(h0), "n"(L0));
+    SSM_READOUT_ASM(NOP, SSM_DPP_TERM("v_mul_f32_dpp", 0, 1, 2, 3), : "=&v"(acc) : "v"(c0), "v"(h0), "n"(L0));
   } else {
-    asm("s_nop 1\n\t" SSM_DPP_TERM("v_fmac_f32_dpp", 0, 1, 2, 3) : "+v"(acc) : "v"(c0), "v"(h0), "n"(L0));
+    SSM_READOUT_ASM(NOP, SSM_DPP_TERM("v_fmac_f32_dpp", 0, 1, 2, 3), : "+v"(acc) : "v"(c0), "v"(h0), "n"(L0));
   }
   return acc;
 }
-template <bool FIRST, int L0, int L1>
+template <bool FIRST, bool NOP, int L0, int L1>
 __device__ __forceinline__ float readout2(float acc, float c0, float c1, float h0, float h1) {
   if constexpr (FIRST) {
-    asm("s_nop 1\n\t" SSM_DPP_TERM("v_mul_f32_dpp", 0, 1, 3, 5) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 2, 4, 6)
-        : "=&v"(acc) : "v"(c0), "v"(c1), "v"(h0), "v"(h1), "n"(L0), "n"(L1));
+    SSM_READOUT_ASM(NOP, SSM_DPP_TERM("v_mul_f32_dpp", 0, 1, 3, 5) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 2, 4, 6),
+                    : "=&v"(acc) : "v"(c0), "v"(c1), "v"(h0), "v"(h1), "n"(L0), "n"(L1));
   } else {
-    asm("s_nop 1\n\t" SSM_DPP_TERM("v_fmac_f32_dpp", 0, 1, 3, 5) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 2, 4, 6)
-        : "+v"(acc) : "v"(c0), "v"(c1), "v"(h0), "v"(h1), "n"(L0), "n"(L1));
+    SSM_READOUT_ASM(NOP, SSM_DPP_TERM("v_fmac_f32_dpp", 0, 1, 3, 5) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 2, 4, 6),
+                    : "+v"(acc) : "v"(c0), "v"(c1), "v"(h0), "v"(h1), "n"(L0), "n"(L1));
   }
   return acc;
 }
-template <bool FIRST, int L0, int L1, int L2, int L3>
+template <bool FIRST, bool NOP, int L0, int L1, int L2, int L3>
 __device__ __forceinline__ float readout4(float acc, float c0, float c1, float c2, float c3, float h0, float h1,
                                           float h2, float h3) {
   if constexpr (FIRST) {
-    asm("s_nop 1\n\t" SSM_DPP_TERM("v_mul_f32_dpp", 0, 1, 5, 9) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 2, 6, 10)
-            SSM_DPP_TERM("v_fmac_f32_dpp", 0, 3, 7, 11) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 4, 8, 12)
-        : "=&v"(acc) : "v"(c0), "v"(c1), "v"(c2), "v"(c3), "v"(h0), "v"(h1), "v"(h2), "v"(h3),
-          "n"(L0), "n"(L1), "n"(L2), "n"(L3));
+    SSM_READOUT_ASM(NOP,
+                    SSM_DPP_TERM("v_mul_f32_dpp", 0, 1, 5, 9) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 2, 6, 10)
+                        SSM_DPP_TERM("v_fmac_f32_dpp", 0, 3, 7, 11) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 4, 8, 12),
+                    : "=&v"(acc) : "v"(c0), "v"(c1), "v"(c2), "v"(c3), "v"(h0), "v"(h1), "v"(h2), "v"(h3),
+                      "n"(L0), "n"(L1), "n"(L2), "n"(L3));
   } else {
-    asm("s_nop 1\n\t" SSM_DPP_TERM("v_fmac_f32_dpp", 0, 1, 5, 9) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 2, 6, 10)
-            SSM_DPP_TERM("v_fmac_f32_dpp", 0, 3, 7, 11) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 4, 8, 12)
-        : "+v"(acc) : "v"(c0), "v"(c1), "v"(c2), "v"(c3), "v"(h0), "v"(h1), "v"(h2), "v"(h3),
-          "n"(L0), "n"(L1), "n"(L2), "n"(L3));
+    SSM_READOUT_ASM(NOP,
+                    SSM_DPP_TERM("v_fmac_f32_dpp", 0, 1, 5, 9) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 2, 6, 10)
+                        SSM_DPP_TERM("v_fmac_f32_dpp", 0, 3, 7, 11) SSM_DPP_TERM("v_fmac_f32_dpp", 0, 4, 8, 12),
+                    : "+v"(acc) : "v"(c0), "v"(c1), "v"(c2), "v"(c3), "v"(h0), "v"(h1), "v"(h2), "v"(h3),
+                      "n"(L0), "n"(L1), "n"(L2), "n"(L3));
   }
   return acc;
 }
+#undef SSM_READOUT_ASM
 #undef SSM_DPP_TERM
 
 // Where this wave's slice of one B_t or C_t row lives in the ring.  A row-load
@@ -281,12 +269,7 @@ __device__ __forceinline__ void owner_loop(Smem& sm, __amdgpu_buffer_rsrc_t bx, 
       // are sent out of range; tokens after it fail the range check.
       const int32_t tr = t0 + j - c.t_begin;
       const uint32_t off = (c.active && tr >= 0) ? yo + static_cast<uint32_t>(tr) * c.D * ES : kOutOfRange;
-      if constexpr (sizeof(S) == 4) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), by, static_cast<int>(off), 0, 0);
-      } else {
-        __hip_bfloat16 hb = __float2bfloat16(yv);
-        __builtin_amdgcn_raw_buffer_store_b16(__bfloat16_as_ushort(hb), by, static_cast<int>(off), 0, 0);
-      }
+      store_val<S>(by, off, yv);
     }
   };
 
@@ -403,14 +386,17 @@ __device__ __forceinline__ void scan_loop(Smem& sm, __amdgpu_buffer_rsrc_t bB, _
       if constexpr (!STATE_ONLY) {
         auto csrc = [&](int k) { return BL::odd_half(k) ? Chi[q] : Clo[q]; };
         float acc = 0.0f;
+        constexpr bool kWidened = j % BL::TPL == 0;  // C words widened just before this token
         if constexpr (K == 1) {
-          acc = readout1<true, BL::lane_of(j, 0)>(acc, csrc(0), hv[0]);
+          acc = readout1<true, kWidened, BL::lane_of(j, 0)>(acc, csrc(0), hv[0]);
         } else if constexpr (K == 2) {
-          acc = readout2<true, BL::lane_of(j, 0), BL::lane_of(j, 1)>(acc, csrc(0), csrc(1), hv[0], hv[1]);
+          acc = readout2<true, kWidened, BL::lane_of(j, 0), BL::lane_of(j, 1)>(acc, csrc(0), csrc(1), hv[0],
+                                                                               hv[1]);
         } else {
           auto chunk = [&](auto g_c) {
             constexpr int g = decltype(g_c)::value;
-            acc = readout4<g == 0, BL::lane_of(j, 4 * g), BL::lane_of(j, 4 * g + 1), BL::lane_of(j, 4 * g + 2),
+            acc = readout4<g == 0, kWidened && g == 0, BL::lane_of(j, 4 * g), BL::lane_of(j, 4 * g + 1),
+                           BL::lane_of(j, 4 * g + 2),
                            BL::lane_of(j, 4 * g + 3)>(acc, csrc(4 * g), csrc(4 * g + 1), csrc(4 * g + 2),
                                                       csrc(4 * g + 3), hv[4 * g], hv[4 * g + 1], hv[4 * g + 2],
                                                       hv[4 * g + 3]);
