@@ -254,14 +254,22 @@ __device__ __forceinline__ void owner_loop(Smem& sm, __amdgpu_buffer_rsrc_t bx, 
     }
   };
 
-  // finish the tile at t0 (its keep values in slot `slot`) from LDS buffer `buf`
-  auto finish_tile = [&](auto slot_c, int buf, int32_t t0) {
+  // Partial readouts of the tile to finish, read at the start of the
+  // iteration so their LDS latency hides behind compute_tile.
+  float pr[NS_OWN][4];
+  auto read_partials = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NS_OWN; ++i)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pr[i][w] = sm.P[buf][4 * i + o][w][c.lane];
+  };
+  // finish the tile at t0 (its keep values in slot `slot`) from the partials in pr
+  auto finish_tile = [&](auto slot_c, int32_t t0) {
     constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
     for (int i = 0; i < NS_OWN; ++i) {
       const int j = 4 * i + o;
-      float yv = ((sm.P[buf][j][0][c.lane] + sm.P[buf][j][1][c.lane]) + sm.P[buf][j][2][c.lane]) +
-                 sm.P[buf][j][3][c.lane];
+      float yv = ((pr[i][0] + pr[i][1]) + pr[i][2]) + pr[i][3];
       yv += keep_dx[slot][i];
       if constexpr (GATE) yv *= keep_g[slot][i];
       // by covers exactly the segment's tokens: tokens before it (the tile
@@ -290,9 +298,10 @@ __device__ __forceinline__ void owner_loop(Smem& sm, __amdgpu_buffer_rsrc_t bx, 
     auto step = [&](auto kc, auto next_c, auto prev_c) {
       constexpr int kk = decltype(kc)::value;  // k0 + kk is the tile being scanned
       const int32_t tk = c.t_begin + (k0 + kk) * NS_T;
+      if constexpr (!STATE_ONLY) read_partials((kk + 1) & 1);
       compute_tile(next_c, (kk + 1) & 1, tk + NS_T);
       load_tile(next_c, tk + NS_T + NS_PF * NS_T);
-      if constexpr (!STATE_ONLY) finish_tile(prev_c, (kk + 1) & 1, tk - NS_T);
+      if constexpr (!STATE_ONLY) finish_tile(prev_c, tk - NS_T);
       __syncthreads();
     };
     // ring slot of tile m is m % 4; k0 is a multiple of 4
@@ -302,7 +311,10 @@ __device__ __forceinline__ void owner_loop(Smem& sm, __amdgpu_buffer_rsrc_t bx, 
     step(I3{}, I0{}, I2{});
   }
   // the last scanned tile (ntiles-1 has slot 3)
-  if constexpr (!STATE_ONLY) finish_tile(I3{}, (c.ntiles - 1) & 1, c.t_begin + (c.ntiles - 1) * NS_T);
+  if constexpr (!STATE_ONLY) {
+    read_partials((c.ntiles - 1) & 1);
+    finish_tile(I3{}, c.t_begin + (c.ntiles - 1) * NS_T);
+  }
 }
 
 // ---- scan waves (0..3): the recurrence ---------------------------------------
@@ -345,6 +357,8 @@ __device__ __forceinline__ void scan_loop(Smem& sm, __amdgpu_buffer_rsrc_t bB, _
         Bhi[q] = BL::kPairs ? __uint_as_float(bq[slot][q] & 0xffff0000u) : 0.0f;
       }
     }
+    // (Reading a token's LDS terms earlier than its use, in bursts or a few
+    // tokens ahead, measured slower on this GPU: the reads stay next to it.)
     auto token = [&](auto j_c) {
       constexpr int j = decltype(j_c)::value;
       constexpr int q = BL::load_of(j);

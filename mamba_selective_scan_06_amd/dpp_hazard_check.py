@@ -41,10 +41,21 @@ def _split(line: str):
 
 
 def check_lines(lines: list[str], name: str = "<asm>") -> list[str]:
+    """Problems found for the DPP instructions written in inline asm (between
+    the compiler's ;;#ASMSTART and ;;#ASMEND markers); the compiler resolves
+    the hazard itself for the DPP it generates."""
     problems = []
+    in_asm = False
     for i, line in enumerate(lines):
+        marker = line.strip()
+        if marker.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if marker.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
         ins = _split(line)
-        if ins is None:
+        if ins is None or not in_asm:
             continue
         mnem, ops = ins
         if not mnem.startswith("v_") or "_dpp" not in mnem or len(ops) < 2:

@@ -12,7 +12,7 @@ import pytest
 from mamba_selective_scan_06_amd import build as hipbuild
 from mamba_selective_scan_06_amd.dpp_hazard_check import check_lines
 
-DPP = "\tv_fmac_f32_dpp v7, v5, v8 row_newbcast:3 row_mask:0xf bank_mask:0xf"
+DPP = [";;#ASMSTART", "\tv_fmac_f32_dpp v7, v5, v8 row_newbcast:3 row_mask:0xf bank_mask:0xf", ";;#ASMEND"]
 
 
 @pytest.mark.parametrize("before,n_bad", [
@@ -26,9 +26,15 @@ DPP = "\tv_fmac_f32_dpp v7, v5, v8 row_newbcast:3 row_mask:0xf bank_mask:0xf"
     (["\tv_mul_f32_e32 v9, v1, v2", "\tv_mul_f32_e32 v9, v1, v2", ".LBB0_3:"], 1),  # a path may enter
     ([".LBB0_3:", "\ts_nop 1"], 0),
     (["\tds_read_b32 v5, v2", "\ts_waitcnt lgkmcnt(0)"], 0),           # not a VALU write
+    (["\tv_lshlrev_b32_e32 v5, 16, v3", ";;#ASMEND", ";;#ASMSTART"], 1),  # across asm blocks
 ])
 def test_checker_on_listings(before, n_bad):
-    assert len(check_lines(before + [DPP])) == n_bad
+    assert len(check_lines(before + DPP)) == n_bad
+
+
+def test_compiler_generated_dpp_is_left_to_the_compiler():
+    listing = ["\tv_lshlrev_b32_e32 v5, 16, v3", "\tv_mul_f32_dpp v7, v5, v8 row_newbcast:3 bound_ctrl:1"]
+    assert check_lines(listing) == []
 
 
 def test_built_listings_are_clean():
