@@ -7,6 +7,10 @@ returned), inputs resident in HBM.  Prints one JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
+With a chunked workload (the 256K-token sequence run as 32 chained calls) a
+step is the whole chain; with the decode workload a step is its 128
+single-token steps.  Those lines add per-call / per-decode-step times.
+
 The metric is scan elements per second, B*L*D*N / step time, in GElem/s.  The
 roofline object reports the algorithmic HBM bytes of one launch (every input
 read once, y and hT written once) over the launch's average duration, timed
@@ -104,6 +108,140 @@ def cpu_baseline(w, inp, max_threads=16):
     }
 
 
+def _roofline(alg_bytes, kern_s, kernel):
+    achieved = alg_bytes / kern_s / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel,
+            "kernel_avg_us": round(kern_s * 1e6, 2), "algorithmic_bytes": alg_bytes}
+
+
+def bench_chunked(w, args, ssm, torch):
+    """A long sequence run as `w.chunks` calls, each starting from the previous
+    call's final state (state buffers alternate, so calls may split time).
+    One step = all the calls over the whole sequence."""
+    import workloads
+    dev = torch.device("cuda:0")
+    log(f"workload {w.describe()}")
+    inp = workloads.make_inputs(w)
+    Lc = w.seqlen // w.chunks
+    chunks = []
+    for c in range(w.chunks):
+        sl = slice(c * Lc, (c + 1) * Lc)
+        chunks.append({k: (inp[k][:, sl].contiguous().to(dev) if inp[k] is not None else None)
+                       for k in ("x", "delta", "z", "B", "C")})
+    A, D, bias = (inp[k].to(dev) for k in ("A", "D", "delta_bias"))
+    ys = [torch.empty_like(ch["x"]) for ch in chunks]
+    hs = [torch.zeros(w.batch, w.dim, w.dstate, dtype=torch.float32, device=dev) for _ in range(2)]
+    stream = torch.cuda.current_stream(dev)
+
+    def one_pass(events=None):
+        hs[0].zero_()
+        for c, ch in enumerate(chunks):
+            h_in, h_out = hs[c % 2], hs[(c + 1) % 2]
+            if events is not None:
+                events[c][0].record(stream)
+            ssm.scan_fwd(ch["x"], ch["delta"], A, ch["B"], ch["C"], D, ch["z"], bias,
+                         h_in if c > 0 else None, out=ys[c], final_state_out=h_out)
+            if events is not None:
+                events[c][1].record(stream)
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    steps = max(args.steps, 1)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in chunks] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one_pass(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    call_ms = [a.elapsed_time(b) for e in evs for a, b in e]
+    per_call_s = float(np.mean(call_ms)) * 1e-3
+    es = 2 if "bfloat16" in str(w.dtype) else 4
+    bld, bln = w.batch * Lc * w.dim, w.batch * Lc * w.dstate
+    state = w.batch * w.dim * w.dstate * 4
+    call_bytes = (4 if w.gate else 3) * bld * es + 2 * bln * es + w.dim * w.dstate * 4 + 2 * w.dim * 4 + 2 * state
+    probe = ssm.make_args(chunks[1]["x"], chunks[1]["delta"], A, chunks[1]["B"], chunks[1]["C"], D,
+                          chunks[1]["z"], bias, hs[0], hs[1], ys[1])
+    nbytes = ssm.workspace_bytes(probe)
+    if nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        probe.workspace, probe.workspace_bytes = ws.data_ptr(), nbytes
+    plan = ssm.plan(probe)
+    ms_per_step = elapsed * 1e3 / steps
+    return {
+        "metric": "scan GElem/s (B*L*D*N) over the chained calls + % HBM roofline per call",
+        "value": round(w.elems / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GElem/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
+                   "io_dtype": str(w.dtype).replace("torch.", ""), "gate": w.gate, "calls": w.chunks,
+                   "call_seqlen": Lc, "plan": {"variant": plan[0], "time_splits": plan[1]}},
+        "per_call_us": round(per_call_s * 1e6, 2),
+        "calls_total_kernel_us": round(per_call_s * w.chunks * 1e6, 2),
+        "roofline": _roofline(call_bytes, per_call_s, "scan_nsplit_kernel (+ state-only pass)"),
+    }
+
+
+def bench_decode(w, args, ssm, torch):
+    """`w.steps` successive single-token steps, updating one fp32 state in place
+    (fresh inputs each step, generated and moved to the device beforehand).
+    One bench step = all the decode steps."""
+    import workloads
+    dev = torch.device("cuda:0")
+    log(f"workload {w.describe()}")
+    inp = workloads.make_inputs(w, seqlen=1)
+    A, D, bias = (inp[k].to(dev) for k in ("A", "D", "delta_bias"))
+    h = inp["h0"].to(dev)
+    steps_in = []
+    for t in range(w.steps):
+        st = workloads.make_decode_step(w, t)
+        steps_in.append({k: (v.to(dev) if v is not None else None) for k, v in st.items()})
+    y = torch.empty_like(steps_in[0]["x"])
+    stream = torch.cuda.current_stream(dev)
+
+    def one_pass(events=None):
+        for t, st in enumerate(steps_in):
+            if events is not None:
+                events[t][0].record(stream)
+            ssm.scan_fwd(st["x"], st["delta"], A, st["B"], st["C"], D, st["z"], bias, h, out=y,
+                         final_state_out=h)
+            if events is not None:
+                events[t][1].record(stream)
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    passes = max(args.steps, 1)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in steps_in] for _ in range(passes)]
+    t0 = time.perf_counter()
+    for i in range(passes):
+        one_pass(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    step_ms = [a.elapsed_time(b) for e in evs for a, b in e]
+    per_step_s = float(np.mean(step_ms)) * 1e-3
+    es = 2 if "bfloat16" in str(w.dtype) else 4
+    bd = w.batch * w.dim
+    step_bytes = (4 if w.gate else 3) * bd * es + 2 * w.batch * w.dstate * es + w.dim * w.dstate * 4 + \
+        2 * w.dim * 4 + 2 * bd * w.dstate * 4
+    ms_per_pass = elapsed * 1e3 / passes
+    return {
+        "metric": "scan GElem/s (B*D*N per token step) + % HBM roofline per step",
+        "value": round(w.elems / (ms_per_pass * 1e-3) / 1e9, 2), "unit": "GElem/s", "n_gpus": 1,
+        "steps": passes, "warmup": args.warmup, "ms_per_step": round(ms_per_pass, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
+                   "io_dtype": str(w.dtype).replace("torch.", ""), "gate": w.gate, "decode_steps": w.steps,
+                   "plan": {"variant": "decode", "in_place": True}},
+        "per_step_kernel_us": round(per_step_s * 1e6, 2),
+        "wall_us_per_decode_step": round(ms_per_pass * 1e3 / w.steps, 2),
+        "roofline": _roofline(step_bytes, per_step_s, "scan_decode_kernel"),
+    }
+
+
 def main():
     import workloads
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -143,10 +281,12 @@ def main():
         return
 
     w = workloads.BY_NAME[args.workload]
-    if w.steps or w.chunks > 1:
-        print("bench.py times single-call workloads; the chunked and decode workloads are parity cases",
-              file=sys.stderr)
-        sys.exit(2)
+    if w.chunks > 1:
+        print(json.dumps(bench_chunked(w, args, ssm, torch)), flush=True)
+        return
+    if w.steps:
+        print(json.dumps(bench_decode(w, args, ssm, torch)), flush=True)
+        return
     dev = torch.device("cuda:0")
     log(f"workload {w.describe()}")
     t0 = time.time()
