@@ -9,7 +9,7 @@
 // per-channel scalars (softplus, gate) are recomputed by the Q lanes of a
 // channel; the readout sum over n is reduced across them with lane shuffles.
 // h0 and hT may be the same buffer: every lane reads its own states before
-// writing them.
+// writing them (each state float4 belongs to exactly one lane and one row).
 #include "device_common.hpp"
 #include "scan_internal.hpp"
 
@@ -30,54 +30,79 @@ __device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float out[4])
   out[2] = __uint_as_float(v.y << 16); out[3] = __uint_as_float(v.y & 0xffff0000u);
 }
 
+#ifndef SSM_DECODE_ROWS
+#define SSM_DECODE_ROWS 2
+#endif
+// Batch rows per thread: every thread keeps R independent state float4 loads
+// in flight (the step is bound by that traffic), with the row's scalar loads
+// issued first.
+constexpr int kDecodeRows = SSM_DECODE_ROWS;
+
 template <typename S, int Q>
 __global__ __launch_bounds__(256) void scan_decode_kernel(
     const S* __restrict__ x, const S* __restrict__ dl, const float* __restrict__ A,
     const S* __restrict__ Bm, const S* __restrict__ Cm, const float* __restrict__ Dsk,
     const S* __restrict__ z, const float* __restrict__ bias, const float* h0, float* hT,
-    S* __restrict__ y, int64_t D) {
+    S* __restrict__ y, int64_t Bsz, int64_t D) {
   constexpr int N = 4 * Q;
   constexpr int CH = 256 / Q;  // channels per block
-  const int64_t b = blockIdx.y;
+  constexpr int R = kDecodeRows;
   const int q = threadIdx.x % Q;
   const int64_t dq = static_cast<int64_t>(blockIdx.x) * CH + threadIdx.x / Q;
-  const bool active = dq < D;
-  const int64_t d = active ? dq : D - 1;  // inactive lanes read a valid channel, write nothing
-  const int64_t i = b * D + d;              // (b, t=0, d) and (b, d) share this index
-
-  const float xv = to_f32(x[i]);
-  const float dt = softplus_f32(to_f32(dl[i]) + (bias ? bias[d] : 0.0f));
-  const float u = dt * xv;
-
-  float a[4], hv[4], Bv[4], Cv[4];
+  const bool dact = dq < D;
+  const int64_t d = dact ? dq : D - 1;  // inactive lanes read a valid channel, write nothing
+  float a[4];
   {
     const float4 av = *reinterpret_cast<const float4*>(A + d * N + 4 * q);
-    a[0] = av.x; a[1] = av.y; a[2] = av.z; a[3] = av.w;
+    a[0] = av.x * kLog2e; a[1] = av.y * kLog2e; a[2] = av.z * kLog2e; a[3] = av.w * kLog2e;
   }
-  if (h0) {
-    const float4 hv4 = *reinterpret_cast<const float4*>(h0 + i * N + 4 * q);
-    hv[0] = hv4.x; hv[1] = hv4.y; hv[2] = hv4.z; hv[3] = hv4.w;
-  } else {
-    hv[0] = hv[1] = hv[2] = hv[3] = 0.0f;
-  }
-  load4<S>(Bm + b * N + 4 * q, Bv);
-  load4<S>(Cm + b * N + 4 * q, Cv);
-  float acc = 0.0f;
+  const float bias_d = bias ? bias[d] : 0.0f;
+  const float D_d = Dsk ? Dsk[d] : 0.0f;
+
+  float hv[R][4], xv[R], rawd[R];
+  bool act[R];
+  int64_t idx[R], brow[R];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float ab = fast_exp2(dt * (a[k] * kLog2e));
-    hv[k] = __builtin_fmaf(ab, hv[k], u * Bv[k]);
-    acc = __builtin_fmaf(Cv[k], hv[k], acc);
+  for (int r = 0; r < R; ++r) {
+    const int64_t bq = static_cast<int64_t>(blockIdx.y) * R + r;
+    act[r] = dact && bq < Bsz;
+    brow[r] = bq < Bsz ? bq : Bsz - 1;
+    idx[r] = brow[r] * D + d;  // (b, t=0, d) and (b, d) share this index
+    if (h0) {
+      const float4 hv4 = *reinterpret_cast<const float4*>(h0 + idx[r] * N + 4 * q);
+      hv[r][0] = hv4.x; hv[r][1] = hv4.y; hv[r][2] = hv4.z; hv[r][3] = hv4.w;
+    } else {
+      hv[r][0] = hv[r][1] = hv[r][2] = hv[r][3] = 0.0f;
+    }
+    xv[r] = to_f32(x[idx[r]]);
+    rawd[r] = to_f32(dl[idx[r]]);
   }
-  // Sum the Q partial readouts of this channel (lanes q = 0..Q-1 are adjacent).
 #pragma unroll
-  for (int off = 1; off < Q; off <<= 1) acc += __shfl_xor(acc, off, 64);
-  if (active) {
-    if (hT) *reinterpret_cast<float4*>(hT + i * N + 4 * q) = make_float4(hv[0], hv[1], hv[2], hv[3]);
-    if (q == 0) {
-      if (Dsk) acc = __builtin_fmaf(Dsk[d], xv, acc);
-      if (z) acc *= silu_f32(to_f32(z[i]));
-      store_elem(y + i, acc);
+  for (int r = 0; r < R; ++r) {
+    const int64_t b = brow[r];
+    float Bv[4], Cv[4];
+    load4<S>(Bm + b * N + 4 * q, Bv);
+    load4<S>(Cm + b * N + 4 * q, Cv);
+    const float dt = softplus_f32(rawd[r] + bias_d);
+    const float u = dt * xv[r];
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float ab = fast_exp2(dt * a[k]);
+      hv[r][k] = __builtin_fmaf(ab, hv[r][k], u * Bv[k]);
+      acc = __builtin_fmaf(Cv[k], hv[r][k], acc);
+    }
+    // Sum the Q partial readouts of this channel (lanes q = 0..Q-1 are adjacent).
+#pragma unroll
+    for (int off = 1; off < Q; off <<= 1) acc += __shfl_xor(acc, off, 64);
+    if (act[r]) {
+      if (hT)
+        *reinterpret_cast<float4*>(hT + idx[r] * N + 4 * q) = make_float4(hv[r][0], hv[r][1], hv[r][2], hv[r][3]);
+      if (q == 0) {
+        acc = __builtin_fmaf(D_d, xv[r], acc);
+        if (z) acc *= silu_f32(to_f32(z[idx[r]]));
+        store_elem(y + idx[r], acc);
+      }
     }
   }
 }
@@ -85,11 +110,13 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(
 template <typename S, int Q>
 hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   constexpr int CH = 256 / Q;
-  dim3 grid(static_cast<unsigned>((p.dim + CH - 1) / CH), static_cast<unsigned>(p.batch));
+  dim3 grid(static_cast<unsigned>((p.dim + CH - 1) / CH),
+            static_cast<unsigned>((p.batch + kDecodeRows - 1) / kDecodeRows));
   hipLaunchKernelGGL((scan_decode_kernel<S, Q>), grid, dim3(256), 0, stream,
                      static_cast<const S*>(p.x), static_cast<const S*>(p.delta), p.A,
                      static_cast<const S*>(p.B), static_cast<const S*>(p.C), p.D,
-                     static_cast<const S*>(p.z), p.delta_bias, p.h0, p.hT, static_cast<S*>(p.y), p.dim);
+                     static_cast<const S*>(p.z), p.delta_bias, p.h0, p.hT, static_cast<S*>(p.y), p.batch,
+                     p.dim);
   return hipGetLastError();
 }
 
