@@ -37,6 +37,14 @@ class _Args(ctypes.Structure):
     ]
 
 
+class _Grads(ctypes.Structure):
+    _fields_ = [
+        ("dy", _dp), ("dhT", _dp),
+        ("dx", _dp), ("ddelta", _dp), ("dA", _dp), ("dB", _dp), ("dC", _dp),
+        ("dD", _dp), ("dz", _dp), ("ddelta_bias", _dp), ("dh0", _dp),
+    ]
+
+
 def lib_path(mutant: int = 0, out_dir: str | None = None) -> str:
     d = out_dir or _BUILD
     name = "liboracle.so" if mutant == 0 else f"liboracle_mutant{mutant}.so"
@@ -65,6 +73,8 @@ class Oracle:
         self._lib.oracle_scan_f64.restype = ctypes.c_int
         self._lib.oracle_assoc_scan_f64.argtypes = [ctypes.POINTER(_Args)]
         self._lib.oracle_assoc_scan_f64.restype = ctypes.c_int
+        self._lib.oracle_scan_bwd_f64.argtypes = [ctypes.POINTER(_Args), ctypes.POINTER(_Grads)]
+        self._lib.oracle_scan_bwd_f64.restype = ctypes.c_int
         self._lib.oracle_softplus_vec.argtypes = [_dp, _dp, ctypes.c_int64]
         self._lib.oracle_softplus_vec.restype = None
         self._lib.oracle_mutant_id.restype = ctypes.c_int
@@ -128,6 +138,34 @@ class Oracle:
         del keep
         return y, hT
 
+    def scan_bwd(self, x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *, dy, dhT=None):
+        """Gradients of the scalar loss sum(dy * y) + sum(dhT * hT) with respect
+        to every input, as a dict of float64 numpy arrays (keys x, delta, A, B,
+        C, D, z, delta_bias, h0; an absent optional input has no entry, except
+        h0, whose gradient is always returned)."""
+        args, keep, _, _ = self._pack(x, delta, A, B, C, D, z, delta_bias, h0, False)
+        xx, dd, AA, BB, CC, DD, zz, bb, hh = keep[:9]
+        dy = self._f64(dy)
+        dhT = self._f64(dhT)
+        assert dy.shape == xx.shape and (dhT is None or dhT.shape == (xx.shape[0], xx.shape[2], AA.shape[1]))
+        out = {"x": np.zeros_like(xx), "delta": np.zeros_like(dd), "A": np.zeros_like(AA),
+               "B": np.zeros_like(BB), "C": np.zeros_like(CC),
+               "h0": np.zeros((xx.shape[0], xx.shape[2], AA.shape[1]), dtype=np.float64)}
+        if DD is not None:
+            out["D"] = np.zeros_like(DD)
+        if zz is not None:
+            out["z"] = np.zeros_like(zz)
+        if bb is not None:
+            out["delta_bias"] = np.zeros_like(bb)
+        p = self._ptr
+        g = _Grads(p(dy), p(dhT), p(out["x"]), p(out["delta"]), p(out["A"]), p(out["B"]), p(out["C"]),
+                   p(out.get("D")), p(out.get("z")), p(out.get("delta_bias")), p(out["h0"]))
+        rc = self._lib.oracle_scan_bwd_f64(ctypes.byref(args), ctypes.byref(g))
+        if rc != 0:
+            raise RuntimeError("oracle_scan_bwd_f64 failed")
+        del keep
+        return out
+
     def softplus(self, v):
         v = self._f64(v)
         out = np.empty_like(v)
@@ -157,6 +195,10 @@ def scan(*args, **kw):
 
 def assoc_scan(*args, **kw):
     return get().assoc_scan(*args, **kw)
+
+
+def scan_bwd(*args, **kw):
+    return get().scan_bwd(*args, **kw)
 
 
 def softplus(v):

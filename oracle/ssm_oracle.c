@@ -23,6 +23,9 @@
  * (B, D, N).  All arrays are dense row-major fp64 holding exactly the values
  * the device receives (bf16/fp32 widened without rounding).
  *
+ * It also holds the backward pass (gradients of a scalar loss), see
+ * oracle_scan_bwd_f64 below.
+ *
  * Build-time mutations (ORACLE_MUTANT=k, k>0) exist only so the test suite
  * can show that its closed-form pins catch plausible mistakes; the default
  * build (k=0) is the oracle.
@@ -246,6 +249,124 @@ int oracle_assoc_scan_f64(const oracle_args *a) {
       }
     }
   free(pa); free(pb); free(qa); free(qb); free(hs);
+  return 0;
+}
+
+/* ---- Backward pass (gradients of a scalar loss through the forward) ----
+ *
+ * Given dL/dy (B, L, D) and, optionally, dL/dhT (B, D, N), returns dL/d of
+ * every input of oracle_scan_f64.  This is reverse-mode differentiation of
+ * the same recurrence (sections 2.2, 3.1, 3.3, 3.4 of the page above),
+ * worked out by hand per chain (b, d):
+ *   forward  v = raw + bias, delta = softplus(v), a_n = exp(delta A_n),
+ *            u = delta x, h_t = a h_{t-1} + u B_t, s = C_t . h_t,
+ *            y0 = s + D x, y = y0 g with g = SiLU(z) (g = 1 without a gate);
+ *   reverse  (t = L-1 .. 0, carry_n = dL/dhT_n at the start)
+ *            gy0 = dy g,  dz = dy y0 SiLU'(z),  dD += gy0 x,
+ *            lambda_n = gy0 C_t,n + carry_n           (dL/dh_t,n)
+ *            ga_n = lambda_n h_{t-1,n},  dA_n += ga_n a_n delta,
+ *            gdelta = sum_n ga_n a_n A_n + x sum_n lambda_n B_t,n,
+ *            dB_t,n += lambda_n u,  dC_t,n += gy0 h_t,n,
+ *            dx = gy0 D + delta sum_n lambda_n B_t,n,
+ *            draw = gdelta sigmoid(v),  dbias += draw,
+ *            carry_n = a_n lambda_n;
+ *            after t = 0: dh0_n = carry_n.
+ * SiLU'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))); softplus' = sigmoid.
+ * Sums over b, t and d run in increasing index order.  Single-threaded: the
+ * reductions over channels (dB, dC) and over batch rows (dA, dD, dbias)
+ * would otherwise need merging; inputs here are small.
+ * Pinned in tests/test_oracle_bwd.py by central finite differences of
+ * oracle_scan_f64 (an independent computation) on every input element. */
+typedef struct {
+  const double *dy;   /* (B, L, D) required           */
+  const double *dhT;  /* (B, D, N) or NULL (zero)      */
+  double *dx, *ddelta, *dA, *dB, *dC, *dD, *dz, *ddelta_bias, *dh0;  /* each NULL or sized like its input */
+} oracle_grads;
+
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+int oracle_scan_bwd_f64(const oracle_args *a, const oracle_grads *g) {
+  if (!a || !g || !a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !g->dy) return -1;
+  if (a->batch < 0 || a->seqlen < 0 || a->dim < 0 || a->dstate <= 0) return -1;
+  const int64_t Bn = a->batch, L = a->seqlen, D = a->dim, N = a->dstate;
+  const size_t Lz = (size_t)(L > 0 ? L : 1);
+  double *hs = (double *)malloc(sizeof(double) * Lz * (size_t)N);  /* h_t for t = 0..L-1 */
+  double *dl = (double *)malloc(sizeof(double) * Lz);              /* delta_t */
+  double *carry = (double *)malloc(sizeof(double) * (size_t)N);
+  if (!hs || !dl || !carry) { free(hs); free(dl); free(carry); return -1; }
+  if (g->dA) memset(g->dA, 0, sizeof(double) * (size_t)(D * N));
+  if (g->dB) memset(g->dB, 0, sizeof(double) * (size_t)(Bn * L * N));
+  if (g->dC) memset(g->dC, 0, sizeof(double) * (size_t)(Bn * L * N));
+  if (g->dD) memset(g->dD, 0, sizeof(double) * (size_t)D);
+  if (g->ddelta_bias) memset(g->ddelta_bias, 0, sizeof(double) * (size_t)D);
+  for (int64_t b = 0; b < Bn; ++b)
+    for (int64_t d = 0; d < D; ++d) {
+      const double bias = a->delta_bias ? a->delta_bias[d] : 0.0;
+      const double Dd = a->Dskip ? a->Dskip[d] : 0.0;
+      /* forward, keeping every state */
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t i = (b * L + t) * D + d;
+        dl[t] = oracle_softplus(a->delta[i] + bias);
+        for (int64_t n = 0; n < N; ++n) {
+          const double hp = t > 0 ? hs[(t - 1) * N + n] : (a->h0 ? a->h0[(b * D + d) * N + n] : 0.0);
+          hs[t * N + n] = exp(dl[t] * a->A[d * N + n]) * hp + dl[t] * a->x[i] * a->Bm[(b * L + t) * N + n];
+        }
+      }
+      /* reverse */
+      for (int64_t n = 0; n < N; ++n) carry[n] = g->dhT ? g->dhT[(b * D + d) * N + n] : 0.0;
+#if ORACLE_MUTANT == 17
+      for (int64_t n = 0; n < N; ++n) carry[n] = 0.0; /* dL/dhT dropped */
+#endif
+      for (int64_t t = L - 1; t >= 0; --t) {
+        const int64_t i = (b * L + t) * D + d;
+        const double xv = a->x[i], v = a->delta[i] + bias, dt = dl[t];
+        double s = 0.0;
+        for (int64_t n = 0; n < N; ++n) s += a->Cm[(b * L + t) * N + n] * hs[t * N + n];
+        const double y0 = s + Dd * xv;
+        double gate = 1.0;
+        if (a->z) {
+          const double zv = a->z[i], sz = sigmoid(zv);
+          gate = zv * sz;
+          if (g->dz) g->dz[i] = g->dy[i] * y0 * sz * (1.0 + zv * (1.0 - sz));
+        }
+        const double gy0 = g->dy[i] * gate;
+        if (g->dD) g->dD[d] += gy0 * xv;
+        double gu = 0.0, gdel = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          const int64_t bn = (b * L + t) * N + n;
+          const double An = a->A[d * N + n], an = exp(dt * An);
+          const double hp = t > 0 ? hs[(t - 1) * N + n] : (a->h0 ? a->h0[(b * D + d) * N + n] : 0.0);
+          const double lam = gy0 * a->Cm[bn] + carry[n];
+          const double ga = lam * hp;
+          if (g->dA) g->dA[d * N + n] += ga * an * dt;
+#if ORACLE_MUTANT == 16
+          gdel -= ga * an * An; /* sign of the decay term */
+#else
+          gdel += ga * an * An;
+#endif
+          gu += lam * a->Bm[bn];
+          if (g->dB) g->dB[bn] += lam * dt * xv;
+          if (g->dC) g->dC[bn] += gy0 * hs[t * N + n];
+#if ORACLE_MUTANT == 15
+          carry[n] = lam; /* decay missing from the carried adjoint */
+#else
+          carry[n] = an * lam;
+#endif
+        }
+        gdel += gu * xv;
+        if (g->dx) g->dx[i] = gy0 * Dd + gu * dt;
+#if ORACLE_MUTANT == 18
+        const double graw = gdel; /* softplus derivative missing */
+#else
+        const double graw = gdel * sigmoid(v);
+#endif
+        if (g->ddelta) g->ddelta[i] = graw;
+        if (g->ddelta_bias) g->ddelta_bias[d] += graw;
+      }
+      if (g->dh0)
+        for (int64_t n = 0; n < N; ++n) g->dh0[(b * D + d) * N + n] = carry[n];
+    }
+  free(hs); free(dl); free(carry);
   return 0;
 }
 
