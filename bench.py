@@ -242,6 +242,96 @@ def bench_decode(w, args, ssm, torch):
     }
 
 
+def bench_backward(w, args, ssm, torch):
+    """One step = one ssm_scan_bwd over the workload: every gradient (x, delta,
+    z, A, B, C, D, delta_bias, h0) from dy (and dhT when the workload returns
+    the final state), states recomputed from the inputs inside the call."""
+    import workloads
+    dev = torch.device("cuda:0")
+    log(f"workload {w.describe()} (backward)")
+    inp = workloads.make_inputs(w)
+    cot = workloads.make_cotangents(w)
+    d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+    dy = cot["dy"].to(dev)
+    dhT = cot["dhT"].to(dev) if w.final_state else None
+    names = ("x", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0")
+    grads = {k: torch.empty_like(d[k]) for k in names if k != "h0" and d[k] is not None}
+    grads["h0"] = torch.empty(w.batch, w.dim, w.dstate, dtype=torch.float32, device=dev)
+    a0 = ssm.make_bwd_args(*(d[k] for k in names), dy=dy, dhT=dhT, grads=grads, time_splits=args.time_splits)
+    nbytes = ssm.bwd_workspace_bytes(a0)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    a0.workspace, a0.workspace_bytes = ws.data_ptr(), nbytes
+    splits = ssm.bwd_plan(a0)
+    log(f"time segments {splits}, workspace {nbytes} B")
+    lib = ssm.lib()
+    import ctypes
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        rc = lib.ssm_scan_bwd(ctypes.byref(a0), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"ssm_scan_bwd: {ssm.strerror(rc)}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    steps = max(args.steps, 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    call_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    es = 2 if "bfloat16" in str(w.dtype) else 4
+    bld, bln, bdn = w.batch * w.seqlen * w.dim, w.batch * w.seqlen * w.dstate, w.batch * w.dim * w.dstate
+    n_tok = 4 if w.gate else 3  # (B, L, D) tensors read: x, delta, dy, (z)
+    alg = (n_tok + n_tok - 1) * bld * es  # and written: dx, ddelta, (dz)
+    alg += 4 * bln * es  # B, C read; dB, dC written
+    alg += 2 * w.dim * w.dstate * 4 + 4 * w.dim * 4  # A read, dA written; D, bias read, dD, dbias written
+    alg += bdn * 4 * (2 if w.final_state else 1) + (bdn * 4 if w.h0_std > 0 else 0)  # dhT, dh0, h0
+    ms_per_step = elapsed * 1e3 / steps
+    out = {
+        "metric": "backward scan GElem/s (B*L*D*N) + % HBM roofline",
+        "value": round(w.elems / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GElem/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "pass": "backward", "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
+                   "dstate": w.dstate, "io_dtype": str(w.dtype).replace("torch.", ""), "gate": w.gate,
+                   "time_splits": splits, "workspace_bytes": nbytes},
+        "roofline": _roofline(alg, call_s, "ssm_scan_bwd (local, combine, main, two reductions)"),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        nd = min(w.dim, 512)
+        sub = {k: v for k, v in inp.items()}
+        for k in ("x", "delta", "z"):
+            if sub[k] is not None:
+                sub[k] = sub[k][:1, :, :nd]
+        for k in ("B", "C"):
+            sub[k] = sub[k][:1]
+        sub["A"] = sub["A"][:nd]
+        for k in ("D", "delta_bias"):
+            sub[k] = sub[k][:nd]
+        if sub["h0"] is not None:
+            sub["h0"] = sub["h0"][:1, :nd]
+        dys = cot["dy"][:1, :, :nd]
+        dhs = cot["dhT"][:1, :nd] if w.final_state else None
+        log(f"cpu baseline (oracle backward, batch row 0, {nd} channels) ...")
+        t = time.perf_counter()
+        oracle.scan_bwd(*(sub[k] for k in names), dy=dys, dhT=dhs)
+        sec = time.perf_counter() - t
+        el = w.seqlen * nd * w.dstate
+        out["cpu_baseline"] = {
+            "value": round(el / sec / 1e9, 5), "unit": "GElem/s", "cores": 1, "kind": "oracle",
+            "sample": f"batch row 0, channels 0..{nd - 1}, all {w.seqlen} tokens ({el} elements), fp64 "
+                      f"reverse-mode oracle, single thread; {sec:.2f} s including input widening",
+        }
+    return out
+
+
 def main():
     import workloads
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -253,6 +343,7 @@ def main():
     ap.add_argument("--time-splits", type=int, default=0)
     ap.add_argument("--generic-a", action="store_true", help="never take the structured-decay path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true", help="time ssm_scan_bwd (all gradients) instead")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the scan, copy a MIB-MiB buffer `steps` times (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -281,6 +372,12 @@ def main():
         return
 
     w = workloads.BY_NAME[args.workload]
+    if args.backward:
+        if w.chunks > 1 or w.steps:
+            print("--backward runs the single-call workloads", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(bench_backward(w, args, ssm, torch)), flush=True)
+        return
     if w.chunks > 1:
         print(json.dumps(bench_chunked(w, args, ssm, torch)), flush=True)
         return

@@ -108,6 +108,75 @@ int64_t ssm_scan_workspace_bytes(const ssm_scan_args *args);
  * variant * 65536 + time_splits.  Host-only.  Negative on invalid arguments. */
 int64_t ssm_scan_plan(const ssm_scan_args *args);
 
+/* ---- backward -------------------------------------------------------------
+ * Gradients of a scalar loss through the forward above, given dL/dy (and
+ * optionally dL/dhT): reverse-mode differentiation of the sections 2.2, 3.1,
+ * 3.3 and 3.4 operations, walking the recurrence from t = L-1 down to 0 with
+ * the state adjoint g (g starts as dL/dhT, each token maps it to
+ * exp(delta A) o (gy0 C_t + g), where gy0 = dL/dy_t SiLU(z_t)).
+ *
+ * The forward's inputs are passed again exactly as they were given to
+ * ssm_scan_fwd (the states are recomputed, nothing is saved between the two
+ * calls).  Every gradient pointer is optional: NULL skips that output.  Shapes
+ * and dtypes of the gradients are those of the matching input: dx, ddelta, dz
+ * (B, L, D) and dB, dC (B, L, N) in `dtype`; dA (D, N), dD (D),
+ * ddelta_bias (D) and dh0 (B, D, N) fp32.  ddelta is the gradient with
+ * respect to the raw step size (before bias and softplus).  dA, dD,
+ * ddelta_bias sum over batch rows (and dB, dC over channels) inside the
+ * library, in a fixed order: the results are deterministic.  Gradients of
+ * inputs that were not given (D, z, delta_bias, h0 NULL) are those of a zero
+ * input: dz needs z, the others are still defined.
+ *
+ * Limits of this version: dstate N in 1..16 (SSM_ERR_DSTATE otherwise). */
+typedef struct ssm_scan_bwd_args {
+  int64_t batch, seqlen, dim, dstate; /* as ssm_scan_args; N <= 16           */
+  int32_t dtype;                      /* ssm_dtype of x, delta, B, C, z, dy and the (B, L, .) gradients */
+  int32_t flags;                      /* ssm_flags; SSM_FLAG_GENERIC_A is accepted and has no effect */
+  const void *x;           /* (B, L, D)                                        required */
+  const void *delta;       /* (B, L, D) raw step size                          required */
+  const float *A;          /* (D, N)                                           required */
+  const void *B;           /* (B, L, N)                                        required */
+  const void *C;           /* (B, L, N)                                        required */
+  const float *D;          /* (D) or NULL                                               */
+  const void *z;           /* (B, L, D) or NULL                                         */
+  const float *delta_bias; /* (D) or NULL                                               */
+  const float *h0;         /* (B, D, N) or NULL                                         */
+  const void *dy;          /* (B, L, D) dL/dy                                  required */
+  const float *dhT;        /* (B, D, N) dL/dhT, or NULL (= zeros)                       */
+  void *dx;                /* (B, L, D) out                                             */
+  void *ddelta;            /* (B, L, D) out                                             */
+  float *dA;               /* (D, N) out                                                */
+  void *dB;                /* (B, L, N) out                                             */
+  void *dC;                /* (B, L, N) out                                             */
+  float *dD;               /* (D) out                                                   */
+  void *dz;                /* (B, L, D) out; requires z                                 */
+  float *ddelta_bias;      /* (D) out                                                   */
+  float *dh0;              /* (B, D, N) out                                             */
+  void *workspace;         /* device scratch of ssm_scan_bwd_workspace_bytes bytes       */
+  int64_t workspace_bytes; /* its size                                                  */
+  int32_t time_splits;     /* segments per sequence: 0 = automatic, >= 1 = that many    */
+  int32_t reserved;        /* must be 0                                                 */
+} ssm_scan_bwd_args;
+
+/* Backward scan.  Errors as for ssm_scan_fwd, plus: SSM_ERR_NULL when a
+ * required pointer is NULL or dz is given without z; SSM_ERR_ALIAS when a
+ * gradient overlaps an input or another gradient; SSM_ERR_WORKSPACE when the
+ * workspace is NULL or smaller than ssm_scan_bwd_workspace_bytes (required
+ * whenever B * L * D > 0); SSM_ERR_VARIANT for unknown flags, a negative
+ * time_splits or reserved != 0.  The workspace is overwritten; its contents
+ * on entry do not matter.  Problems with L == 0 give dh0 = dhT (or zeros) and
+ * zero dA, dD, ddelta_bias; with B == 0 or D == 0 every non-empty gradient is
+ * zero. */
+int ssm_scan_bwd(const ssm_scan_bwd_args *args, void *stream);
+
+/* Bytes of workspace ssm_scan_bwd needs for these arguments.  Host-only.
+ * Negative SSM_ERR_* code for invalid arguments. */
+int64_t ssm_scan_bwd_workspace_bytes(const ssm_scan_bwd_args *args);
+
+/* Number of time segments ssm_scan_bwd would use.  Host-only.  Negative on
+ * invalid arguments. */
+int64_t ssm_scan_bwd_plan(const ssm_scan_bwd_args *args);
+
 /* Static, human-readable text for a status code. */
 const char *ssm_scan_strerror(int code);
 

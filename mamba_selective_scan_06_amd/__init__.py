@@ -31,8 +31,8 @@ VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 FLAG_GENERIC_A = 1
 
 # Exported symbols the header declares (checked by the tests).
-EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_scan_strerror",
-           "ssm_scan_abi_version")
+EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_scan_bwd",
+           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd_plan", "ssm_scan_strerror", "ssm_scan_abi_version")
 
 
 class ScanArgs(ctypes.Structure):
@@ -48,6 +48,27 @@ class ScanArgs(ctypes.Structure):
         ("time_splits", ctypes.c_int32),
     ]
 
+
+class ScanBwdArgs(ctypes.Structure):
+    """Mirror of ssm_scan_bwd_args in include/ssm_scan.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("delta", ctypes.c_void_p), ("A", ctypes.c_void_p),
+        ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p),
+        ("z", ctypes.c_void_p), ("delta_bias", ctypes.c_void_p), ("h0", ctypes.c_void_p),
+        ("dy", ctypes.c_void_p), ("dhT", ctypes.c_void_p),
+        ("dx", ctypes.c_void_p), ("ddelta", ctypes.c_void_p), ("dA", ctypes.c_void_p),
+        ("dB", ctypes.c_void_p), ("dC", ctypes.c_void_p), ("dD", ctypes.c_void_p),
+        ("dz", ctypes.c_void_p), ("ddelta_bias", ctypes.c_void_p), ("dh0", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
+        ("time_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+# Gradient outputs of the backward: name of the input they belong to -> struct field.
+GRAD_FIELDS = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
+               "delta_bias": "ddelta_bias", "h0": "dh0"}
 
 _lib = None
 
@@ -67,6 +88,13 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_workspace_bytes.restype = ctypes.c_int64
         L.ssm_scan_plan.argtypes = [P]
         L.ssm_scan_plan.restype = ctypes.c_int64
+        PB = ctypes.POINTER(ScanBwdArgs)
+        L.ssm_scan_bwd.argtypes = [PB, ctypes.c_void_p]
+        L.ssm_scan_bwd.restype = ctypes.c_int
+        L.ssm_scan_bwd_workspace_bytes.argtypes = [PB]
+        L.ssm_scan_bwd_workspace_bytes.restype = ctypes.c_int64
+        L.ssm_scan_bwd_plan.argtypes = [PB]
+        L.ssm_scan_bwd_plan.restype = ctypes.c_int64
         L.ssm_scan_strerror.argtypes = [ctypes.c_int]
         L.ssm_scan_strerror.restype = ctypes.c_char_p
         L.ssm_scan_abi_version.argtypes = []
@@ -187,4 +215,89 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
     return y
 
 
-__all__ = ["scan_fwd", "make_args", "plan", "workspace_bytes", "lib", "strerror", "ScanArgs", "EXPORTS"]
+def make_bwd_args(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *, dy, dhT=None,
+                  grads=None, workspace=None, time_splits=0) -> ScanBwdArgs:
+    """Check shapes/dtypes/devices and fill an ssm_scan_bwd_args.  `grads` maps
+    input names (x, delta, A, B, C, D, z, delta_bias, h0) to output tensors."""
+    fa = make_args(x, delta, A, B, C, D, z, delta_bias, h0)
+    bsz, L, dim = x.shape
+    N = A.shape[1]
+    io, dev, f32 = x.dtype, x.device, torch.float32
+    _check("dy", dy, (bsz, L, dim), io, dev)
+    _check("dhT", dhT, (bsz, dim, N), f32, dev)
+    grads = grads or {}
+    shapes = {"x": ((bsz, L, dim), io), "delta": ((bsz, L, dim), io), "A": ((dim, N), f32),
+              "B": ((bsz, L, N), io), "C": ((bsz, L, N), io), "D": ((dim,), f32), "z": ((bsz, L, dim), io),
+              "delta_bias": ((dim,), f32), "h0": ((bsz, dim, N), f32)}
+    a = ScanBwdArgs()
+    for f, _ in ScanArgs._fields_:
+        if f in dict(ScanBwdArgs._fields_) and f not in ("workspace", "workspace_bytes", "time_splits"):
+            setattr(a, f, getattr(fa, f))
+    a.dy, a.dhT = _ptr(dy), _ptr(dhT)
+    for k, t in grads.items():
+        if k not in GRAD_FIELDS:
+            raise ValueError(f"no gradient for {k!r}")
+        _check("d" + k, t, *shapes[k], dev)
+        setattr(a, GRAD_FIELDS[k], _ptr(t))
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.time_splits = int(time_splits)
+    a.reserved = 0
+    return a
+
+
+def bwd_workspace_bytes(args: ScanBwdArgs) -> int:
+    r = lib().ssm_scan_bwd_workspace_bytes(ctypes.byref(args))
+    if r < 0:
+        raise RuntimeError(f"ssm_scan_bwd_workspace_bytes: {strerror(int(r))}")
+    return int(r)
+
+
+def bwd_plan(args: ScanBwdArgs) -> int:
+    """Number of time segments the backward would use."""
+    r = lib().ssm_scan_bwd_plan(ctypes.byref(args))
+    if r < 0:
+        raise RuntimeError(f"ssm_scan_bwd_plan: {strerror(int(r))}")
+    return int(r)
+
+
+def scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *, dy, dhT=None,
+             wanted=None, workspace=None, time_splits=0):
+    """Backward selective scan on the GPU: gradients of sum(dy * y) + sum(dhT * hT)
+    with respect to the inputs, as a dict keyed like the inputs (x, delta, A, B,
+    C, h0 always; D, z, delta_bias when given).  `wanted` restricts the outputs
+    to those names.  Launches on torch's current HIP stream and does not
+    synchronise."""
+    if not x.is_cuda:
+        raise ValueError("scan_bwd runs on the GPU only: move the tensors to a HIP device")
+    L_ = lib()
+    given = {"x": x, "delta": delta, "A": A, "B": B, "C": C, "D": D, "z": z, "delta_bias": delta_bias}
+    names = ["x", "delta", "A", "B", "C", "h0"] + [k for k in ("D", "z", "delta_bias") if given[k] is not None]
+    if wanted is not None:
+        names = [k for k in names if k in set(wanted)]
+    bsz, _, dim = x.shape
+    N = A.shape[1]
+    grads = {}
+    for k in names:
+        if k == "h0":
+            grads[k] = torch.empty((bsz, dim, N), dtype=torch.float32, device=x.device)
+        else:
+            grads[k] = torch.empty_like(given[k])
+    args = make_bwd_args(x, delta, A, B, C, D, z, delta_bias, h0, dy=dy, dhT=dhT, grads=grads,
+                         time_splits=time_splits)
+    if workspace is None:
+        nbytes = L_.ssm_scan_bwd_workspace_bytes(ctypes.byref(args))
+        if nbytes < 0:
+            raise RuntimeError(f"ssm_scan_bwd: {strerror(int(nbytes))}")
+        workspace = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=x.device)
+    args.workspace = _ptr(workspace)
+    args.workspace_bytes = workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = L_.ssm_scan_bwd(ctypes.byref(args), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise RuntimeError(f"ssm_scan_bwd: {strerror(rc)}")
+    return grads
+
+
+__all__ = ["scan_fwd", "scan_bwd", "make_args", "make_bwd_args", "plan", "bwd_plan", "workspace_bytes",
+           "bwd_workspace_bytes", "lib", "strerror", "ScanArgs", "ScanBwdArgs", "EXPORTS"]

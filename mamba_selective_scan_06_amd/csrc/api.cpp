@@ -150,6 +150,115 @@ int make_plan(const ssm_scan_args* a, bool have_workspace_info, Plan* pl) {
   return SSM_OK;
 }
 
+// ---- backward --------------------------------------------------------------------------
+
+struct BwdPlan {
+  int splits;
+  int64_t seg_len, nck, chunk;
+  // byte offsets of the workspace regions, and the total
+  int64_t off_ck, off_ckds, off_segh, off_segc, off_segds, off_pA, off_pD, off_pbias, off_pB, off_pC, total;
+};
+
+// Workgroups (one wave each) per batch row and segment: 64 / G channels each.
+int64_t bwd_blocks(const ssm_scan_bwd_args* a) {
+  const int64_t per = 64 / ssm::bwd_lanes_per_channel(a->dstate);
+  return (a->dim + per - 1) / per;
+}
+
+int validate_bwd(const ssm_scan_bwd_args* a) {
+  if (!a) return SSM_ERR_NULL;
+  if (a->batch < 0 || a->seqlen < 0 || a->dim < 0 || a->dstate < 0) return SSM_ERR_SHAPE;
+  if (a->dstate < 1 || a->dstate > ssm::kBwdMaxState) return SSM_ERR_DSTATE;
+  if (a->dtype != SSM_DTYPE_F32 && a->dtype != SSM_DTYPE_BF16) return SSM_ERR_DTYPE;
+  if (a->batch > 65535) return SSM_ERR_SHAPE;
+  if (a->flags & ~static_cast<int32_t>(SSM_FLAG_GENERIC_A)) return SSM_ERR_VARIANT;
+  if (a->time_splits < 0 || a->reserved != 0) return SSM_ERR_VARIANT;
+  int64_t bl, bld, bln, bd, bdn, dn, tmp;
+  if (!mul_ok(a->batch, a->seqlen, &bl) || !mul_ok(bl, a->dim, &bld) || !mul_ok(bl, a->dstate, &bln) ||
+      !mul_ok(a->batch, a->dim, &bd) || !mul_ok(bd, a->dstate, &bdn) || !mul_ok(a->dim, a->dstate, &dn))
+    return SSM_ERR_SHAPE;
+  // the partial dB/dC rows hold one entry per block of 64 / G channels: B L nblk N floats
+  if (!mul_ok(bln, bwd_blocks(a), &tmp) || !mul_ok(tmp, 8, &tmp) || !mul_ok(bld, 4, &tmp) ||
+      !mul_ok(bdn, 4, &tmp))
+    return SSM_ERR_SHAPE;
+  const bool has_tokens = bld > 0;
+  if (has_tokens && (!a->x || !a->delta || !a->A || !a->B || !a->C || !a->dy)) return SSM_ERR_NULL;
+  if (a->dz && !a->z) return SSM_ERR_NULL;
+  const void* ptrs[] = {a->x,  a->delta, a->A,  a->B,      a->C,  a->D,  a->z,           a->delta_bias,
+                        a->h0, a->dy,    a->dhT, a->dx,    a->ddelta, a->dA, a->dB,      a->dC,
+                        a->dD, a->dz,    a->ddelta_bias,   a->dh0, a->workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return SSM_ERR_ALIGN;
+  const int64_t es = a->dtype == SSM_DTYPE_F32 ? 4 : 2;
+  const int64_t xb = bld * es, nb = bln * es, sb = bdn * 4, db = a->dim * 4, ab = dn * 4;
+  const void* ins[] = {a->x, a->delta, a->A, a->B, a->C, a->D, a->z, a->delta_bias, a->h0, a->dy, a->dhT};
+  const int64_t insz[] = {xb, xb, ab, nb, nb, db, xb, db, sb, xb, sb};
+  const void* outs[] = {a->dx, a->ddelta, a->dA, a->dB, a->dC, a->dD, a->dz, a->ddelta_bias, a->dh0};
+  const int64_t outsz[] = {xb, xb, ab, nb, nb, db, xb, db, sb};
+  for (int i = 0; i < 9; ++i) {
+    for (int j = 0; j < 11; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return SSM_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return SSM_ERR_ALIAS;
+  }
+  return SSM_OK;
+}
+
+// Segments, chunking and workspace layout of a validated problem with B L D > 0.
+int make_bwd_plan(const ssm_scan_bwd_args* a, BwdPlan* pl) {
+  const int64_t L = a->seqlen, N = a->dstate;
+  const int64_t T = ssm::bwd_chunk_len(N);
+  const int64_t nblk = bwd_blocks(a);
+  if (nblk > INT32_MAX) return SSM_ERR_SHAPE;  // blocks map to grid.x
+  int64_t S = a->time_splits;
+  if (S == 0) {
+    // Split until there are 4096 waves (4 per SIMD), keeping segments at least
+    // 64 tokens long.  The split's extra cost, an adjoint-only pass, does not
+    // grow with the number of segments.
+    const int64_t waves = nblk * a->batch;
+    S = 1;
+    while (waves * S < 4096 && L / (2 * S) >= 64 && S < 1024) S *= 2;
+  }
+  if (S > L) S = L;
+  int64_t seg_len = round_up((L + S - 1) / S, T);
+  // The kernels address a segment's tokens through buffer descriptors with
+  // 32-bit byte offsets: a segment of any token tensor (and of the partial
+  // dB / dC rows) must stay below 2 GiB, which may add segments.
+  const int64_t es = a->dtype == SSM_DTYPE_F32 ? 4 : 2;
+  int64_t per_tok = a->dim * es;
+  if (nblk * N * 4 > per_tok) per_tok = nblk * N * 4;
+  const int64_t max_seg = INT32_MAX / per_tok / T * T;
+  if (max_seg < T) return SSM_ERR_SHAPE;
+  if (seg_len > max_seg) seg_len = max_seg;
+  S = (L + seg_len - 1) / seg_len;
+  if (S > 65535) return SSM_ERR_VARIANT;  // segments map to grid.z
+  pl->splits = static_cast<int>(S);
+  pl->seg_len = seg_len;
+  pl->chunk = T;
+  pl->nck = (L + T - 1) / T;
+  const int64_t B = a->batch, D = a->dim;
+  int64_t off = 0;
+  auto take = [&](int64_t floats) {
+    const int64_t o = off;
+    off += round_up(floats * 4, 256);
+    return o;
+  };
+  pl->off_ck = take(B * pl->nck * D * N);
+  pl->off_ckds = take(B * pl->nck * D);
+  pl->off_segh = take(B * S * D * N);
+  pl->off_segc = take(B * S * D * N);
+  pl->off_segds = take(B * S * D);
+  pl->off_pA = take(B * S * D * N);
+  pl->off_pD = take(B * S * D);
+  pl->off_pbias = take(B * S * D);
+  pl->off_pB = take(B * L * nblk * N);  // written whether or not dB / dC are asked for
+  pl->off_pC = take(B * L * nblk * N);
+  pl->total = off;
+  return SSM_OK;
+}
+
+bool bwd_has_work(const ssm_scan_bwd_args* a) { return a->batch > 0 && a->seqlen > 0 && a->dim > 0; }
+
 }  // namespace
 
 extern "C" {
@@ -159,15 +268,15 @@ int ssm_scan_abi_version(void) { return SSM_SCAN_ABI_VERSION; }
 const char* ssm_scan_strerror(int code) {
   switch (code) {
     case SSM_OK: return "success";
-    case SSM_ERR_NULL: return "a required pointer is NULL";
+    case SSM_ERR_NULL: return "a required pointer is NULL (or dz given without z)";
     case SSM_ERR_SHAPE: return "invalid shape (negative extent, batch > 65535, or size overflow)";
-    case SSM_ERR_DSTATE: return "dstate must be in 1..64";
+    case SSM_ERR_DSTATE: return "dstate out of range (1..64 forward, 1..16 backward)";
     case SSM_ERR_DTYPE: return "dtype must be SSM_DTYPE_F32 or SSM_DTYPE_BF16";
     case SSM_ERR_ALIGN: return "every tensor base address must be 16-byte aligned";
-    case SSM_ERR_ALIAS: return "y overlaps an input, or hT overlaps an input other than h0";
-    case SSM_ERR_WORKSPACE: return "time_splits > 1 needs a workspace of ssm_scan_workspace_bytes bytes";
+    case SSM_ERR_ALIAS: return "an output overlaps an input or another output (hT may equal h0)";
+    case SSM_ERR_WORKSPACE: return "workspace missing or smaller than the *_workspace_bytes query returns";
     case SSM_ERR_LAUNCH: return "kernel launch failed";
-    case SSM_ERR_VARIANT: return "variant, flags or time_splits not valid for this problem";
+    case SSM_ERR_VARIANT: return "variant, flags, time_splits or reserved not valid for this problem";
     default: return "unknown status code";
   }
 }
@@ -234,6 +343,83 @@ int ssm_scan_fwd(const ssm_scan_args* a, void* stream) {
     e = ssm::launch_nsplit(p, s);
   else
     e = ssm::launch_lane(p, s);
+  return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
+}
+
+int64_t ssm_scan_bwd_workspace_bytes(const ssm_scan_bwd_args* a) {
+  const int rc = validate_bwd(a);
+  if (rc != SSM_OK) return rc;
+  if (!bwd_has_work(a)) return 0;
+  BwdPlan pl;
+  const int prc = make_bwd_plan(a, &pl);
+  return prc != SSM_OK ? prc : pl.total;
+}
+
+int64_t ssm_scan_bwd_plan(const ssm_scan_bwd_args* a) {
+  const int rc = validate_bwd(a);
+  if (rc != SSM_OK) return rc;
+  if (!bwd_has_work(a)) return 1;
+  BwdPlan pl;
+  const int prc = make_bwd_plan(a, &pl);
+  return prc != SSM_OK ? prc : pl.splits;
+}
+
+int ssm_scan_bwd(const ssm_scan_bwd_args* a, void* stream) {
+  int rc = validate_bwd(a);
+  if (rc != SSM_OK) return rc;
+  ssm::BwdProblem p{};
+  p.batch = a->batch;
+  p.seqlen = a->seqlen;
+  p.dim = a->dim;
+  p.dstate = a->dstate;
+  p.dtype = a->dtype;
+  p.x = a->x;
+  p.delta = a->delta;
+  p.A = a->A;
+  p.B = a->B;
+  p.C = a->C;
+  p.D = a->D;
+  p.z = a->z;
+  p.delta_bias = a->delta_bias;
+  p.h0 = a->h0;
+  p.dy = a->dy;
+  p.dhT = a->dhT;
+  p.dx = a->dx;
+  p.ddelta = a->ddelta;
+  p.dA = a->dA;
+  p.dB = a->dB;
+  p.dC = a->dC;
+  p.dD = a->dD;
+  p.dz = a->dz;
+  p.ddelta_bias = a->ddelta_bias;
+  p.dh0 = a->dh0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (!bwd_has_work(a)) {
+    e = ssm::launch_bwd_empty(p, s);
+    return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
+  }
+  BwdPlan pl;
+  rc = make_bwd_plan(a, &pl);
+  if (rc != SSM_OK) return rc;
+  if (!a->workspace || a->workspace_bytes < pl.total) return SSM_ERR_WORKSPACE;
+  char* w = static_cast<char*>(a->workspace);
+  auto reg = [&](int64_t off) { return reinterpret_cast<float*>(w + off); };
+  p.splits = pl.splits;
+  p.seg_len = pl.seg_len;
+  p.nck = pl.nck;
+  p.nblk = bwd_blocks(a);
+  p.ck = reg(pl.off_ck);
+  p.ckds = reg(pl.off_ckds);
+  p.segh = reg(pl.off_segh);
+  p.segc = reg(pl.off_segc);
+  p.segds = reg(pl.off_segds);
+  p.pA = reg(pl.off_pA);
+  p.pD = reg(pl.off_pD);
+  p.pbias = reg(pl.off_pbias);
+  p.pB = reg(pl.off_pB);
+  p.pC = reg(pl.off_pC);
+  e = ssm::launch_bwd(p, s);
   return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
 

@@ -40,4 +40,62 @@ hipError_t launch_lane(const Problem& p, hipStream_t stream);
 hipError_t launch_decode(const Problem& p, hipStream_t stream);
 hipError_t launch_state_copy(const Problem& p, hipStream_t stream);  // seqlen == 0: hT <- h0 or 0
 
+// ---- backward -----------------------------------------------------------------------
+// Largest state size of the backward kernels.
+constexpr int kBwdMaxState = 64;
+
+// Lane layout of the backward kernels: G = ceil(N / K) adjacent lanes share a
+// channel and each owns K consecutive states (K = 4 for N <= 4, else 8).
+constexpr int bwd_lane_states(int64_t dstate) { return dstate <= 4 ? 4 : 8; }
+constexpr int bwd_lanes_per_channel(int64_t dstate) {
+  return dstate <= 8 ? 1 : (dstate <= 16 ? 2 : (dstate <= 32 ? 4 : 8));
+}
+// Tokens per checkpoint chunk: the chunk's recomputed states live in
+// registers, (T + 1) * K of them per lane.
+constexpr int bwd_chunk_len(int64_t dstate) { return bwd_lane_states(dstate) == 4 ? 16 : 8; }
+
+struct BwdProblem {
+  int64_t batch, seqlen, dim, dstate;
+  int dtype;        // 0 = fp32, 1 = bf16
+  int splits;       // time segments, >= 1
+  int64_t seg_len;  // tokens per segment, a multiple of the chunk length
+  int64_t nck;      // checkpoint chunks per sequence, ceil(L / chunk)
+  int64_t nblk;     // workgroups per (batch row, segment): ceil(D / (64 / G))
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* delta_bias;
+  const float* h0;
+  const void* dy;
+  const float* dhT;
+  void* dx;
+  void* ddelta;
+  float* dA;
+  void* dB;
+  void* dC;
+  float* dD;
+  void* dz;
+  float* ddelta_bias;
+  float* dh0;
+  // workspace regions (fp32)
+  float* ck;     // (B, nck, D, N) state entering each chunk, from a zero state at its segment start
+  float* ckds;   // (B, nck, D) sum of softplus(delta) from the segment start to the chunk start
+  float* segh;   // (B, S, D, N) segment end state from zero -> true state entering the segment
+  float* segc;   // (B, S, D, N) adjoint at segment start from zero -> true adjoint leaving the segment end
+  float* segds;  // (B, S, D) sum of softplus(delta) over each segment
+  float* pA;     // (B, S, D, N) partial dA
+  float* pD;     // (B, S, D) partial dD
+  float* pbias;  // (B, S, D) partial d delta_bias
+  float* pB;     // (B, L, nblk, N) partial dB, one row per block of 64 / G channels
+  float* pC;     // (B, L, nblk, N) partial dC
+};
+
+hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream);
+// Outputs of a problem with no token (L == 0) or no chain (B == 0 or D == 0).
+hipError_t launch_bwd_empty(const BwdProblem& p, hipStream_t stream);
+
 }  // namespace ssm

@@ -142,6 +142,22 @@ def make_decode_step(w: Workload, step: int, *, batch: int | None = None, dim: i
     }
 
 
+def make_cotangents(w: Workload, *, batch: int | None = None, seqlen: int | None = None,
+                    dim: int | None = None, dstate: int | None = None, seed_extra=()):
+    """Seeded upstream gradients for a backward call: dy (B, L, D) in the
+    workload's dtype and dhT (B, D, N) fp32, both N(0, 1)."""
+    bsz = batch or w.batch
+    L = seqlen if seqlen is not None else (1 if w.steps else w.seqlen)
+    dim = dim or w.dim
+    N = dstate or w.dstate
+    g = _streams(w.index, (2000, *seed_extra))
+    f32 = np.float32
+    return {
+        "dy": _cast(g[0].standard_normal((bsz, L, dim), dtype=f32), w.dtype),
+        "dhT": torch.from_numpy(g[1].standard_normal((bsz, dim, N), dtype=f32)),
+    }
+
+
 def tolerance(dtype: torch.dtype) -> float:
     """Max floored relative error allowed: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs."""
     return 1e-4 if dtype == torch.float32 else 2e-2
