@@ -56,15 +56,19 @@ def algorithmic_bytes(w) -> int:
     return n
 
 
+# Sources the forward scan kernels are built from (the backward's are not).
+FORWARD_SOURCES = ("buffer_io.hpp", "device_common.hpp", "nsplit_dispatch.cpp", "nsplit_inst.hip",
+                   "scan_decode.hip", "scan_lane.hip", "scan_nsplit_impl.hpp")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources, so stored traffic counters can be matched to
-    the kernel build they were measured on."""
+    """Hash of the forward kernels' HIP sources, so stored traffic counters can
+    be matched to the kernel build they were measured on."""
     csrc = os.path.join(HERE, "mamba_selective_scan_06_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + fh.read())
+    for f in FORWARD_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 

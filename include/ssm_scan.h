@@ -131,7 +131,7 @@ int64_t ssm_scan_plan(const ssm_scan_args *args);
 typedef struct ssm_scan_bwd_args {
   int64_t batch, seqlen, dim, dstate; /* as ssm_scan_args; N <= 16           */
   int32_t dtype;                      /* ssm_dtype of x, delta, B, C, z, dy and the (B, L, .) gradients */
-  int32_t flags;                      /* ssm_flags; SSM_FLAG_GENERIC_A is accepted and has no effect */
+  int32_t flags;                      /* ssm_flags: SSM_FLAG_GENERIC_A as for the forward */
   const void *x;           /* (B, L, D)                                        required */
   const void *delta;       /* (B, L, D) raw step size                          required */
   const float *A;          /* (D, N)                                           required */

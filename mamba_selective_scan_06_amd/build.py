@@ -27,11 +27,12 @@ ARCH = "gfx950"
 NSPLIT_INST = [(s, k) for s in ("float", "uint16_t") for k in (1, 2, 4, 8, 16)]
 UNITS = [("api.cpp", [], "api"), ("nsplit_dispatch.cpp", [], "nsplit_dispatch"),
          ("scan_lane.hip", [], "scan_lane"), ("scan_decode.hip", [], "scan_decode"),
-         ("scan_bwd.hip", [], "scan_bwd")] + [
+         ("scan_bwd.hip", [], "scan_bwd"),
+         ("scan_bwd_inst.hip", ["-DBWD_S=float"], "bwd_f32"), ("scan_bwd_inst.hip", ["-DBWD_S=uint16_t"], "bwd_bf16")] + [
     ("nsplit_inst.hip", [f"-DNSPLIT_S={s}", f"-DNSPLIT_K={k}"], f"nsplit_{'f32' if s == 'float' else 'bf16'}_k{k}")
     for s, k in NSPLIT_INST]
 SOURCES = sorted({u[0] for u in UNITS})
-HEADERS = ["buffer_io.hpp", "device_common.hpp", "scan_internal.hpp", "scan_nsplit_impl.hpp"]
+HEADERS = ["buffer_io.hpp", "device_common.hpp", "scan_bwd_impl.hpp", "scan_internal.hpp", "scan_nsplit_impl.hpp"]
 
 COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -159,10 +159,10 @@ struct BwdPlan {
   int64_t off_ck, off_ckds, off_segh, off_segc, off_segds, off_pA, off_pD, off_pbias, off_pB, off_pC, total;
 };
 
-// Workgroups (one wave each) per batch row and segment: 64 / G channels each.
+// Waves per batch row and segment: workgroups of G waves cover 64 channels,
+// each wave 64 / G of them.  Each wave writes one partial dB / dC row.
 int64_t bwd_blocks(const ssm_scan_bwd_args* a) {
-  const int64_t per = 64 / ssm::bwd_lanes_per_channel(a->dstate);
-  return (a->dim + per - 1) / per;
+  return (a->dim + 63) / 64 * ssm::bwd_lanes_per_channel(a->dstate);
 }
 
 int validate_bwd(const ssm_scan_bwd_args* a) {
@@ -373,6 +373,7 @@ int ssm_scan_bwd(const ssm_scan_bwd_args* a, void* stream) {
   p.dim = a->dim;
   p.dstate = a->dstate;
   p.dtype = a->dtype;
+  p.flags = a->flags;
   p.x = a->x;
   p.delta = a->delta;
   p.A = a->A;

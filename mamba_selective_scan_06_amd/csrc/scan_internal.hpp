@@ -57,10 +57,11 @@ constexpr int bwd_chunk_len(int64_t dstate) { return bwd_lane_states(dstate) == 
 struct BwdProblem {
   int64_t batch, seqlen, dim, dstate;
   int dtype;        // 0 = fp32, 1 = bf16
+  int flags;        // ssm_flags (kFlagGenericA)
   int splits;       // time segments, >= 1
   int64_t seg_len;  // tokens per segment, a multiple of the chunk length
   int64_t nck;      // checkpoint chunks per sequence, ceil(L / chunk)
-  int64_t nblk;     // workgroups per (batch row, segment): ceil(D / (64 / G))
+  int64_t nblk;     // waves per (batch row, segment): ceil(D / 64) * G, one partial dB / dC row each
   const void* x;
   const void* delta;
   const float* A;
@@ -90,11 +91,21 @@ struct BwdProblem {
   float* pA;     // (B, S, D, N) partial dA
   float* pD;     // (B, S, D) partial dD
   float* pbias;  // (B, S, D) partial d delta_bias
-  float* pB;     // (B, L, nblk, N) partial dB, one row per block of 64 / G channels
+  float* pB;     // (B, L, nblk, N) partial dB, one row per wave (64 / G channels)
   float* pC;     // (B, L, nblk, N) partial dC
 };
 
 hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream);
+
+namespace bwd {
+// Pieces of the backward launch sequence that live in different units.
+hipError_t launch_combine(const BwdProblem& p, hipStream_t stream);
+hipError_t launch_reduce_d(const BwdProblem& p, hipStream_t stream);
+template <typename S>
+hipError_t launch_typed(const BwdProblem& p, hipStream_t stream);  // S = float or uint16_t (bf16 bits)
+extern template hipError_t launch_typed<float>(const BwdProblem& p, hipStream_t stream);
+extern template hipError_t launch_typed<uint16_t>(const BwdProblem& p, hipStream_t stream);
+}  // namespace bwd
 // Outputs of a problem with no token (L == 0) or no chain (B == 0 or D == 0).
 hipError_t launch_bwd_empty(const BwdProblem& p, hipStream_t stream);
 
