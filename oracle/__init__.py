@@ -75,6 +75,9 @@ class Oracle:
         self._lib.oracle_assoc_scan_f64.restype = ctypes.c_int
         self._lib.oracle_scan_bwd_f64.argtypes = [ctypes.POINTER(_Args), ctypes.POINTER(_Grads)]
         self._lib.oracle_scan_bwd_f64.restype = ctypes.c_int
+        i64 = ctypes.c_int64
+        self._lib.oracle_conv1d_silu_f64.argtypes = [i64, i64, i64, i64, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+        self._lib.oracle_conv1d_silu_f64.restype = ctypes.c_int
         self._lib.oracle_softplus_vec.argtypes = [_dp, _dp, ctypes.c_int64]
         self._lib.oracle_softplus_vec.restype = None
         self._lib.oracle_mutant_id.restype = ctypes.c_int
@@ -166,6 +169,28 @@ class Oracle:
         del keep
         return out
 
+    def conv1d_silu(self, x, w, bias=None, state=None):
+        """Depthwise causal conv1d + SiLU over x (B, L, D) with taps w (D, W),
+        optional bias (D) and state (B, W-1, D) (the previous call's last W-1
+        input rows).  Returns (u, pre, state_out) as float64 numpy arrays."""
+        x = self._f64(x)
+        w = self._f64(w)
+        bias = self._f64(bias)
+        state = self._f64(state)
+        Bn, L, D = x.shape
+        W = w.shape[1]
+        assert w.shape == (D, W) and (bias is None or bias.shape == (D,))
+        assert state is None or state.shape == (Bn, W - 1, D)
+        u = np.empty_like(x)
+        pre = np.empty_like(x)
+        state_out = np.empty((Bn, W - 1, D), dtype=np.float64)
+        p = self._ptr
+        rc = self._lib.oracle_conv1d_silu_f64(Bn, L, D, W, p(x), p(w), p(bias), p(state), p(pre), p(u),
+                                             p(state_out))
+        if rc != 0:
+            raise RuntimeError("oracle_conv1d_silu_f64 failed")
+        return u, pre, state_out
+
     def softplus(self, v):
         v = self._f64(v)
         out = np.empty_like(v)
@@ -199,6 +224,10 @@ def assoc_scan(*args, **kw):
 
 def scan_bwd(*args, **kw):
     return get().scan_bwd(*args, **kw)
+
+
+def conv1d_silu(*args, **kw):
+    return get().conv1d_silu(*args, **kw)
 
 
 def softplus(v):

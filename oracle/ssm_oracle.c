@@ -24,7 +24,7 @@
  * the device receives (bf16/fp32 widened without rounding).
  *
  * It also holds the backward pass (gradients of a scalar loss), see
- * oracle_scan_bwd_f64 below.
+ * oracle_scan_bwd_f64, and the conv1d + SiLU prologue, oracle_conv1d_silu_f64.
  *
  * Build-time mutations (ORACLE_MUTANT=k, k>0) exist only so the test suite
  * can show that its closed-form pins catch plausible mistakes; the default
@@ -76,6 +76,9 @@ static double silu(double z) {
   return z / (1.0 + exp(-z));
 #endif
 }
+
+/* SiLU of the conv prologue, separate from the gate's so that each has its own pins. */
+static double silu_plain(double v) { return v / (1.0 + exp(-v)); }
 
 /* One independent chain: batch row b, channel d, all N states, t = 0..L-1. */
 static void scan_channel(const oracle_args *a, int64_t b, int64_t d, double *h) {
@@ -367,6 +370,48 @@ int oracle_scan_bwd_f64(const oracle_args *a, const oracle_grads *g) {
         for (int64_t n = 0; n < N; ++n) g->dh0[(b * D + d) * N + n] = carry[n];
     }
   free(hs); free(dl); free(carry);
+  return 0;
+}
+
+/* Depthwise causal convolution and SiLU: the block's prologue on x before the
+ * scan (youngju.dev, section 3.4 listing: nn.Conv1d(d_inner, d_inner, d_conv,
+ * padding=d_conv-1, groups=d_inner) with its bias, output cut to the first L
+ * positions, then F.silu).  PyTorch's Conv1d is a cross-correlation, and the
+ * left padding of W-1 positions makes output t see inputs t-(W-1) .. t:
+ *   pre[b,t,d] = bias[d] + sum_{k=0}^{W-1} w[d,k] * x[b, t-(W-1)+k, d]
+ *   u[b,t,d]   = SiLU(pre[b,t,d]) = pre / (1 + exp(-pre))
+ * Inputs at negative token index are the padding zeros, or, when `state` is
+ * given, the previous call's last W-1 input rows: state is (B, W-1, D) with
+ * row W-1+i holding token i < 0.  state_out (B, W-1, D) receives the last W-1
+ * rows of [state; x], i.e. the state for the next call.  pre, u and
+ * state_out may each be NULL. */
+int oracle_conv1d_silu_f64(int64_t Bn, int64_t L, int64_t D, int64_t W, const double *x, const double *w,
+                           const double *bias, const double *state, double *pre, double *u, double *state_out) {
+  if (Bn < 0 || L < 0 || D < 0 || W < 1 || (L > 0 && (!x || !w))) return -1;
+  const int64_t H = W - 1;
+  for (int64_t b = 0; b < Bn; ++b)
+    for (int64_t d = 0; d < D; ++d) {
+      /* input at token index i, for i >= -(W-1) */
+#define XIN(i) ((i) >= 0 ? x[(b * L + (i)) * D + d] : (state ? state[(b * H + H + (i)) * D + d] : 0.0))
+      for (int64_t t = 0; t < L; ++t) {
+        double acc = bias ? bias[d] : 0.0;
+        for (int64_t k = 0; k < W; ++k) {
+#if ORACLE_MUTANT == 19
+          acc += w[d * W + (W - 1 - k)] * XIN(t - H + k); /* taps reversed */
+#elif ORACLE_MUTANT == 20
+          acc += w[d * W + k] * (t - H + k - 1 >= -H ? XIN(t - H + k - 1) : 0.0); /* one token late */
+#else
+          acc += w[d * W + k] * XIN(t - H + k);
+#endif
+        }
+        const int64_t i = (b * L + t) * D + d;
+        if (pre) pre[i] = acc;
+        if (u) u[i] = silu_plain(acc);
+      }
+      if (state_out)
+        for (int64_t j = 0; j < H; ++j) state_out[(b * H + j) * D + d] = XIN(L - H + j);
+#undef XIN
+    }
   return 0;
 }
 
