@@ -336,6 +336,57 @@ def bench_backward(w, args, ssm, torch):
     return out
 
 
+def bench_conv(w, args, ssm, torch):
+    """One step = one ssm_conv1d_silu_fwd (width 4, bias, zero padding) over the
+    workload's x: u = SiLU(causal depthwise conv(x)), the block's prologue."""
+    import workloads
+    dev = torch.device("cuda:0")
+    log(f"workload {w.describe()} (conv1d + SiLU prologue)")
+    x = workloads.make_inputs(w)["x"]
+    prm = workloads.make_conv_params(w)
+    xs = [x.to(dev), x.to(dev)]  # alternate so the previous step's rows are not in the LLC
+    wt, bs = prm["weight"].to(dev), prm["bias"].to(dev)
+    us = [torch.empty_like(xs[0]) for _ in xs]
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        ssm.conv1d_silu(xs[i % 2], wt, bs, out=us[i % 2])
+    torch.cuda.synchronize()
+    steps = max(args.steps, 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        ssm.conv1d_silu(xs[i % 2], wt, bs, out=us[i % 2])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    es = 2 if "bfloat16" in str(w.dtype) else 4
+    bld = w.batch * w.seqlen * w.dim
+    alg = 2 * bld * es + w.dim * 4 * 4 + w.dim * 4  # x read, u written, taps and bias
+    ms = elapsed * 1e3 / steps
+    out = {
+        "metric": "conv1d+SiLU prologue GElem/s (B*L*D) + % HBM roofline",
+        "value": round(bld / (ms * 1e-3) / 1e9, 2), "unit": "GElem/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "pass": "conv1d_silu", "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
+                   "width": 4, "io_dtype": str(w.dtype).replace("torch.", "")},
+        "roofline": _roofline(alg, kern_s, "conv_silu_kernel"),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        nd = min(w.dim, 256)
+        t = time.perf_counter()
+        oracle.conv1d_silu(x[:, :, :nd], prm["weight"][:nd], prm["bias"][:nd])
+        sec = time.perf_counter() - t
+        el = w.batch * w.seqlen * nd
+        out["cpu_baseline"] = {"value": round(el / sec / 1e9, 5), "unit": "GElem/s", "cores": 1, "kind": "oracle",
+                               "sample": f"channels 0..{nd - 1} of every batch row and token ({el} elements), fp64 "
+                                         f"oracle, single thread; {sec:.2f} s including input widening"}
+    return out
+
+
 def main():
     import workloads
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -348,6 +399,7 @@ def main():
     ap.add_argument("--generic-a", action="store_true", help="never take the structured-decay path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true", help="time ssm_scan_bwd (all gradients) instead")
+    ap.add_argument("--prologue", action="store_true", help="time the conv1d + SiLU prologue on x instead")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the scan, copy a MIB-MiB buffer `steps` times (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -376,6 +428,12 @@ def main():
         return
 
     w = workloads.BY_NAME[args.workload]
+    if args.prologue:
+        if w.chunks > 1 or w.steps:
+            print("--prologue runs the single-call workloads", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(bench_conv(w, args, ssm, torch)), flush=True)
+        return
     if args.backward:
         if w.chunks > 1 or w.steps:
             print("--backward runs the single-call workloads", file=sys.stderr)

@@ -177,6 +177,38 @@ int64_t ssm_scan_bwd_workspace_bytes(const ssm_scan_bwd_args *args);
  * invalid arguments. */
 int64_t ssm_scan_bwd_plan(const ssm_scan_bwd_args *args);
 
+/* ---- conv1d + SiLU prologue -------------------------------------------------
+ * The block's prologue on x (section 3.4 listing: a depthwise Conv1d with
+ * groups = channels and padding = width - 1, its output cut to the first L
+ * positions, then SiLU):
+ *   u[b,t,d] = SiLU(bias[d] + sum_{k<W} weight[d,k] * x[b, t-(W-1)+k, d])
+ * x at a negative token index is the padding zero or, when `state` is given,
+ * row W-1+i of state: the previous call's last W-1 input rows, so that a long
+ * sequence can be fed in consecutive calls.  u is the sequence the scan and
+ * the caller's projection to B, C and delta consume (section 3.4 derives them
+ * from it), so u is materialised; it is not fused into the scan.
+ * Layouts: x, u (B, L, D) and state, state_out (B, W-1, D) in `dtype`;
+ * weight (D, W) and bias (D) fp32.  Arithmetic is fp32; u is rounded once,
+ * to nearest-even. */
+typedef struct ssm_conv_args {
+  int64_t batch, seqlen, dim; /* B, L, D >= 0                                             */
+  int32_t width;              /* W = d_conv, 1..4                                         */
+  int32_t dtype;              /* ssm_dtype of x, state, u, state_out                      */
+  const void *x;              /* (B, L, D) input                                  required */
+  const float *weight;        /* (D, W) taps; tap W-1 multiplies the current token required */
+  const float *bias;          /* (D) or NULL (zero)                                        */
+  const void *state;          /* (B, W-1, D) previous inputs, or NULL (zero padding)       */
+  void *u;                    /* (B, L, D) output                                 required */
+  void *state_out;            /* (B, W-1, D) last W-1 input rows out, or NULL              */
+} ssm_conv_args;
+
+/* Errors as for ssm_scan_fwd: SSM_ERR_NULL (x, weight, u missing when
+ * B*L*D > 0), SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_VARIANT (width outside
+ * 1..4), SSM_ERR_ALIGN (16-byte alignment), SSM_ERR_ALIAS (u overlapping an
+ * input, or state_out overlapping x, state or u).  With L == 0, state_out
+ * receives state (or zeros). */
+int ssm_conv1d_silu_fwd(const ssm_conv_args *args, void *stream);
+
 /* Static, human-readable text for a status code. */
 const char *ssm_scan_strerror(int code);
 

@@ -32,7 +32,8 @@ FLAG_GENERIC_A = 1
 
 # Exported symbols the header declares (checked by the tests).
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_scan_bwd",
-           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd_plan", "ssm_scan_strerror", "ssm_scan_abi_version")
+           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd_plan", "ssm_conv1d_silu_fwd", "ssm_scan_strerror",
+           "ssm_scan_abi_version")
 
 
 class ScanArgs(ctypes.Structure):
@@ -66,6 +67,16 @@ class ScanBwdArgs(ctypes.Structure):
     ]
 
 
+class ConvArgs(ctypes.Structure):
+    """Mirror of ssm_conv_args in include/ssm_scan.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+        ("width", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+        ("state", ctypes.c_void_p), ("u", ctypes.c_void_p), ("state_out", ctypes.c_void_p),
+    ]
+
+
 # Gradient outputs of the backward: name of the input they belong to -> struct field.
 GRAD_FIELDS = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
                "delta_bias": "ddelta_bias", "h0": "dh0"}
@@ -95,6 +106,8 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_bwd_workspace_bytes.restype = ctypes.c_int64
         L.ssm_scan_bwd_plan.argtypes = [PB]
         L.ssm_scan_bwd_plan.restype = ctypes.c_int64
+        L.ssm_conv1d_silu_fwd.argtypes = [ctypes.POINTER(ConvArgs), ctypes.c_void_p]
+        L.ssm_conv1d_silu_fwd.restype = ctypes.c_int
         L.ssm_scan_strerror.argtypes = [ctypes.c_int]
         L.ssm_scan_strerror.restype = ctypes.c_char_p
         L.ssm_scan_abi_version.argtypes = []
@@ -299,5 +312,50 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *, dy,
     return grads
 
 
-__all__ = ["scan_fwd", "scan_bwd", "make_args", "make_bwd_args", "plan", "bwd_plan", "workspace_bytes",
+def make_conv_args(x, weight, bias=None, state=None, u=None, state_out=None) -> ConvArgs:
+    """Check shapes/dtypes/devices and fill an ssm_conv_args."""
+    if x.dim() != 3 or weight.dim() != 2:
+        raise ValueError("x must be (B, L, D) and weight (D, W)")
+    bsz, L, dim = x.shape
+    W = weight.shape[1]
+    io, dev, f32 = x.dtype, x.device, torch.float32
+    if io not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _check("weight", weight, (dim, W), f32, dev)
+    _check("bias", bias, (dim,), f32, dev)
+    _check("state", state, (bsz, W - 1, dim), io, dev)
+    _check("u", u, (bsz, L, dim), io, dev)
+    _check("state_out", state_out, (bsz, W - 1, dim), io, dev)
+    _check("x", x, (bsz, L, dim), io, dev)
+    a = ConvArgs()
+    a.batch, a.seqlen, a.dim, a.width = bsz, L, dim, W
+    a.dtype = DTYPE_F32 if io == torch.float32 else DTYPE_BF16
+    a.x, a.weight, a.bias, a.state = _ptr(x), _ptr(weight), _ptr(bias), _ptr(state)
+    a.u, a.state_out = _ptr(u), _ptr(state_out)
+    return a
+
+
+def conv1d_silu(x, weight, bias=None, state=None, *, return_state=False, out=None, state_out=None):
+    """Depthwise causal conv1d + SiLU on the GPU: u = SiLU(bias + sum_k weight[:, k] x[t-(W-1)+k]).
+    `state` (B, W-1, D) carries the previous call's last W-1 input rows.  Returns u,
+    or (u, state_out) with return_state=True.  Launches on torch's current HIP
+    stream and does not synchronise."""
+    if not x.is_cuda:
+        raise ValueError("conv1d_silu runs on the GPU only: move the tensors to a HIP device")
+    L_ = lib()
+    u = out if out is not None else torch.empty_like(x)
+    so = state_out
+    if so is None and return_state:
+        so = torch.empty((x.shape[0], weight.shape[1] - 1, x.shape[2]), dtype=x.dtype, device=x.device)
+    args = make_conv_args(x, weight, bias, state, u, so)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = L_.ssm_conv1d_silu_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise RuntimeError(f"ssm_conv1d_silu_fwd: {strerror(rc)}")
+    if return_state or state_out is not None:
+        return u, so
+    return u
+
+
+__all__ = ["scan_fwd", "scan_bwd", "conv1d_silu", "make_conv_args", "ConvArgs", "make_args", "make_bwd_args", "plan", "bwd_plan", "workspace_bytes",
            "bwd_workspace_bytes", "lib", "strerror", "ScanArgs", "ScanBwdArgs", "EXPORTS"]

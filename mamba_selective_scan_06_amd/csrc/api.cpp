@@ -259,6 +259,35 @@ int make_bwd_plan(const ssm_scan_bwd_args* a, BwdPlan* pl) {
 
 bool bwd_has_work(const ssm_scan_bwd_args* a) { return a->batch > 0 && a->seqlen > 0 && a->dim > 0; }
 
+// ---- conv1d + SiLU prologue ---------------------------------------------------------------
+
+int validate_conv(const ssm_conv_args* a) {
+  if (!a) return SSM_ERR_NULL;
+  if (a->batch < 0 || a->seqlen < 0 || a->dim < 0) return SSM_ERR_SHAPE;
+  if (a->dtype != SSM_DTYPE_F32 && a->dtype != SSM_DTYPE_BF16) return SSM_ERR_DTYPE;
+  if (a->width < 1 || a->width > 4) return SSM_ERR_VARIANT;
+  if (a->batch > 65535) return SSM_ERR_SHAPE;  // batch rows map to grid.z
+  const int64_t H = a->width - 1;
+  int64_t bl, bld, bhd, dw, tmp;
+  if (!mul_ok(a->batch, a->seqlen, &bl) || !mul_ok(bl, a->dim, &bld) || !mul_ok(a->batch * H, a->dim, &bhd) ||
+      !mul_ok(a->dim, a->width, &dw) || !mul_ok(bld, 4, &tmp) || !mul_ok(bhd, 4, &tmp) || !mul_ok(dw, 4, &tmp))
+    return SSM_ERR_SHAPE;
+  if (bld > 0 && (!a->x || !a->weight || !a->u)) return SSM_ERR_NULL;
+  const void* ptrs[] = {a->x, a->weight, a->bias, a->state, a->u, a->state_out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return SSM_ERR_ALIGN;
+  const int64_t es = a->dtype == SSM_DTYPE_F32 ? 4 : 2;
+  const int64_t xb = bld * es, sb = bhd * es;
+  const void* ins[] = {a->x, a->weight, a->bias, a->state};
+  const int64_t insz[] = {xb, dw * 4, a->dim * 4, sb};
+  for (int i = 0; i < 4; ++i) {
+    if (overlaps(a->u, xb, ins[i], insz[i])) return SSM_ERR_ALIAS;
+    if (overlaps(a->state_out, sb, ins[i], insz[i])) return SSM_ERR_ALIAS;
+  }
+  if (overlaps(a->state_out, sb, a->u, xb)) return SSM_ERR_ALIAS;
+  return SSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -421,6 +450,26 @@ int ssm_scan_bwd(const ssm_scan_bwd_args* a, void* stream) {
   p.pB = reg(pl.off_pB);
   p.pC = reg(pl.off_pC);
   e = ssm::launch_bwd(p, s);
+  return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
+}
+
+int ssm_conv1d_silu_fwd(const ssm_conv_args* a, void* stream) {
+  const int rc = validate_conv(a);
+  if (rc != SSM_OK) return rc;
+  if (a->batch == 0 || a->dim == 0) return SSM_OK;
+  ssm::ConvProblem p;
+  p.batch = a->batch;
+  p.seqlen = a->seqlen;
+  p.dim = a->dim;
+  p.width = a->width;
+  p.dtype = a->dtype;
+  p.x = a->x;
+  p.weight = a->weight;
+  p.bias = a->bias;
+  p.state = a->state;
+  p.u = a->u;
+  p.state_out = a->state_out;
+  const hipError_t e = ssm::launch_conv(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
 

@@ -109,4 +109,19 @@ extern template hipError_t launch_typed<uint16_t>(const BwdProblem& p, hipStream
 // Outputs of a problem with no token (L == 0) or no chain (B == 0 or D == 0).
 hipError_t launch_bwd_empty(const BwdProblem& p, hipStream_t stream);
 
+// ---- conv1d + SiLU prologue ----------------------------------------------------------
+struct ConvProblem {
+  int64_t batch, seqlen, dim;
+  int width;  // 1..4
+  int dtype;  // 0 = fp32, 1 = bf16
+  const void* x;
+  const float* weight;
+  const float* bias;
+  const void* state;
+  void* u;
+  void* state_out;
+};
+
+hipError_t launch_conv(const ConvProblem& p, hipStream_t stream);
+
 }  // namespace ssm

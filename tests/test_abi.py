@@ -16,7 +16,7 @@ FAKE = 0x7F0000000000  # aligned, never dereferenced
 
 def _header_functions():
     text = open(ssm.HEADER_PATH).read()
-    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char \*)\s*(ssm_scan_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char \*)\s*(ssm_\w+)\s*\(", text, re.M)))
 
 
 def _args(**kw):

@@ -158,6 +158,18 @@ def make_cotangents(w: Workload, *, batch: int | None = None, seqlen: int | None
     }
 
 
+def make_conv_params(w: Workload, dim: int | None = None, width: int = 4, seed_extra=()):
+    """Taps (D, W) and bias (D) of the conv1d prologue, fp32, drawn like PyTorch's
+    Conv1d initialisation for a depthwise layer: uniform on +-1/sqrt(W)."""
+    dim = dim or w.dim
+    g = _streams(w.index, (3000, *seed_extra))
+    bound = 1.0 / math.sqrt(width)
+    return {
+        "weight": torch.from_numpy(g[0].uniform(-bound, bound, size=(dim, width)).astype(np.float32)),
+        "bias": torch.from_numpy(g[1].uniform(-bound, bound, size=dim).astype(np.float32)),
+    }
+
+
 def tolerance(dtype: torch.dtype) -> float:
     """Max floored relative error allowed: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs."""
     return 1e-4 if dtype == torch.float32 else 2e-2
