@@ -45,6 +45,15 @@ class _Grads(ctypes.Structure):
     ]
 
 
+class _SsdArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dstate", ctypes.c_int64),
+        ("x", _dp), ("dt", _dp), ("A", _dp), ("Bm", _dp), ("Cm", _dp),
+        ("Dskip", _dp), ("dt_bias", _dp), ("s0", _dp), ("y", _dp), ("sT", _dp),
+    ]
+
+
 def lib_path(mutant: int = 0, out_dir: str | None = None) -> str:
     d = out_dir or _BUILD
     name = "liboracle.so" if mutant == 0 else f"liboracle_mutant{mutant}.so"
@@ -76,6 +85,8 @@ class Oracle:
         self._lib.oracle_scan_bwd_f64.argtypes = [ctypes.POINTER(_Args), ctypes.POINTER(_Grads)]
         self._lib.oracle_scan_bwd_f64.restype = ctypes.c_int
         i64 = ctypes.c_int64
+        self._lib.oracle_ssd_f64.argtypes = [ctypes.POINTER(_SsdArgs)]
+        self._lib.oracle_ssd_f64.restype = ctypes.c_int
         self._lib.oracle_conv1d_silu_f64.argtypes = [i64, i64, i64, i64, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
         self._lib.oracle_conv1d_silu_f64.restype = ctypes.c_int
         self._lib.oracle_softplus_vec.argtypes = [_dp, _dp, ctypes.c_int64]
@@ -191,6 +202,24 @@ class Oracle:
             raise RuntimeError("oracle_conv1d_silu_f64 failed")
         return u, pre, state_out
 
+    def ssd(self, x, dt, A, B, C, D=None, dt_bias=None, s0=None):
+        """Mamba-2 SSD layer, recurrent form: x (B, L, H, P), dt (B, L, H), A (H),
+        B and C (B, L, G, N), D and dt_bias (H), s0 (B, H, P, N).  Returns
+        (y, sT) as float64 numpy arrays."""
+        x, dt, A, B, C = (self._f64(t) for t in (x, dt, A, B, C))
+        D, dt_bias, s0 = (self._f64(t) for t in (D, dt_bias, s0))
+        Bn, L, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        assert dt.shape == (Bn, L, H) and A.shape == (H,) and B.shape == C.shape == (Bn, L, G, N)
+        assert s0 is None or s0.shape == (Bn, H, P, N)
+        y = np.empty_like(x)
+        sT = np.empty((Bn, H, P, N), dtype=np.float64)
+        p = self._ptr
+        a = _SsdArgs(Bn, L, H, P, G, N, p(x), p(dt), p(A), p(B), p(C), p(D), p(dt_bias), p(s0), p(y), p(sT))
+        if self._lib.oracle_ssd_f64(ctypes.byref(a)) != 0:
+            raise RuntimeError("oracle_ssd_f64 failed")
+        return y, sT
+
     def softplus(self, v):
         v = self._f64(v)
         out = np.empty_like(v)
@@ -228,6 +257,10 @@ def scan_bwd(*args, **kw):
 
 def conv1d_silu(*args, **kw):
     return get().conv1d_silu(*args, **kw)
+
+
+def ssd(*args, **kw):
+    return get().ssd(*args, **kw)
 
 
 def softplus(v):

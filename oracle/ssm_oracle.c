@@ -24,7 +24,8 @@
  * the device receives (bf16/fp32 widened without rounding).
  *
  * It also holds the backward pass (gradients of a scalar loss), see
- * oracle_scan_bwd_f64, and the conv1d + SiLU prologue, oracle_conv1d_silu_f64.
+ * oracle_scan_bwd_f64, the conv1d + SiLU prologue, oracle_conv1d_silu_f64, and
+ * the Mamba-2 state-space dual layer in recurrent form, oracle_ssd_f64.
  *
  * Build-time mutations (ORACLE_MUTANT=k, k>0) exist only so the test suite
  * can show that its closed-form pins catch plausible mistakes; the default
@@ -412,6 +413,67 @@ int oracle_conv1d_silu_f64(int64_t Bn, int64_t L, int64_t D, int64_t W, const do
         for (int64_t j = 0; j < H; ++j) state_out[(b * H + j) * D + d] = XIN(L - H + j);
 #undef XIN
     }
+  return 0;
+}
+
+/* Mamba-2 state-space dual layer, recurrent form (youngju.dev, section 4.1:
+ * h_t = A_t h_{t-1} + B_t x_t, y_t = C_t h_t, multi-head, larger N).  Per batch
+ * row b, head h (scalar decay rate A[h]), head channel p and state n, with the
+ * selection and Euler input term of sections 3.1 and 3.3 applied per head:
+ *   delta_t = softplus(dt[b,t,h] + dt_bias[h]),  a_t = exp(delta_t A[h])
+ *   S_t[p,n] = a_t S_{t-1}[p,n] + delta_t x[b,t,h,p] B[b,t,g,n]
+ *   y[b,t,h,p] = sum_n C[b,t,g,n] S_t[p,n] + D[h] x[b,t,h,p]
+ * where g = h / (H / G) is the head's group (B and C are shared by the H / G
+ * heads of a group).  x, y are (B, L, H, P); dt is (B, L, H); B, C are
+ * (B, L, G, N); A, D, dt_bias are (H); the state S0 / ST is (B, H, P, N). */
+typedef struct {
+  int64_t batch, seqlen, nheads, headdim, ngroups, dstate;
+  const double *x, *dt, *A, *Bm, *Cm;
+  const double *Dskip;   /* NULL: no skip term */
+  const double *dt_bias; /* NULL: zero bias    */
+  const double *s0;      /* NULL: zero state   */
+  double *y;             /* (B, L, H, P)       */
+  double *sT;            /* NULL or (B, H, P, N) */
+} oracle_ssd_args;
+
+int oracle_ssd_f64(const oracle_ssd_args *a) {
+  if (!a || a->batch < 0 || a->seqlen < 0 || a->nheads < 0 || a->headdim <= 0 || a->ngroups <= 0 ||
+      a->dstate <= 0 || a->nheads % a->ngroups != 0)
+    return -1;
+  const int64_t Bn = a->batch, L = a->seqlen, H = a->nheads, P = a->headdim, G = a->ngroups, N = a->dstate;
+  double *S = (double *)malloc(sizeof(double) * (size_t)(P * N));
+  if (!S) return -1;
+  for (int64_t b = 0; b < Bn; ++b)
+    for (int64_t h = 0; h < H; ++h) {
+      const int64_t g = h / (H / G);
+      for (int64_t i = 0; i < P * N; ++i) S[i] = a->s0 ? a->s0[(b * H + h) * P * N + i] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        const double delta = oracle_softplus(a->dt[(b * L + t) * H + h] + (a->dt_bias ? a->dt_bias[h] : 0.0));
+#if ORACLE_MUTANT == 21
+        const double at = exp(a->A[h]); /* step size left out of the decay */
+#else
+        const double at = exp(delta * a->A[h]);
+#endif
+        const double *Bt = a->Bm + ((b * L + t) * G + g) * N;
+        const double *Ct = a->Cm + ((b * L + t) * G + g) * N;
+        for (int64_t p = 0; p < P; ++p) {
+          const double xv = a->x[((b * L + t) * H + h) * P + p];
+          double acc = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            S[p * N + n] = at * S[p * N + n] + delta * xv * Bt[n];
+#if ORACLE_MUTANT == 22
+            acc += Bt[n] * S[p * N + n]; /* B read out instead of C */
+#else
+            acc += Ct[n] * S[p * N + n];
+#endif
+          }
+          a->y[((b * L + t) * H + h) * P + p] = acc + (a->Dskip ? a->Dskip[h] : 0.0) * xv;
+        }
+      }
+      if (a->sT)
+        for (int64_t i = 0; i < P * N; ++i) a->sT[(b * H + h) * P * N + i] = S[i];
+    }
+  free(S);
   return 0;
 }
 
