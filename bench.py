@@ -387,6 +387,68 @@ def bench_conv(w, args, ssm, torch):
     return out
 
 
+def bench_ssd(args, ssm, torch):
+    """One step = one ssm_ssd_fwd over the Mamba-2-shaped layer (B4 L8192 H64 P64
+    G1 N128, bf16, hT returned)."""
+    import workloads
+    w = workloads.SSD_BY_NAME[args.ssd]
+    dev = torch.device("cuda:0")
+    log(f"workload {w.describe()}")
+    inp = workloads.make_ssd_inputs(w)
+    d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+    xs = [d["x"], d["x"].clone()]  # alternate so the previous step's x is not in the LLC
+    names = ("dt", "A", "B", "C", "D", "dt_bias")
+    ys = [torch.empty_like(xs[0]) for _ in xs]
+    hT = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        ssm.ssd_fwd(xs[i % 2], *(d[k] for k in names), None, out=ys[i % 2], final_state_out=hT)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    steps = max(args.steps, 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    toks = w.batch * w.seqlen * w.nheads
+    alg = (2 * toks * w.headdim * 2 + toks * 2 + 2 * w.batch * w.seqlen * w.ngroups * w.dstate * 2
+           + w.batch * w.nheads * w.headdim * w.dstate * 4 + 3 * w.nheads * 4)  # x, y, dt, B, C, hT, A/D/bias
+    Q, N, P = 64, w.dstate, w.headdim
+    flops = toks * 2 * (Q * N + Q * P + 2 * N * P)  # C B^T, M X, C H^T, the state update: per token and head
+    ms = elapsed * 1e3 / steps
+    roof = _roofline(alg, kern_s, "ssd_fwd_kernel")
+    roof["mfma_tflops"] = round(flops / kern_s / 1e12, 2)
+    roof["mfma_frac_bf16_dense"] = round(flops / kern_s / 2.5e15, 4)
+    out = {
+        "metric": "SSD layer GElem/s (B*L*H*P*N) + % HBM roofline",
+        "value": round(w.elems / (ms * 1e-3) / 1e9, 2), "unit": "GElem/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "ngroups": w.ngroups, "dstate": w.dstate, "chunk": Q},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t = time.perf_counter()
+        oracle.ssd(inp["x"][:1], inp["dt"][:1], inp["A"], inp["B"][:1], inp["C"][:1], D=inp["D"],
+                   dt_bias=inp["dt_bias"])
+        sec = time.perf_counter() - t
+        el = w.seqlen * w.nheads * w.headdim * w.dstate
+        out["cpu_baseline"] = {"value": round(el / sec / 1e9, 5), "unit": "GElem/s", "cores": 1, "kind": "oracle",
+                               "sample": f"batch row 0, all {w.nheads} heads and {w.seqlen} tokens ({el} state "
+                                         f"updates), fp64 recurrence, single thread; {sec:.2f} s including input widening"}
+    return out
+
+
 def main():
     import workloads
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -400,6 +462,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true", help="time ssm_scan_bwd (all gradients) instead")
     ap.add_argument("--prologue", action="store_true", help="time the conv1d + SiLU prologue on x instead")
+    ap.add_argument("--ssd", nargs="?", const="mamba2_B4_L8192_H64_P64_N128", default=None, metavar="WORKLOAD",
+                    help="time the Mamba-2 SSD layer instead")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the scan, copy a MIB-MiB buffer `steps` times (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -427,6 +491,9 @@ def main():
                           "seconds_per_copy": dt, "GBps": 2 * n * 4 / dt / 1e9}), flush=True)
         return
 
+    if args.ssd:
+        print(json.dumps(bench_ssd(args, ssm, torch)), flush=True)
+        return
     w = workloads.BY_NAME[args.workload]
     if args.prologue:
         if w.chunks > 1 or w.steps:

@@ -209,6 +209,42 @@ typedef struct ssm_conv_args {
  * receives state (or zeros). */
 int ssm_conv1d_silu_fwd(const ssm_conv_args *args, void *stream);
 
+/* ---- Mamba-2 state-space dual (SSD) layer -----------------------------------
+ * The multi-head recurrence of section 4.1 (h_t = A_t h_{t-1} + B_t x_t,
+ * y_t = C_t h_t) with a scalar decay rate per head and the selection and
+ * Euler input term of sections 3.1 and 3.3, per batch row b, head h, head
+ * channel p and state n:
+ *   delta = softplus(dt[b,t,h] + dt_bias[h]),  a = exp(delta A[h])
+ *   S_t[p,n] = a S_{t-1}[p,n] + delta x[b,t,h,p] B[b,t,g,n]
+ *   y[b,t,h,p] = sum_n C[b,t,g,n] S_t[p,n] + D[h] x[b,t,h,p]
+ * g = h / (H / G): B and C are shared by the H / G heads of a group.  It is
+ * evaluated in the chunked matrix (dual) form on the matrix cores.
+ * Layouts: x, y (B, L, H, P); dt (B, L, H); B, C (B, L, G, N) in bf16;
+ * A, D, dt_bias (H) and the state S0 / ST (B, H, P, N) fp32.
+ * Limits of this version: dtype SSM_DTYPE_BF16, headdim P = 64,
+ * dstate N in {64, 128, 256} (SSM_ERR_VARIANT otherwise). */
+typedef struct ssm_ssd_args {
+  int64_t batch, seqlen;      /* B <= 65535, L >= 0                                  */
+  int64_t nheads, headdim;    /* H >= 1, P = 64                                       */
+  int64_t ngroups, dstate;    /* G divides H; N in {64, 128, 256}                     */
+  int32_t dtype;              /* SSM_DTYPE_BF16                                       */
+  int32_t reserved;           /* must be 0                                            */
+  const void *x;              /* (B, L, H, P)                                required */
+  const void *dt;             /* (B, L, H) raw step, before bias and softplus required */
+  const float *A;             /* (H) decay rate per head (normally < 0)      required */
+  const void *B;              /* (B, L, G, N)                                required */
+  const void *C;              /* (B, L, G, N)                                required */
+  const float *D;             /* (H) or NULL                                           */
+  const float *dt_bias;       /* (H) or NULL                                           */
+  const float *h0;            /* (B, H, P, N) initial state or NULL (zeros)            */
+  float *hT;                  /* (B, H, P, N) final state out or NULL                  */
+  void *y;                    /* (B, L, H, P) out                            required */
+} ssm_ssd_args;
+
+/* Errors as for ssm_scan_fwd; y and hT must not overlap any input or each
+ * other (hT may not alias h0).  With L == 0, hT receives h0 (or zeros). */
+int ssm_ssd_fwd(const ssm_ssd_args *args, void *stream);
+
 /* Static, human-readable text for a status code. */
 const char *ssm_scan_strerror(int code);
 

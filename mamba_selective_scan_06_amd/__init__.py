@@ -32,8 +32,8 @@ FLAG_GENERIC_A = 1
 
 # Exported symbols the header declares (checked by the tests).
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_scan_bwd",
-           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd_plan", "ssm_conv1d_silu_fwd", "ssm_scan_strerror",
-           "ssm_scan_abi_version")
+           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd_plan", "ssm_conv1d_silu_fwd", "ssm_ssd_fwd",
+           "ssm_scan_strerror", "ssm_scan_abi_version")
 
 
 class ScanArgs(ctypes.Structure):
@@ -77,6 +77,18 @@ class ConvArgs(ctypes.Structure):
     ]
 
 
+class SsdArgs(ctypes.Structure):
+    """Mirror of ssm_ssd_args in include/ssm_scan.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dstate", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("dt", ctypes.c_void_p), ("A", ctypes.c_void_p),
+        ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p), ("h0", ctypes.c_void_p), ("hT", ctypes.c_void_p), ("y", ctypes.c_void_p),
+    ]
+
+
 # Gradient outputs of the backward: name of the input they belong to -> struct field.
 GRAD_FIELDS = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
                "delta_bias": "ddelta_bias", "h0": "dh0"}
@@ -106,6 +118,8 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_bwd_workspace_bytes.restype = ctypes.c_int64
         L.ssm_scan_bwd_plan.argtypes = [PB]
         L.ssm_scan_bwd_plan.restype = ctypes.c_int64
+        L.ssm_ssd_fwd.argtypes = [ctypes.POINTER(SsdArgs), ctypes.c_void_p]
+        L.ssm_ssd_fwd.restype = ctypes.c_int
         L.ssm_conv1d_silu_fwd.argtypes = [ctypes.POINTER(ConvArgs), ctypes.c_void_p]
         L.ssm_conv1d_silu_fwd.restype = ctypes.c_int
         L.ssm_scan_strerror.argtypes = [ctypes.c_int]
@@ -357,5 +371,52 @@ def conv1d_silu(x, weight, bias=None, state=None, *, return_state=False, out=Non
     return u
 
 
-__all__ = ["scan_fwd", "scan_bwd", "conv1d_silu", "make_conv_args", "ConvArgs", "make_args", "make_bwd_args", "plan", "bwd_plan", "workspace_bytes",
+def make_ssd_args(x, dt, A, B, C, D=None, dt_bias=None, h0=None, hT=None, y=None) -> SsdArgs:
+    """Check shapes/dtypes/devices and fill an ssm_ssd_args."""
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be (B, L, H, P) and B, C (B, L, G, N)")
+    bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    bf, f32, dev = torch.bfloat16, torch.float32, x.device
+    _check("x", x, (bsz, L, H, P), bf, dev)
+    _check("dt", dt, (bsz, L, H), bf, dev)
+    _check("A", A, (H,), f32, dev)
+    _check("B", B, (bsz, L, G, N), bf, dev)
+    _check("C", C, (bsz, L, G, N), bf, dev)
+    _check("D", D, (H,), f32, dev)
+    _check("dt_bias", dt_bias, (H,), f32, dev)
+    _check("h0", h0, (bsz, H, P, N), f32, dev)
+    _check("hT", hT, (bsz, H, P, N), f32, dev)
+    _check("y", y, (bsz, L, H, P), bf, dev)
+    a = SsdArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.ngroups, a.dstate = bsz, L, H, P, G, N
+    a.dtype, a.reserved = DTYPE_BF16, 0
+    a.x, a.dt, a.A, a.B, a.C = _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C)
+    a.D, a.dt_bias, a.h0, a.hT, a.y = _ptr(D), _ptr(dt_bias), _ptr(h0), _ptr(hT), _ptr(y)
+    return a
+
+
+def ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, h0=None, *, return_final_state=False, out=None,
+            final_state_out=None):
+    """Mamba-2 SSD layer forward on the GPU (chunked matrix form on the matrix
+    cores).  Returns y, or (y, hT) with return_final_state=True.  Launches on
+    torch's current HIP stream and does not synchronise."""
+    if not x.is_cuda:
+        raise ValueError("ssd_fwd runs on the GPU only: move the tensors to a HIP device")
+    L_ = lib()
+    y = out if out is not None else torch.empty_like(x)
+    hT = final_state_out
+    if hT is None and return_final_state:
+        hT = torch.empty((x.shape[0], x.shape[2], x.shape[3], B.shape[3]), dtype=torch.float32, device=x.device)
+    args = make_ssd_args(x, dt, A, B, C, D, dt_bias, h0, hT, y)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = L_.ssm_ssd_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise RuntimeError(f"ssm_ssd_fwd: {strerror(rc)}")
+    if return_final_state or final_state_out is not None:
+        return y, hT
+    return y
+
+
+__all__ = ["scan_fwd", "scan_bwd", "conv1d_silu", "ssd_fwd", "make_ssd_args", "SsdArgs", "make_conv_args", "ConvArgs", "make_args", "make_bwd_args", "plan", "bwd_plan", "workspace_bytes",
            "bwd_workspace_bytes", "lib", "strerror", "ScanArgs", "ScanBwdArgs", "EXPORTS"]

@@ -259,6 +259,37 @@ int make_bwd_plan(const ssm_scan_bwd_args* a, BwdPlan* pl) {
 
 bool bwd_has_work(const ssm_scan_bwd_args* a) { return a->batch > 0 && a->seqlen > 0 && a->dim > 0; }
 
+// ---- Mamba-2 SSD ------------------------------------------------------------------------------
+
+int validate_ssd(const ssm_ssd_args* a) {
+  if (!a) return SSM_ERR_NULL;
+  if (a->batch < 0 || a->seqlen < 0 || a->nheads < 1 || a->headdim < 1 || a->ngroups < 1 || a->dstate < 1)
+    return SSM_ERR_SHAPE;
+  if (a->dtype != SSM_DTYPE_BF16) return a->dtype == SSM_DTYPE_F32 ? SSM_ERR_VARIANT : SSM_ERR_DTYPE;
+  if (a->reserved != 0 || a->headdim != 64 || a->nheads % a->ngroups != 0) return SSM_ERR_VARIANT;
+  if (a->dstate != 64 && a->dstate != 128 && a->dstate != 256) return SSM_ERR_VARIANT;
+  if (a->batch > 65535 || a->nheads > 65535) return SSM_ERR_SHAPE;
+  int64_t bl, blh, xe, bn, st, tmp;
+  if (!mul_ok(a->batch, a->seqlen, &bl) || !mul_ok(bl, a->nheads, &blh) || !mul_ok(blh, a->headdim, &xe) ||
+      !mul_ok(bl, a->ngroups * a->dstate, &bn) || !mul_ok(a->batch * a->nheads, a->headdim * a->dstate, &st) ||
+      !mul_ok(xe, 2, &tmp) || !mul_ok(st, 4, &tmp) || !mul_ok(bn, 2, &tmp))
+    return SSM_ERR_SHAPE;
+  const bool tokens = bl > 0;
+  if (!a->A) return SSM_ERR_NULL;
+  if (tokens && (!a->x || !a->dt || !a->B || !a->C || !a->y)) return SSM_ERR_NULL;
+  const void* ptrs[] = {a->x, a->dt, a->A, a->B, a->C, a->D, a->dt_bias, a->h0, a->hT, a->y};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return SSM_ERR_ALIGN;
+  const void* ins[] = {a->x, a->dt, a->A, a->B, a->C, a->D, a->dt_bias, a->h0};
+  const int64_t insz[] = {xe * 2, blh * 2, a->nheads * 4, bn * 2, bn * 2, a->nheads * 4, a->nheads * 4, st * 4};
+  for (int i = 0; i < 8; ++i) {
+    if (overlaps(a->y, xe * 2, ins[i], insz[i])) return SSM_ERR_ALIAS;
+    if (overlaps(a->hT, st * 4, ins[i], insz[i])) return SSM_ERR_ALIAS;
+  }
+  if (overlaps(a->hT, st * 4, a->y, xe * 2)) return SSM_ERR_ALIAS;
+  return SSM_OK;
+}
+
 // ---- conv1d + SiLU prologue ---------------------------------------------------------------
 
 int validate_conv(const ssm_conv_args* a) {
@@ -470,6 +501,31 @@ int ssm_conv1d_silu_fwd(const ssm_conv_args* a, void* stream) {
   p.u = a->u;
   p.state_out = a->state_out;
   const hipError_t e = ssm::launch_conv(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
+}
+
+int ssm_ssd_fwd(const ssm_ssd_args* a, void* stream) {
+  const int rc = validate_ssd(a);
+  if (rc != SSM_OK) return rc;
+  if (a->batch == 0) return SSM_OK;
+  ssm::SsdProblem p;
+  p.batch = a->batch;
+  p.seqlen = a->seqlen;
+  p.nheads = a->nheads;
+  p.headdim = a->headdim;
+  p.ngroups = a->ngroups;
+  p.dstate = a->dstate;
+  p.x = a->x;
+  p.dt = a->dt;
+  p.A = a->A;
+  p.B = a->B;
+  p.C = a->C;
+  p.D = a->D;
+  p.dt_bias = a->dt_bias;
+  p.h0 = a->h0;
+  p.hT = a->hT;
+  p.y = a->y;
+  const hipError_t e = ssm::launch_ssd(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
 

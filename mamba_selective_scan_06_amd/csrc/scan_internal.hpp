@@ -124,4 +124,21 @@ struct ConvProblem {
 
 hipError_t launch_conv(const ConvProblem& p, hipStream_t stream);
 
+// ---- Mamba-2 state-space dual layer ---------------------------------------------------
+struct SsdProblem {
+  int64_t batch, seqlen, nheads, headdim, ngroups, dstate;
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const float* dt_bias;
+  const float* h0;
+  float* hT;
+  void* y;
+};
+
+hipError_t launch_ssd(const SsdProblem& p, hipStream_t stream);
+
 }  // namespace ssm

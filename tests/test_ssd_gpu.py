@@ -1,0 +1,125 @@
+"""Mamba-2 SSD layer on the GPU (ssm_ssd_fwd through the C ABI, chunked
+matrix form on bf16 MFMA) against the fp64 oracle's recurrence.
+
+Tolerance: 2e-2 floored max relative error (bf16 inputs, workloads.rel_err).
+Besides the inputs' own rounding, the kernel rounds three MFMA operands to
+bf16 (the decayed mask M, the weighted x of the state update and the state
+copy read by the inter-chunk term), each a relative 2^-9 per element inside
+fp32 sums; y is rounded once to bf16.  The fp32 final state is held to the
+same bound.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import mamba_selective_scan_06_amd as ssm
+import oracle
+import workloads
+from tests.gpu_helpers import DEV, check
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a HIP GPU"),
+]
+
+SW = workloads.SSD_WORKLOADS
+TENS = ("x", "dt", "A", "B", "C", "D", "dt_bias", "h0")
+TOL = workloads.tolerance(torch.bfloat16)
+
+
+def gpu_ssd(inp):
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    y, hT = ssm.ssd_fwd(*(d[k] for k in TENS), return_final_state=True)
+    torch.cuda.synchronize()
+    return y.float().cpu().double().numpy(), hT.cpu().double().numpy()
+
+
+def oracle_ssd(inp):
+    return oracle.ssd(*(inp[k] for k in ("x", "dt", "A", "B", "C")), D=inp["D"], dt_bias=inp["dt_bias"],
+                      s0=inp["h0"])
+
+
+CASES = [
+    dict(dstate=64, ngroups=2, seqlen=200),
+    dict(dstate=128, ngroups=1, seqlen=200),
+    dict(dstate=256, ngroups=4, seqlen=130),
+    dict(dstate=128, ngroups=2, seqlen=64),   # exactly one chunk
+    dict(dstate=128, ngroups=2, seqlen=65),   # one token into the second chunk
+    dict(dstate=64, ngroups=1, seqlen=1),
+    dict(dstate=64, ngroups=4, seqlen=63),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"N{c['dstate']}-G{c['ngroups']}-L{c['seqlen']}" for c in CASES])
+@pytest.mark.parametrize("with_h0", [False, True], ids=["zero-state", "h0"])
+def test_ssd_small_all_elements(case, with_h0):
+    inp = workloads.make_ssd_inputs(SW[0], with_h0=with_h0, **case)
+    y, hT = gpu_ssd(inp)
+    yr, hr = oracle_ssd(inp)
+    check("y", y, yr, torch.bfloat16)
+    check("hT", hT, hr, torch.bfloat16)
+
+
+def test_ssd_without_skip_and_bias():
+    """D and dt_bias absent: the scan part of y alone (D x no longer masks it)."""
+    inp = workloads.make_ssd_inputs(SW[0], dstate=128, seqlen=150)
+    inp["D"] = None
+    inp["dt_bias"] = None
+    y, hT = gpu_ssd(inp)
+    yr, hr = oracle_ssd(inp)
+    check("y", y, yr, torch.bfloat16)
+    check("hT", hT, hr, torch.bfloat16)
+
+
+def test_ssd_chained_calls():
+    """A sequence fed as three calls through the carried state matches the
+    oracle's single call."""
+    inp = workloads.make_ssd_inputs(SW[0], dstate=128, seqlen=300, with_h0=True)
+    yr, hr = oracle_ssd(inp)
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    h = d["h0"]
+    ys = []
+    for a, b in [(0, 70), (70, 192), (192, 300)]:
+        sl = slice(a, b)
+        y, h = ssm.ssd_fwd(d["x"][:, sl].contiguous(), d["dt"][:, sl].contiguous(), d["A"],
+                           d["B"][:, sl].contiguous(), d["C"][:, sl].contiguous(), d["D"], d["dt_bias"], h,
+                           return_final_state=True)
+        ys.append(y)
+    torch.cuda.synchronize()
+    check("y chained", torch.cat(ys, dim=1).float().cpu().double().numpy(), yr, torch.bfloat16)
+    check("hT chained", h.cpu().double().numpy(), hr, torch.bfloat16)
+
+
+def test_ssd_empty_sequence_passes_state():
+    inp = workloads.make_ssd_inputs(SW[0], dstate=64, seqlen=0, with_h0=True)
+    y, hT = gpu_ssd(inp)
+    assert y.shape[1] == 0
+    assert np.array_equal(hT, inp["h0"].double().numpy())
+
+
+def test_ssd_deterministic():
+    inp = workloads.make_ssd_inputs(SW[0], dstate=128, seqlen=200)
+    y1, h1 = gpu_ssd(inp)
+    y2, h2 = gpu_ssd(inp)
+    assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
+
+
+def test_ssd_mamba2_full_size_sampled_heads():
+    """The page's Mamba-2 layer shape at B4 L8192 (H64 P64 N128), launched as the
+    bench launches it; heads are independent, so two heads of every batch row are
+    checked against the oracle (their group's B and C)."""
+    w = SW[1]
+    inp = workloads.make_ssd_inputs(w)
+    y, hT = gpu_ssd(inp)
+    for hsel in (0, 37):
+        sub = {k: v for k, v in inp.items()}
+        hi = torch.tensor([hsel])
+        for k in ("x", "dt"):
+            sub[k] = inp[k].index_select(2, hi).contiguous()
+        for k in ("A", "D", "dt_bias"):
+            sub[k] = inp[k].index_select(0, hi)
+        yr, hr = oracle.ssd(sub["x"], sub["dt"], sub["A"], inp["B"], inp["C"], D=sub["D"], dt_bias=sub["dt_bias"])
+        check(f"y head {hsel}", y[:, :, hsel:hsel + 1], yr, torch.bfloat16)
+        check(f"hT head {hsel}", hT[:, hsel:hsel + 1], hr, torch.bfloat16)

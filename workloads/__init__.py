@@ -170,6 +170,65 @@ def make_conv_params(w: Workload, dim: int | None = None, width: int = 4, seed_e
     }
 
 
+@dataclasses.dataclass(frozen=True)
+class SsdWorkload:
+    """A Mamba-2 state-space dual layer: x (B, L, H, P), B/C (B, L, G, N)."""
+    index: int
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    dstate: int
+
+    @property
+    def elems(self) -> int:
+        """B*L*H*P*N state updates of the whole workload."""
+        return self.batch * self.seqlen * self.nheads * self.headdim * self.dstate
+
+    def describe(self) -> str:
+        return (f"{self.name}: B={self.batch} L={self.seqlen} H={self.nheads} P={self.headdim} "
+                f"G={self.ngroups} N={self.dstate} bf16")
+
+
+# The page's Mamba-2 layer (d_model 2048, expand 2, headdim 64, d_state 128:
+# 64 heads, one B/C group) at the token count of the 1.4B-shaped scan layer,
+# and a small case for element-wise parity.
+SSD_WORKLOADS = [
+    SsdWorkload(100, "ssd_small_B2_L200_H4_P64_G2_N64", 2, 200, 4, 64, 2, 64),
+    SsdWorkload(101, "mamba2_B4_L8192_H64_P64_N128", 4, 8192, 64, 64, 1, 128),
+]
+SSD_BY_NAME = {w.name: w for w in SSD_WORKLOADS}
+
+
+def make_ssd_inputs(w: SsdWorkload, *, batch=None, seqlen=None, nheads=None, ngroups=None, dstate=None,
+                    with_h0=False, seed_extra=()):
+    """Seeded CPU tensors of one SSD call: x, dt, B, C bf16 ~ N(0, 1); A[h] = -U(1, 16)
+    (the Mamba-2 initialisation A = -exp(A_log), A_log = log U(1, 16)); dt_bias the
+    inverse softplus of log-uniform [1e-3, 1e-1] steps; D = 1; h0 ~ N(0, 0.1) or None."""
+    bsz = batch or w.batch
+    L = seqlen if seqlen is not None else w.seqlen
+    H = nheads or w.nheads
+    G = ngroups or w.ngroups
+    N = dstate or w.dstate
+    P = w.headdim
+    g = _streams(w.index, seed_extra)
+    f32 = np.float32
+    bf = torch.bfloat16
+    u = np.exp(g[5].uniform(math.log(1e-3), math.log(1e-1), size=H))
+    return {
+        "x": _cast(g[0].standard_normal((bsz, L, H, P), dtype=f32), bf),
+        "dt": _cast(g[1].standard_normal((bsz, L, H), dtype=f32), bf),
+        "A": torch.from_numpy(-g[4].uniform(1.0, 16.0, size=H).astype(f32)),
+        "B": _cast(g[2].standard_normal((bsz, L, G, N), dtype=f32), bf),
+        "C": _cast(g[3].standard_normal((bsz, L, G, N), dtype=f32), bf),
+        "D": torch.ones(H, dtype=torch.float32),
+        "dt_bias": torch.from_numpy(np.log(np.expm1(u)).astype(f32)),
+        "h0": torch.from_numpy((g[6].standard_normal((bsz, H, P, N)) * 0.1).astype(f32)) if with_h0 else None,
+    }
+
+
 def tolerance(dtype: torch.dtype) -> float:
     """Max floored relative error allowed: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs."""
     return 1e-4 if dtype == torch.float32 else 2e-2
