@@ -125,8 +125,14 @@ struct ConvProblem {
 hipError_t launch_conv(const ConvProblem& p, hipStream_t stream);
 
 // ---- Mamba-2 state-space dual layer ---------------------------------------------------
+// One kernel serves two recurrences over a P x N matrix state per (b, h):
+//   mode 0 (SSD):  a_t = softplus(dt + dt_bias[h]) A[h],  i_t = softplus(dt + dt_bias[h]),  + D[h] x
+//   mode 1 (gated linear attention): a_t = log_f[b,t,h] (0 if null), i_t = in_gate[b,t,h] (1 if null)
+//   mode 2: mode 1 with the feature map elu(v) + 1 applied to B (keys) and C (queries)
+// S_t = exp(a_t) S_{t-1} + i_t x_t B_t^T,  y_t = S_t C_t.
 struct SsdProblem {
   int64_t batch, seqlen, nheads, headdim, ngroups, dstate;
+  int mode = 0;
   const void* x;
   const void* dt;
   const float* A;
@@ -134,6 +140,8 @@ struct SsdProblem {
   const void* C;
   const float* D;
   const float* dt_bias;
+  const float* log_f = nullptr;
+  const float* in_gate = nullptr;
   const float* h0;
   float* hT;
   void* y;

@@ -1,34 +1,50 @@
-// Mamba-2 state-space dual (SSD) layer, forward, in chunked matrix form on
-// MFMA (page youngju.dev "Mamba 논문 리뷰", section 4.1: the recurrence
-// h_t = A_t h_{t-1} + B_t x_t, y_t = C_t h_t is also the structured masked
-// attention Y = (T o M) X).  Per batch row b and head h, with scalar decay
-// rate A[h], delta_t = softplus(dt + dt_bias[h]) and the Euler input term:
-//   S_t = exp(delta_t A[h]) S_{t-1} + delta_t x_t B_t^T      (S: P x N, fp32)
-//   y_t = S_t C_t + D[h] x_t
-// Cut into chunks of Q = 64 tokens, with cs_t the running sum of delta A
-// inside the chunk (cs_end its last value) and H the state entering it:
-//   G      = C B^T                               (Q x Q, contraction over N)
-//   M[t,s] = G[t,s] exp(cs_t - cs_s) delta_s  for s <= t, else 0
-//   y      = M X + exp(cs_t) C H^T + D x        (Q x P)
-//   H'     = exp(cs_end) H + (X o w)^T B,  w_s = exp(cs_end - cs_s) delta_s
-// Every product is a bf16 MFMA (v_mfma_f32_32x32x16_bf16) with fp32
-// accumulation; the state H stays fp32 in registers.  The three operands that
-// are computed in fp32 (M, x o w and the state copy read by C H^T) are split
-// into hi + lo bf16 halves, each product taking two MFMAs: rounding them to
-// one bf16 alone costs a relative 1e-2 in y and 2e-2 in the state, the split
-// leaves about 2^-16.  The other operands (x, B, C) are bf16 inputs, exact.
+// Matrix-state recurrences in chunked matrix form on MFMA: the Mamba-2
+// state-space dual (SSD) layer (page youngju.dev "Mamba 논문 리뷰", section
+// 4.1: the recurrence h_t = A_t h_{t-1} + B_t x_t, y_t = C_t h_t equals the
+// structured masked attention Y = (T o M) X) and its gated-linear-attention
+// relatives (the linear-attention recurrence s_t = s_{t-1} + k_t^T v_t of the
+// HedgeMamba review's stage 2, and the mLSTM update of the xLSTM review: the
+// matrix state scaled by a forget gate plus an input-gated outer product).
 //
-// One workgroup (4 waves) per (b, h) walks the chunks in order.  Per chunk:
-//   1. one wave turns dt into delta and the prefix sums cs (LDS);
-//   2. x and B are written to LDS transposed (token index contiguous), x also
-//      scaled by w, for the two products that contract over tokens;
-//   3. each wave computes one 32x32 tile of G (its C and B operands come
-//      straight from HBM, n contiguous), masks it into M (LDS), and one 32x32
-//      tile of C H^T;
-//   4. each wave finishes one 32x32 tile of y (M X from LDS) and N/64 tiles
-//      of the state update.
-// Tokens past L are padded with delta = 0 and x = B = C = 0, which leaves the
-// state unchanged, and are not stored.
+// Per batch row b and head h, with per-token log decay a_t and input scale i_t:
+//   S_t = exp(a_t) S_{t-1} + i_t x_t B_t^T      (S: P x N, fp32)
+//   y_t = S_t C_t (+ D[h] x_t for SSD)
+//   SSD: i_t = softplus(dt + dt_bias[h]), a_t = i_t A[h]
+//   gated linear attention: a_t = log_f (0 if absent), i_t = in_gate (1 if absent);
+//   optionally the feature map elu(v) + 1 on B (keys) and C (queries).
+// Cut into chunks of Q = 64 tokens, cs_t the running sum of a inside the chunk
+// (cs_end its last value) and H the state entering it:
+//   M[t,s] = (C_t . B_s) exp(cs_t - cs_s) i_s  for s <= t, else 0;  M[t,t] += D
+//   y      = M X + exp(cs_t) C H^T               (Q x P)
+//   H'     = exp(cs_end) H + (X o w)^T B,  w_s = exp(cs_end - cs_s) i_s
+// Every product is v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  The
+// operands computed in fp32 (M, x o w and the state read by C H^T) are split
+// into hi + lo bf16 halves, two MFMAs each: one bf16 rounding of them costs
+// about 1e-2 relative in y and 2e-2 in the state, the split about 2^-16.
+// x, B and C are bf16 inputs, exact.  D enters through M's diagonal.
+//
+// One workgroup per (b, h) walks the chunks in order: 8 waves for N <= 128
+// (two per SIMD), 4 for N = 256 (LDS).  Wave w owns the channel slice p in
+// [16 (w mod 4), +16) and, with 8 waves, one half of the n range: its part of
+// the state stays in registers in MFMA accumulator layout, which is also the
+// operand layout C H^T needs, so the state never goes through LDS; the two
+// waves of a slice exchange their halves of C H^T through LDS.  Products are
+// taken transposed (y^T = X^T M^T, G^T = B C^T) so each lane's accumulator
+// holds 4 consecutive channels or tokens: y leaves as 8-byte stores and M
+// enters LDS as 8-byte writes.  B and C are staged in LDS with n permuted
+// inside each 32-wide group so that a lane's 8 operand values for C H^T sit in
+// one 16-byte read.  Global traffic uses buffer loads and stores whose
+// descriptor covers the chunk's valid tokens (past L: loads read 0, stores are
+// dropped), and the next chunk's x, B, C and per-token inputs are loaded
+// during the current chunk (the barriers wait on LDS only).  Per chunk:
+//   A. per-token prefix sums (wave 0); x^T, B^T, B, C into LDS; prefetch;
+//   B. x o w into LDS; M = masked G^T tiles (12 16x16 tiles); partial C H^T;
+//   C. y^T for the wave's tiles (M X from LDS), store; state update.
+// Tokens past L are padded with i = 0, a = 0 and x = B = C = 0, which leaves
+// the state unchanged.
+#include <type_traits>
+
+#include "buffer_io.hpp"
 #include "device_common.hpp"
 #include "scan_internal.hpp"
 
@@ -36,113 +52,205 @@ namespace ssm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQ = 64;   // tokens per chunk
 constexpr int kP = 64;   // head channels (headdim)
-constexpr int kPad = 8;  // bf16 padding of every LDS row (16 bytes), against bank conflicts
+constexpr int kPad = 8;  // bf16 padding of LDS rows (16 bytes), against bank conflicts
 
-__device__ __forceinline__ bf16x8 ld_bf16x8(const void* p) {
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
-__device__ __forceinline__ bf16x8 zero_bf16x8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+__device__ __forceinline__ float bits_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-__device__ __forceinline__ uint16_t to_bf16_bits(float v) { return __bfloat16_as_ushort(__float2bfloat16(v)); }
-
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// Two fp32 values rounded (nearest even) to a packed bf16 pair, a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
-// Row and column of element r of a 32x32 MFMA accumulator held by lane l.
-__device__ __forceinline__ int acc_row(int r, int l) { return 8 * (r >> 2) + 4 * (l >> 5) + (r & 3); }
-__device__ __forceinline__ int acc_col(int l) { return l & 31; }
-
-// hi and lo bf16 halves of an fp32 value: v ~ hi + lo to about 2^-16.
-__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
-  hi = to_bf16_bits(v);
-  lo = to_bf16_bits(v - __uint_as_float(static_cast<uint32_t>(hi) << 16));
+// hi and lo bf16 halves of two fp32 values, packed: v ~ hi + lo to about 2^-16.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16(a, b);
+  lo = pack_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
-template <int N>
-struct SsdSmem {
-  uint16_t M[2][kQ][kQ + kPad];   // masked, decayed C B^T, hi and lo halves, rows t
+// bf16 e (0..2W-1, a compile-time constant once unrolled) of W packed words.
+template <int W>
+__device__ __forceinline__ uint32_t elem(const uint32_t (&v)[W], int e) {
+  return (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu);
+}
+
+// elu(v) + 1 on 8 packed bf16, rounded back to bf16.
+__device__ __forceinline__ void feature_map(uint32_t (&v)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xffff0000u);
+    v[i] = pack_bf16(lo > 0.0f ? lo + 1.0f : fast_exp2(lo * kLog2e), hi > 0.0f ? hi + 1.0f : fast_exp2(hi * kLog2e));
+  }
+}
+
+// Eight consecutive n (n0 = 8 q) of one row into the permuted n order: inside a
+// 32-wide group, position 8 g + e holds n = 4 g + (e & 3) + 16 (e >> 2).
+__device__ __forceinline__ void write_perm(uint16_t* row, int n0, const uint32_t (&v)[4]) {
+  const int u = n0 & 31;
+  const int pp = (n0 & ~31) + 8 * ((u & 15) >> 2) + 4 * (u >> 4);
+  *reinterpret_cast<uint2*>(row + pp) = make_uint2(v[0], v[1]);
+  *reinterpret_cast<uint2*>(row + pp + 8) = make_uint2(v[2], v[3]);
+}
+
+template <int N, int NW>
+struct alignas(16) SsdSmem {
+  uint16_t M[2][kQ][kQ + kPad];   // masked decayed C B^T (+ D on the diagonal), hi and lo: [t][s]
   uint16_t xt[kP][kQ + kPad];     // x transposed: [p][s]
   uint16_t xw[2][kP][kQ + kPad];  // x o w transposed, hi and lo: [p][s]
   uint16_t bt[N][kQ + kPad];      // B transposed: [n][s]
-  uint16_t hb[2][kP][N + kPad];   // the state entering the chunk, hi and lo: [p][n]
-  float dl[kQ];                   // delta per token of the chunk (0 past L)
-  float cs[kQ];                   // running sum of delta A inside the chunk
+  uint16_t bn[kQ][N + kPad];      // B, n permuted: [s][n]
+  uint16_t cn[kQ][N + kPad];      // C, n permuted: [t][n]
+  float dl[kQ];                   // input scale i per token (0 past L)
+  float cs[kQ];                   // running sum of the log decay inside the chunk
+  float4 xch[NW > 4 ? NW : 1][2][64];  // halves of C H^T handed to the slice's other wave
 };
 
-template <int N>
-__global__ __launch_bounds__(256) void ssd_fwd_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt,
-                                                      const float* __restrict__ A, const uint16_t* __restrict__ Bm,
-                                                      const uint16_t* __restrict__ Cm, const float* __restrict__ Dsk,
-                                                      const float* __restrict__ dt_bias, const float* __restrict__ h0,
-                                                      float* __restrict__ hT, uint16_t* __restrict__ y, int64_t L,
-                                                      int H, int G) {
-  constexpr int NT = N / 64;  // state tiles (32 x 32) per wave
-  __shared__ SsdSmem<N> sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t b = blockIdx.y;
+struct KArgs {
+  const uint16_t* x;
+  const uint16_t* dt;
+  const float* A;
+  const uint16_t* B;
+  const uint16_t* C;
+  const float* D;
+  const float* dt_bias;
+  const float* log_f;
+  const float* in_gate;
+  const float* h0;
+  float* hT;
+  uint16_t* y;
+  int64_t L;
+  int H, G;
+};
+
+
+template <int N, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
+  constexpr int NK = NW / 4;          // parts of the n range, one per wave of a channel slice
+  constexpr int XC = 8 / NK;          // x channels per staging thread (2 tokens each)
+  constexpr int XG = kP / XC;         // x channel groups
+  constexpr int TPT = N / (8 * NW);   // tokens per staging thread for B and C (8 n each)
+  constexpr int TG = kQ / TPT;        // token groups per n group
+  constexpr int NMK = N / 32 / NK;    // 32-wide k steps over the wave's n part
+  constexpr int NJK = N / 16 / NK;    // 16-row state tiles per wave
+  static_assert(TPT >= 1 && NMK >= 1, "unsupported state size for this wave count");
+  __shared__ SsdSmem<N, NW> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wi = wave_id();
+  const int w = wi & 3, k = wi >> 2;  // channel slice, n part
+  const int lr = lane & 15, lg = lane >> 4;
+  const int64_t b = blockIdx.y, L = a.L;
   const int h = blockIdx.x;
-  const int g = h / (H / G);
-  const float Ah = A[h];
-  const float bias = dt_bias ? dt_bias[h] : 0.0f;
-  const float Dh = Dsk ? Dsk[h] : 0.0f;
-  const int64_t xrow = static_cast<int64_t>(H) * kP;  // elements between tokens in x / y
-  const int64_t brow = static_cast<int64_t>(G) * N;   // elements between tokens in B / C
-  const uint16_t* xb = x + (b * L * H + h) * kP;
-  uint16_t* yb = y + (b * L * H + h) * kP;
-  const uint16_t* Bb = Bm + (b * L * G + g) * N;
-  const uint16_t* Cb = Cm + (b * L * G + g) * N;
-
-  // this wave's tiles: (ti, tj) of G and y; state tiles q = w + 4 i of the N x P state (rows n, cols p)
-  const int ti = w >> 1, tj = w & 1;
-  const int col = acc_col(lane);
-
-  // the state, fp32, in accumulator layout: Hs[i][r] = S[p = 32 (q & 1) + col][n = 32 (q >> 1) + acc_row(r)]
-  float Hs[NT][16];
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const int q = w + 4 * i, p = 32 * (q & 1) + col;
-#pragma unroll
-    for (int r = 0; r < 16; r += 4) {
-      const int n = 32 * (q >> 1) + acc_row(r, lane);
-      float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if (h0) v = *reinterpret_cast<const float4*>(h0 + ((b * H + h) * kP + p) * N + n);
-      Hs[i][r] = v.x, Hs[i][r + 1] = v.y, Hs[i][r + 2] = v.z, Hs[i][r + 3] = v.w;
-    }
+  const int g = h / (a.H / a.G);
+  const int64_t xrow = static_cast<int64_t>(a.H) * kP;  // elements between tokens in x / y
+  const int64_t brow = static_cast<int64_t>(a.G) * N;   // elements between tokens in B / C
+  const uint16_t* xb = a.x + (b * L * a.H + h) * kP;
+  uint16_t* yb = a.y + (b * L * a.H + h) * kP;
+  const uint16_t* Bb = a.B + (b * L * a.G + g) * N;
+  const uint16_t* Cb = a.C + (b * L * a.G + g) * N;
+  float Ah = 0.0f, bias = 0.0f, Dh = 0.0f;
+  if constexpr (MODE == 0) {
+    Ah = a.A[h];
+    bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    Dh = a.D ? a.D[h] : 0.0f;
   }
-  auto write_hb = [&]() {
+  // staging roles: x as 2 tokens x XC channels, B and C as TPT tokens x 8 n
+  const int xpg = tid % XG, xtq = tid / XG;
+  const int btq = tid % TG, bng = tid / TG;
+  // buffer descriptor over the rows [t0, min(t0 + 64, L)) of a (tokens x row) tensor;
+  // empty (every access out of range) past the end or for an absent input
+  auto rows_buf = [&](const void* base, int64_t t0, int64_t row_bytes, int64_t used_bytes, bool present = true) {
+    const int64_t rows = L - t0 < kQ ? L - t0 : kQ;
+    const int64_t bytes = rows > 0 && present ? (rows - 1) * row_bytes + used_bytes : 0;
+    return make_buf(present ? base : a.x, static_cast<uint32_t>(bytes));
+  };
+
+  // the wave's state part: Hs[j][r] = S[p = 16 w + lr][n = 16 (k NJK + j) + 4 lg + r]
+  float Hs[NJK][4];
+  const int64_t sbase = ((b * a.H + h) * kP + 16 * w + lr) * N + 16 * k * NJK + 4 * lg;
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int q = w + 4 * i, p = 32 * (q & 1) + col;
+  for (int j = 0; j < NJK; ++j) {
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (a.h0) v = *reinterpret_cast<const float4*>(a.h0 + sbase + 16 * j);
+    Hs[j][0] = v.x, Hs[j][1] = v.y, Hs[j][2] = v.z, Hs[j][3] = v.w;
+  }
+
+  // raw data of the next chunk, loaded one chunk ahead
+  uint32_t xr[2][XC / 2], br[TPT][4], cr[TPT][4];
+  uint32_t traw = 0, tlf = 0, tig = 0;  // the lane's per-token inputs (raw bits): dt, or log_f and in_gate
+  auto load_x = [&](int64_t t0) {
+    const auto r = rows_buf(xb + t0 * xrow, t0, xrow * 2, kP * 2);
 #pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        const int n = 32 * (q >> 1) + acc_row(r, lane);
-        uint16_t hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) split_bf16(Hs[i][r + e], hi[e], lo[e]);
-        *reinterpret_cast<uint2*>(&sm.hb[0][p][n]) =
-            make_uint2(hi[0] | (static_cast<uint32_t>(hi[1]) << 16), hi[2] | (static_cast<uint32_t>(hi[3]) << 16));
-        *reinterpret_cast<uint2*>(&sm.hb[1][p][n]) =
-            make_uint2(lo[0] | (static_cast<uint32_t>(lo[1]) << 16), lo[2] | (static_cast<uint32_t>(lo[3]) << 16));
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t off = static_cast<uint32_t>((2 * xtq + j) * xrow * 2 + XC * xpg * 2);
+      if constexpr (XC == 8) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        xr[j][0] = v.x, xr[j][1] = v.y, xr[j][2] = v.z, xr[j][3] = v.w;
+      } else {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        xr[j][0] = v.x, xr[j][1] = v.y;
       }
     }
   };
-  write_hb();
+  auto load_bc = [&](int64_t t0) {
+    const auto rb = rows_buf(Bb + t0 * brow, t0, brow * 2, N * 2);
+    const auto rc = rows_buf(Cb + t0 * brow, t0, brow * 2, N * 2);
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      const uint32_t off = static_cast<uint32_t>((TPT * btq + j) * brow * 2 + 16 * bng);
+      const u32x4 vb = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+      const u32x4 vc = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
+      br[j][0] = vb.x, br[j][1] = vb.y, br[j][2] = vb.z, br[j][3] = vb.w;
+      cr[j][0] = vc.x, cr[j][1] = vc.y, cr[j][2] = vc.z, cr[j][3] = vc.w;
+    }
+  };
+  auto load_tok = [&](int64_t t0) {  // wave 0 only: it turns them into delta and the prefix sums
+    if (wi != 0) return;
+    const int64_t i0 = (b * L + t0) * a.H + h;
+    const uint32_t off = static_cast<uint32_t>(lane * a.H);
+    if constexpr (MODE == 0) {
+      traw = __builtin_amdgcn_raw_buffer_load_b16(rows_buf(a.dt + i0, t0, a.H * 2, 2), off * 2, 0, 0);
+    } else {
+      tlf = __builtin_amdgcn_raw_buffer_load_b32(rows_buf(a.log_f + i0, t0, a.H * 4, 4, a.log_f), off * 4, 0, 0);
+      tig = __builtin_amdgcn_raw_buffer_load_b32(rows_buf(a.in_gate + i0, t0, a.H * 4, 4, a.in_gate), off * 4, 0, 0);
+    }
+  };
 
   const int64_t nchunks = (L + kQ - 1) / kQ;
+  load_bc(0);
+  load_tok(0);
+  load_x(0);
+  // wait for the first chunk here, so that the wait at the top of the loop is set
+  // by the loop alone: only the y stores issued after the prefetch are still in
+  // flight there, and the wait lets them run (vmcnt counts stores too)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t t0 = c * kQ;
-    // ---- 1. delta and the prefix sums of delta A (wave 0, one token per lane)
-    if (w == 0) {
-      const int64_t t = t0 + lane;
-      float d = 0.0f;
-      if (t < L) d = softplus_f32(to_f32(dt[(b * L + t) * H + h]) + bias);
-      float s = d * Ah;
+    // ---- A. per-token scalars (wave 0, one token per lane); x^T, B^T, B, C into LDS
+    if (wi == 0) {
+      const bool valid = t0 + lane < L;
+      float d, la;
+      if constexpr (MODE == 0) {
+        d = valid ? softplus_f32(bits_f32(traw) + bias) : 0.0f;
+        la = d * Ah;
+      } else {
+        d = valid ? (a.in_gate ? __uint_as_float(tig) : 1.0f) : 0.0f;
+        la = valid ? __uint_as_float(tlf) : 0.0f;
+      }
+      float s = la;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float o = __shfl_up(s, off, 64);
@@ -151,150 +259,238 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(const uint16_t* __restrict
       sm.dl[lane] = d;
       sm.cs[lane] = s;
     }
-    // ---- loads of this chunk's x and B rows (8 channels or states per vector)
-    uint4 xv[2], bv[N / 32];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {  // x: 64 tokens x 8 vectors of 8 channels
-      const int t = tid & 63, pg = (tid >> 6) + 4 * i;
-      xv[i] = (t0 + t < L) ? *reinterpret_cast<const uint4*>(xb + (t0 + t) * xrow + 8 * pg) : make_uint4(0, 0, 0, 0);
+    for (int e = 0; e < XC; ++e)
+      *reinterpret_cast<uint32_t*>(&sm.xt[XC * xpg + e][2 * xtq]) = elem(xr[0], e) | (elem(xr[1], e) << 16);
+    if constexpr (MODE == 2) {
+#pragma unroll
+      for (int j = 0; j < TPT; ++j) feature_map(br[j]), feature_map(cr[j]);
     }
 #pragma unroll
-    for (int i = 0; i < N / 32; ++i) {  // B: 64 tokens x N/8 vectors
-      const int t = tid & 63, ng = (tid >> 6) + 4 * i;
-      bv[i] = (t0 + t < L) ? *reinterpret_cast<const uint4*>(Bb + (t0 + t) * brow + 8 * ng) : make_uint4(0, 0, 0, 0);
-    }
-    // G and C H^T operands: C rows t = 32 ti + lane % 32 (also the A operand of C H^T),
-    // B rows s = 32 tj + lane % 32, n = 16 k + 8 (lane / 32) + e
-    bf16x8 ca[N / 16], ba[N / 16];
-    {
-      const int tc = 32 * ti + (lane & 31), ts = 32 * tj + (lane & 31), nh = 8 * (lane >> 5);
+    for (int e = 0; e < 8; ++e) {
+      uint16_t* dst = &sm.bt[8 * bng + e][TPT * btq];
+      if constexpr (TPT == 1) {
+        *dst = static_cast<uint16_t>(elem(br[0], e));
+      } else {
+        uint32_t q[TPT / 2];
 #pragma unroll
-      for (int k = 0; k < N / 16; ++k) {
-        ca[k] = (t0 + tc < L) ? ld_bf16x8(Cb + (t0 + tc) * brow + 16 * k + nh) : zero_bf16x8();
-        ba[k] = (t0 + ts < L) ? ld_bf16x8(Bb + (t0 + ts) * brow + 16 * k + nh) : zero_bf16x8();
+        for (int j = 0; j < TPT / 2; ++j) q[j] = elem(br[2 * j], e) | (elem(br[2 * j + 1], e) << 16);
+        if constexpr (TPT == 2) *reinterpret_cast<uint32_t*>(dst) = q[0];
+        if constexpr (TPT == 4) *reinterpret_cast<uint2*>(dst) = make_uint2(q[0], q[1]);
+        if constexpr (TPT == 8) *reinterpret_cast<uint4*>(dst) = make_uint4(q[0], q[1], q[2], q[3]);
       }
     }
-    __syncthreads();  // delta, cs visible
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      write_perm(sm.bn[TPT * btq + j], 8 * bng, br[j]);
+      write_perm(sm.cn[TPT * btq + j], 8 * bng, cr[j]);
+    }
+    load_bc(t0 + kQ);  // past the last chunk these read nothing
+    load_tok(t0 + kQ);
+    __syncthreads();  // dl, cs, xt, bt, bn, cn complete
+
+    // ---- B. x o w; masked G^T tiles into M; the wave's part of C H^T
     const float cs_end = sm.cs[kQ - 1];
-    // ---- 2. transposed x, x o w and B into LDS
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int t = tid & 63, pg = (tid >> 6) + 4 * i;
-      const float wt = fast_exp2((cs_end - sm.cs[t]) * kLog2e) * sm.dl[t];
-      const uint32_t ww[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t bits = static_cast<uint16_t>(ww[e >> 1] >> (16 * (e & 1)));
-        sm.xt[8 * pg + e][t] = bits;
-        split_bf16(wt * __uint_as_float(static_cast<uint32_t>(bits) << 16), sm.xw[0][8 * pg + e][t],
-                   sm.xw[1][8 * pg + e][t]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < N / 32; ++i) {
-      const int t = tid & 63, ng = (tid >> 6) + 4 * i;
-      const uint32_t ww[4] = {bv[i].x, bv[i].y, bv[i].z, bv[i].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm.bt[8 * ng + e][t] = static_cast<uint16_t>(ww[e >> 1] >> (16 * (e & 1)));
-    }
-    // ---- 3. G tile (ti, tj) masked into M; C H^T tile (ti, tj)
-    if (tj <= ti) {  // the tile above the diagonal is all masked
-      f32x16 gacc = {};
-#pragma unroll
-      for (int k = 0; k < N / 16; ++k) gacc = mfma(ca[k], ba[k], gacc);
-      const int s = 32 * tj + col;
-      const float cs_s = sm.cs[s], dl_s = sm.dl[s];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * ti + acc_row(r, lane);
-        const float m = s <= t ? gacc[r] * fast_exp2((sm.cs[t] - cs_s) * kLog2e) * dl_s : 0.0f;
-        split_bf16(m, sm.M[0][t][s], sm.M[1][t][s]);
-      }
-    }
-    f32x16 yoff = {};
     {
-      const int p = 32 * tj + (lane & 31), nh = 8 * (lane >> 5);
+      const int t = 2 * xtq;
+      const float w0 = fast_exp2((cs_end - sm.cs[t]) * kLog2e) * sm.dl[t];
+      const float w1 = fast_exp2((cs_end - sm.cs[t + 1]) * kLog2e) * sm.dl[t + 1];
 #pragma unroll
-      for (int k = 0; k < N / 16; ++k) {
-        yoff = mfma(ca[k], ld_bf16x8(&sm.hb[0][p][16 * k + nh]), yoff);
-        yoff = mfma(ca[k], ld_bf16x8(&sm.hb[1][p][16 * k + nh]), yoff);
+      for (int e = 0; e < XC; ++e) {
+        uint32_t hi, lo;
+        split2(w0 * bits_f32(elem(xr[0], e)), w1 * bits_f32(elem(xr[1], e)), hi, lo);
+        *reinterpret_cast<uint32_t*>(&sm.xw[0][XC * xpg + e][t]) = hi;
+        *reinterpret_cast<uint32_t*>(&sm.xw[1][XC * xpg + e][t]) = lo;
       }
     }
-    __syncthreads();  // M, xt, xw, bt complete; every read of hb done
-    // ---- 4a. y tile (ti, tj) = M X + exp(cs_t) C H^T + D x
-    {
-      f32x16 yacc = {};
-      const int t = 32 * ti + (lane & 31), p = 32 * tj + (lane & 31), kh = 8 * (lane >> 5);
+    load_x(t0 + kQ);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (k < 2 * (ti + 1)) {  // M[t][s] is zero for s past the tile row's end
-          const bf16x8 xk = ld_bf16x8(&sm.xt[p][16 * k + kh]);
-          yacc = mfma(ld_bf16x8(&sm.M[0][t][16 * k + kh]), xk, yacc);
-          yacc = mfma(ld_bf16x8(&sm.M[1][t][16 * k + kh]), xk, yacc);
+    for (int tk = wi; tk < 12; tk += NW) {
+      // the 12 16x16 tiles of M that y reads: tk < 10 enumerates (t tile, s tile)
+      // on or below the diagonal row by row; 10 and 11 are the two above it that
+      // a 32-token k step of y also covers, (0, 1) and (2, 3), all zero
+      int ti, si;
+      if (tk < 10) {
+        ti = (tk >= 1) + (tk >= 3) + (tk >= 6);
+        si = tk - ti * (ti + 1) / 2;
+      } else {
+        ti = tk == 10 ? 0 : 2;
+        si = ti + 1;
+      }
+      const int t = 16 * ti + lr, s0 = 16 * si + 4 * lg;
+      uint2 hw = make_uint2(0, 0), lw = make_uint2(0, 0);
+      if (tk < 10) {
+        f32x4 acc = {};
+#pragma unroll
+        for (int m = 0; m < N / 32; ++m)
+          acc = mfma(lds8(&sm.bn[16 * si + lr][32 * m + 8 * lg]), lds8(&sm.cn[t][32 * m + 8 * lg]), acc);
+        const float cst = sm.cs[t];
+        const float4 css = *reinterpret_cast<const float4*>(&sm.cs[s0]);
+        const float4 dls = *reinterpret_cast<const float4*>(&sm.dl[s0]);
+        const float csv[4] = {css.x, css.y, css.z, css.w}, dlv[4] = {dls.x, dls.y, dls.z, dls.w};
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s = s0 + r;
+          v[r] = acc[r] * fast_exp2((cst - csv[r]) * kLog2e) * dlv[r];
+          v[r] = s <= t ? v[r] : 0.0f;
+          if constexpr (MODE == 0) v[r] += s == t ? Dh : 0.0f;
         }
+        split2(v[0], v[1], hw.x, lw.x);
+        split2(v[2], v[3], hw.y, lw.y);
       }
-      const int pc = 32 * tj + col;
+      *reinterpret_cast<uint2*>(&sm.M[0][t][s0]) = hw;
+      *reinterpret_cast<uint2*>(&sm.M[1][t][s0]) = lw;
+    }
+    f32x4 yo[4] = {};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tr = 32 * ti + acc_row(r, lane);
-        const float xv_tp = __uint_as_float(static_cast<uint32_t>(sm.xt[pc][tr]) << 16);
-        const float v = yacc[r] + fast_exp2(sm.cs[tr] * kLog2e) * yoff[r] + Dh * xv_tp;
-        if (t0 + tr < L) yb[(t0 + tr) * xrow + pc] = to_bf16_bits(v);
+    for (int mm = 0; mm < NMK; ++mm) {
+      const int m = k * NMK + mm;
+      uint32_t hv[4], lv[4];
+      split2(Hs[2 * mm][0], Hs[2 * mm][1], hv[0], lv[0]);
+      split2(Hs[2 * mm][2], Hs[2 * mm][3], hv[1], lv[1]);
+      split2(Hs[2 * mm + 1][0], Hs[2 * mm + 1][1], hv[2], lv[2]);
+      split2(Hs[2 * mm + 1][2], Hs[2 * mm + 1][3], hv[3], lv[3]);
+      const bf16x8 hh = __builtin_bit_cast(bf16x8, make_uint4(hv[0], hv[1], hv[2], hv[3]));
+      const bf16x8 hl = __builtin_bit_cast(bf16x8, make_uint4(lv[0], lv[1], lv[2], lv[3]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 cb = lds8(&sm.cn[16 * i + lr][32 * m + 8 * lg]);
+        yo[i] = mfma(hh, cb, yo[i]);
+        yo[i] = mfma(hl, cb, yo[i]);
       }
     }
-    // ---- 4b. state update: H' = exp(cs_end) H + (X o w)^T B, tiles (rows n, cols p)
+    if constexpr (NK == 2) {  // hand the other wave of the slice its two tiles
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const f32x4 v = k ? yo[u] : yo[2 + u];
+        sm.xch[w + 4 * (1 - k)][u][lane] = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+    __syncthreads();  // M, x o w and the exchanged halves complete
+
+    // ---- C. y^T for the wave's tiles; the state update
+    const auto ybuf = rows_buf(yb + t0 * xrow, t0, xrow * 2, kP * 2);
+    // y tile i (16 tokens) of the slice; KS 32-token k steps cover s <= t
+    auto y_tile = [&](const int i, const f32x4& yt, auto ks, u32x2& out) {
+      constexpr int KS = decltype(ks)::value;
+      f32x4 acc = {};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const bf16x8 xa = lds8(&sm.xt[16 * w + lr][32 * kk + 8 * lg]);
+        acc = mfma(xa, lds8(&sm.M[0][16 * i + lr][32 * kk + 8 * lg]), acc);
+        acc = mfma(xa, lds8(&sm.M[1][16 * i + lr][32 * kk + 8 * lg]), acc);
+      }
+      const int t = 16 * i + lr;
+      const float e = fast_exp2(sm.cs[t] * kLog2e);
+      out = (u32x2){pack_bf16(__builtin_fmaf(e, yt[0], acc[0]), __builtin_fmaf(e, yt[1], acc[1])),
+                    pack_bf16(__builtin_fmaf(e, yt[2], acc[2]), __builtin_fmaf(e, yt[3], acc[3]))};
+    };
+    // the stores stay outside the branches so the wait on the prefetch at the top
+    // of the loop counts them exactly
+    auto y_store = [&](const int i, const u32x2& out) {
+      __builtin_amdgcn_raw_buffer_store_b64(out, ybuf, static_cast<uint32_t>((16 * i + lr) * xrow * 2 + (16 * w + 4 * lg) * 2),
+                                            0, 0);
+    };
+    using One = std::integral_constant<int, 1>;
+    using Two = std::integral_constant<int, 2>;
+    if constexpr (NK == 2) {  // tiles 2k and 2k + 1
+      f32x4 yt[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float4 o = sm.xch[wi][u][lane];
+        yt[u] = k ? yo[2 + u] : yo[u];
+        yt[u][0] += o.x, yt[u][1] += o.y, yt[u][2] += o.z, yt[u][3] += o.w;
+      }
+      u32x2 out[2];
+      if (k == 0) {
+        y_tile(0, yt[0], One{}, out[0]);
+        y_tile(1, yt[1], One{}, out[1]);
+      } else {
+        y_tile(2, yt[0], Two{}, out[0]);
+        y_tile(3, yt[1], Two{}, out[1]);
+      }
+      y_store(2 * k, out[0]);
+      y_store(2 * k + 1, out[1]);
+    } else {
+      u32x2 out[4];
+      y_tile(0, yo[0], One{}, out[0]);
+      y_tile(1, yo[1], One{}, out[1]);
+      y_tile(2, yo[2], Two{}, out[2]);
+      y_tile(3, yo[3], Two{}, out[3]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y_store(i, out[i]);
+    }
     {
       const float dec = fast_exp2(cs_end * kLog2e);
-      const int kh = 8 * (lane >> 5);
+      bf16x8 xh[2], xl[2];
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        const int q = w + 4 * i;
-        const int n = 32 * (q >> 1) + (lane & 31), p = 32 * (q & 1) + (lane & 31);
-        f32x16 sacc = {};
+      for (int kk = 0; kk < 2; ++kk) {
+        xh[kk] = lds8(&sm.xw[0][16 * w + lr][32 * kk + 8 * lg]);
+        xl[kk] = lds8(&sm.xw[1][16 * w + lr][32 * kk + 8 * lg]);
+      }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const bf16x8 bk = ld_bf16x8(&sm.bt[n][16 * k + kh]);
-          sacc = mfma(bk, ld_bf16x8(&sm.xw[0][p][16 * k + kh]), sacc);
-          sacc = mfma(bk, ld_bf16x8(&sm.xw[1][p][16 * k + kh]), sacc);
+      for (int j = 0; j < NJK; ++j) {
+        f32x4 sacc = {};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 bb = lds8(&sm.bt[16 * (k * NJK + j) + lr][32 * kk + 8 * lg]);
+          sacc = mfma(bb, xh[kk], sacc);
+          sacc = mfma(bb, xl[kk], sacc);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Hs[i][r] = __builtin_fmaf(dec, Hs[i][r], sacc[r]);
+        for (int r = 0; r < 4; ++r) Hs[j][r] = __builtin_fmaf(dec, Hs[j][r], sacc[r]);
       }
     }
-    write_hb();
-    __syncthreads();  // LDS free for the next chunk; hb holds the new state
+    __syncthreads();  // LDS free for the next chunk
   }
-  if (hT) {
+  if (a.hT) {
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int q = w + 4 * i, p = 32 * (q & 1) + col;
-#pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        const int n = 32 * (q >> 1) + acc_row(r, lane);
-        *reinterpret_cast<float4*>(hT + ((b * H + h) * kP + p) * N + n) =
-            make_float4(Hs[i][r], Hs[i][r + 1], Hs[i][r + 2], Hs[i][r + 3]);
-      }
-    }
+    for (int j = 0; j < NJK; ++j)
+      *reinterpret_cast<float4*>(a.hT + sbase + 16 * j) = make_float4(Hs[j][0], Hs[j][1], Hs[j][2], Hs[j][3]);
   }
 }
 
-template <int N>
+template <int N, int MODE>
 hipError_t launch_ssd_n(const SsdProblem& p, hipStream_t stream) {
-  hipLaunchKernelGGL((ssd_fwd_kernel<N>), dim3(static_cast<unsigned>(p.nheads), static_cast<unsigned>(p.batch)),
-                     dim3(256), 0, stream, static_cast<const uint16_t*>(p.x), static_cast<const uint16_t*>(p.dt), p.A,
-                     static_cast<const uint16_t*>(p.B), static_cast<const uint16_t*>(p.C), p.D, p.dt_bias, p.h0,
-                     p.hT, static_cast<uint16_t*>(p.y), p.seqlen, static_cast<int>(p.nheads),
-                     static_cast<int>(p.ngroups));
+  constexpr int NW = N <= 128 ? 8 : 4;
+  KArgs k;
+  k.x = static_cast<const uint16_t*>(p.x);
+  k.dt = static_cast<const uint16_t*>(p.dt);
+  k.A = p.A;
+  k.B = static_cast<const uint16_t*>(p.B);
+  k.C = static_cast<const uint16_t*>(p.C);
+  k.D = p.D;
+  k.dt_bias = p.dt_bias;
+  k.log_f = p.log_f;
+  k.in_gate = p.in_gate;
+  k.h0 = p.h0;
+  k.hT = p.hT;
+  k.y = static_cast<uint16_t*>(p.y);
+  k.L = p.seqlen;
+  k.H = static_cast<int>(p.nheads);
+  k.G = static_cast<int>(p.ngroups);
+  hipLaunchKernelGGL((ssd_fwd_kernel<N, MODE, NW>), dim3(static_cast<unsigned>(p.nheads), static_cast<unsigned>(p.batch)),
+                     dim3(64 * NW), 0, stream, k);
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_ssd_m(const SsdProblem& p, hipStream_t stream) {
+  switch (p.dstate) {
+    case 64: return launch_ssd_n<64, MODE>(p, stream);
+    case 128: return launch_ssd_n<128, MODE>(p, stream);
+    default: return launch_ssd_n<256, MODE>(p, stream);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_ssd(const SsdProblem& p, hipStream_t stream) {
-  switch (p.dstate) {
-    case 64: return launch_ssd_n<64>(p, stream);
-    case 128: return launch_ssd_n<128>(p, stream);
-    default: return launch_ssd_n<256>(p, stream);
+  switch (p.mode) {
+    case 1: return launch_ssd_m<1>(p, stream);
+    case 2: return launch_ssd_m<2>(p, stream);
+    default: return launch_ssd_m<0>(p, stream);
   }
 }
 
