@@ -54,6 +54,16 @@ class _SsdArgs(ctypes.Structure):
     ]
 
 
+class _GlaArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dstate", ctypes.c_int64),
+        ("feature_map", ctypes.c_int64),
+        ("q", _dp), ("k", _dp), ("v", _dp), ("log_f", _dp), ("in_gate", _dp), ("s0", _dp),
+        ("y", _dp), ("sT", _dp),
+    ]
+
+
 def lib_path(mutant: int = 0, out_dir: str | None = None) -> str:
     d = out_dir or _BUILD
     name = "liboracle.so" if mutant == 0 else f"liboracle_mutant{mutant}.so"
@@ -87,6 +97,8 @@ class Oracle:
         i64 = ctypes.c_int64
         self._lib.oracle_ssd_f64.argtypes = [ctypes.POINTER(_SsdArgs)]
         self._lib.oracle_ssd_f64.restype = ctypes.c_int
+        self._lib.oracle_gla_f64.argtypes = [ctypes.POINTER(_GlaArgs)]
+        self._lib.oracle_gla_f64.restype = ctypes.c_int
         self._lib.oracle_conv1d_silu_f64.argtypes = [i64, i64, i64, i64, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
         self._lib.oracle_conv1d_silu_f64.restype = ctypes.c_int
         self._lib.oracle_softplus_vec.argtypes = [_dp, _dp, ctypes.c_int64]
@@ -220,6 +232,27 @@ class Oracle:
             raise RuntimeError("oracle_ssd_f64 failed")
         return y, sT
 
+    def gla(self, q, k, v, log_f=None, in_gate=None, s0=None, feature_map=False):
+        """Gated linear attention / mLSTM recurrence: q and k (B, L, G, N), v
+        (B, L, H, P), log_f and in_gate (B, L, H), s0 (B, H, P, N); feature_map
+        applies elu + 1 to q and k.  Returns (y, sT) as float64 numpy arrays."""
+        q, k, v = (self._f64(t) for t in (q, k, v))
+        log_f, in_gate, s0 = (self._f64(t) for t in (log_f, in_gate, s0))
+        Bn, L, H, P = v.shape
+        G, N = k.shape[2], k.shape[3]
+        assert q.shape == k.shape == (Bn, L, G, N)
+        assert log_f is None or log_f.shape == (Bn, L, H)
+        assert in_gate is None or in_gate.shape == (Bn, L, H)
+        assert s0 is None or s0.shape == (Bn, H, P, N)
+        y = np.empty_like(v)
+        sT = np.empty((Bn, H, P, N), dtype=np.float64)
+        p = self._ptr
+        a = _GlaArgs(Bn, L, H, P, G, N, int(bool(feature_map)), p(q), p(k), p(v), p(log_f), p(in_gate), p(s0),
+                     p(y), p(sT))
+        if self._lib.oracle_gla_f64(ctypes.byref(a)) != 0:
+            raise RuntimeError("oracle_gla_f64 failed")
+        return y, sT
+
     def softplus(self, v):
         v = self._f64(v)
         out = np.empty_like(v)
@@ -261,6 +294,10 @@ def conv1d_silu(*args, **kw):
 
 def ssd(*args, **kw):
     return get().ssd(*args, **kw)
+
+
+def gla(*args, **kw):
+    return get().gla(*args, **kw)
 
 
 def softplus(v):

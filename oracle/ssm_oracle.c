@@ -25,7 +25,8 @@
  *
  * It also holds the backward pass (gradients of a scalar loss), see
  * oracle_scan_bwd_f64, the conv1d + SiLU prologue, oracle_conv1d_silu_f64, and
- * the Mamba-2 state-space dual layer in recurrent form, oracle_ssd_f64.
+ * the Mamba-2 state-space dual layer in recurrent form, oracle_ssd_f64, and
+ * the gated-linear-attention / mLSTM matrix-state recurrence, oracle_gla_f64.
  *
  * Build-time mutations (ORACLE_MUTANT=k, k>0) exist only so the test suite
  * can show that its closed-form pins catch plausible mistakes; the default
@@ -468,6 +469,84 @@ int oracle_ssd_f64(const oracle_ssd_args *a) {
 #endif
           }
           a->y[((b * L + t) * H + h) * P + p] = acc + (a->Dskip ? a->Dskip[h] : 0.0) * xv;
+        }
+      }
+      if (a->sT)
+        for (int64_t i = 0; i < P * N; ++i) a->sT[(b * H + h) * P * N + i] = S[i];
+    }
+  free(S);
+  return 0;
+}
+
+/* Matrix-state recurrences related to the selective scan, in recurrent form:
+ * linear attention (page "HedgeMamba" review, stage 2: the recurrence
+ * s_t = s_{t-1} + phi(k_t)^T v_t whose readout phi(q_t) s_t is the causal form
+ * of phi(Q) (phi(K)^T V), with phi = elu + 1 as the example feature map) and
+ * its gated form, the mLSTM update of the xLSTM-distillation review (the
+ * previous matrix state scaled by a forget coefficient plus the input-gated
+ * outer product of value and key).  Per batch row b and head h, group
+ * g = h / (H / G):
+ *   f_t = exp(log_f[b,t,h])   (1 when log_f is absent)
+ *   i_t = in_gate[b,t,h]      (1 when absent)
+ *   S_t[p,n] = f_t S_{t-1}[p,n] + i_t v[b,t,h,p] phi(k[b,t,g,n])
+ *   y[b,t,h,p] = sum_n phi(q[b,t,g,n]) S_t[p,n]
+ * phi(u) = u (feature_map 0) or elu(u) + 1 = (u > 0 ? u + 1 : exp(u))
+ * (feature_map 1).  v, y are (B, L, H, P); q, k are (B, L, G, N); log_f and
+ * in_gate are (B, L, H); the state S0 / ST is (B, H, P, N). */
+typedef struct {
+  int64_t batch, seqlen, nheads, headdim, ngroups, dstate;
+  int64_t feature_map;
+  const double *q, *k, *v;
+  const double *log_f;   /* NULL: no decay (plain linear attention) */
+  const double *in_gate; /* NULL: input gate 1 */
+  const double *s0;      /* NULL: zero state */
+  double *y;             /* (B, L, H, P) */
+  double *sT;            /* NULL or (B, H, P, N) */
+} oracle_gla_args;
+
+static double feature(double u, int64_t fm) { return fm ? (u > 0.0 ? u + 1.0 : exp(u)) : u; }
+
+int oracle_gla_f64(const oracle_gla_args *a) {
+  if (!a || a->batch < 0 || a->seqlen < 0 || a->nheads < 0 || a->headdim <= 0 || a->ngroups <= 0 ||
+      a->dstate <= 0 || a->nheads % a->ngroups != 0 || a->feature_map < 0 || a->feature_map > 1)
+    return -1;
+  const int64_t Bn = a->batch, L = a->seqlen, H = a->nheads, P = a->headdim, G = a->ngroups, N = a->dstate;
+  double *S = (double *)malloc(sizeof(double) * (size_t)(P * N + 2 * N));
+  if (!S) return -1;
+  double *kf = S + P * N, *qf = kf + N;
+  for (int64_t b = 0; b < Bn; ++b)
+    for (int64_t h = 0; h < H; ++h) {
+      const int64_t g = h / (H / G);
+      for (int64_t i = 0; i < P * N; ++i) S[i] = a->s0 ? a->s0[(b * H + h) * P * N + i] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t bth = (b * L + t) * H + h;
+        const double f = a->log_f ? exp(a->log_f[bth]) : 1.0;
+        const double ig = a->in_gate ? a->in_gate[bth] : 1.0;
+        for (int64_t n = 0; n < N; ++n) {
+          kf[n] = feature(a->k[((b * L + t) * G + g) * N + n], a->feature_map);
+#if ORACLE_MUTANT == 24
+          qf[n] = a->q[((b * L + t) * G + g) * N + n]; /* feature map skipped on q */
+#else
+          qf[n] = feature(a->q[((b * L + t) * G + g) * N + n], a->feature_map);
+#endif
+        }
+        for (int64_t p = 0; p < P; ++p) {
+          const double vv = a->v[bth * P + p];
+          double acc = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+#if ORACLE_MUTANT == 23
+            acc += qf[n] * S[p * N + n]; /* read out before the update */
+#endif
+#if ORACLE_MUTANT == 25
+            S[p * N + n] = f * ig * S[p * N + n] + vv * kf[n]; /* input gate on the carried state */
+#else
+            S[p * N + n] = f * S[p * N + n] + ig * vv * kf[n];
+#endif
+#if ORACLE_MUTANT != 23
+            acc += qf[n] * S[p * N + n];
+#endif
+          }
+          a->y[bth * P + p] = acc;
         }
       }
       if (a->sT)
