@@ -449,6 +449,71 @@ def bench_ssd(args, ssm, torch):
     return out
 
 
+def bench_gla(args, ssm, torch):
+    """One step = one ssm_gla_fwd over a gated-linear-attention / mLSTM layer
+    (default B4 L8192 H64 P64 G1 N128 with forget and input gates, bf16, hT
+    returned)."""
+    import workloads
+    w = workloads.GLA_BY_NAME[args.gla]
+    dev = torch.device("cuda:0")
+    log(f"workload {w.describe()}")
+    inp = workloads.make_gla_inputs(w)
+    d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+    vs = [d["v"], d["v"].clone()]  # alternate so the previous step's v is not in the LLC
+    ys = [torch.empty_like(vs[0]) for _ in vs]
+    hT = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        ssm.gla_fwd(d["q"], d["k"], vs[i % 2], d["log_f"], d["in_gate"], None, feature_map=w.feature_map,
+                    out=ys[i % 2], final_state_out=hT)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    steps = max(args.steps, 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    toks = w.batch * w.seqlen * w.nheads
+    alg = (2 * toks * w.headdim * 2 + 2 * w.batch * w.seqlen * w.ngroups * w.dstate * 2
+           + (2 * toks * 4 if w.gated else 0) + w.batch * w.nheads * w.headdim * w.dstate * 4)  # v, y, q, k, gates, hT
+    Q, N, P = 64, w.dstate, w.headdim
+    flops = toks * 2 * (Q * N + Q * P + 2 * N * P)  # Q K^T, M V, Q S^T, the state update: per token and head
+    ms = elapsed * 1e3 / steps
+    roof = _roofline(alg, kern_s, "ssd_fwd_kernel")
+    roof["mfma_tflops"] = round(flops / kern_s / 1e12, 2)
+    roof["mfma_frac_bf16_dense"] = round(flops / kern_s / 2.5e15, 4)
+    out = {
+        "metric": "gated linear attention GElem/s (B*L*H*P*N) + % HBM roofline",
+        "value": round(w.elems / (ms * 1e-3) / 1e9, 2), "unit": "GElem/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "ngroups": w.ngroups, "dstate": w.dstate, "gated": w.gated,
+                   "feature_map": "elu+1" if w.feature_map else None, "chunk": Q},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t = time.perf_counter()
+        one = lambda k: None if inp[k] is None else inp[k][:1]
+        oracle.gla(inp["q"][:1], inp["k"][:1], inp["v"][:1], log_f=one("log_f"), in_gate=one("in_gate"),
+                   feature_map=w.feature_map)
+        sec = time.perf_counter() - t
+        el = w.seqlen * w.nheads * w.headdim * w.dstate
+        out["cpu_baseline"] = {"value": round(el / sec / 1e9, 5), "unit": "GElem/s", "cores": 1, "kind": "oracle",
+                               "sample": f"batch row 0, all {w.nheads} heads and {w.seqlen} tokens ({el} state "
+                                         f"updates), fp64 recurrence, single thread; {sec:.2f} s including input widening"}
+    return out
+
+
 def main():
     import workloads
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -464,6 +529,8 @@ def main():
     ap.add_argument("--prologue", action="store_true", help="time the conv1d + SiLU prologue on x instead")
     ap.add_argument("--ssd", nargs="?", const="mamba2_B4_L8192_H64_P64_N128", default=None, metavar="WORKLOAD",
                     help="time the Mamba-2 SSD layer instead")
+    ap.add_argument("--gla", nargs="?", const="mlstm_B4_L8192_H64_P64_N128", default=None, metavar="WORKLOAD",
+                    help="time the gated-linear-attention / mLSTM layer instead")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the scan, copy a MIB-MiB buffer `steps` times (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -493,6 +560,9 @@ def main():
 
     if args.ssd:
         print(json.dumps(bench_ssd(args, ssm, torch)), flush=True)
+        return
+    if args.gla:
+        print(json.dumps(bench_gla(args, ssm, torch)), flush=True)
         return
     w = workloads.BY_NAME[args.workload]
     if args.prologue:

@@ -245,6 +245,46 @@ typedef struct ssm_ssd_args {
  * other (hT may not alias h0).  With L == 0, hT receives h0 (or zeros). */
 int ssm_ssd_fwd(const ssm_ssd_args *args, void *stream);
 
+/* ---- Gated linear attention / mLSTM matrix-state recurrence ----------------
+ * Linear attention as a recurrence (HedgeMamba review, stage 2:
+ * s_t = s_{t-1} + phi(k_t)^T v_t, read out by phi(q_t), phi = elu + 1 as the
+ * example feature map) and its gated form, the mLSTM update of the xLSTM
+ * review (the matrix state scaled by a forget coefficient plus the
+ * input-gated outer product of value and key).  Per batch row b, head h and
+ * group g = h / (H / G):
+ *   S_t[p,n] = exp(log_f[b,t,h]) S_{t-1}[p,n] + in_gate[b,t,h] v[b,t,h,p] phi(k[b,t,g,n])
+ *   y[b,t,h,p] = sum_n phi(q[b,t,g,n]) S_t[p,n]
+ * with log_f = 0 when NULL (no decay: plain linear attention), in_gate = 1
+ * when NULL, and phi(u) = u, or elu(u) + 1 with feature_map = 1.  The same
+ * chunked matrix form as ssm_ssd_fwd evaluates it (the SSD layer is the case
+ * log_f = delta A[h], in_gate = delta, plus D).  log_f is expected <= 0 (a
+ * forget gate in (0, 1]); larger values can overflow fp32.
+ * Layouts: q, k (B, L, G, N); v, y (B, L, H, P) in bf16; log_f, in_gate
+ * (B, L, H) and the state S0 / ST (B, H, P, N) fp32.  feature_map = 1 rounds
+ * phi(q) and phi(k) to bf16 before the products.
+ * Limits of this version: dtype SSM_DTYPE_BF16, headdim P = 64,
+ * dstate N in {64, 128, 256} (SSM_ERR_VARIANT otherwise). */
+typedef struct ssm_gla_args {
+  int64_t batch, seqlen;      /* B <= 65535, L >= 0                                  */
+  int64_t nheads, headdim;    /* H >= 1, P = 64                                       */
+  int64_t ngroups, dstate;    /* G divides H; N in {64, 128, 256}                     */
+  int32_t dtype;              /* SSM_DTYPE_BF16                                       */
+  int32_t feature_map;        /* 0: phi(u) = u; 1: phi(u) = elu(u) + 1                 */
+  const void *q;              /* (B, L, G, N) queries                        required */
+  const void *k;              /* (B, L, G, N) keys                           required */
+  const void *v;              /* (B, L, H, P) values                         required */
+  const float *log_f;         /* (B, L, H) log forget gate or NULL (0)                 */
+  const float *in_gate;       /* (B, L, H) input gate or NULL (1)                      */
+  const float *h0;            /* (B, H, P, N) initial state or NULL (zeros)            */
+  float *hT;                  /* (B, H, P, N) final state out or NULL                  */
+  void *y;                    /* (B, L, H, P) out                            required */
+} ssm_gla_args;
+
+/* Errors as for ssm_ssd_fwd (SSM_ERR_VARIANT also for feature_map outside
+ * {0, 1}); y and hT must not overlap any input or each other.  With L == 0,
+ * hT receives h0 (or zeros). */
+int ssm_gla_fwd(const ssm_gla_args *args, void *stream);
+
 /* Static, human-readable text for a status code. */
 const char *ssm_scan_strerror(int code);
 

@@ -33,7 +33,7 @@ FLAG_GENERIC_A = 1
 # Exported symbols the header declares (checked by the tests).
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_scan_bwd",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd_plan", "ssm_conv1d_silu_fwd", "ssm_ssd_fwd",
-           "ssm_scan_strerror", "ssm_scan_abi_version")
+           "ssm_gla_fwd", "ssm_scan_strerror", "ssm_scan_abi_version")
 
 
 class ScanArgs(ctypes.Structure):
@@ -89,6 +89,18 @@ class SsdArgs(ctypes.Structure):
     ]
 
 
+class GlaArgs(ctypes.Structure):
+    """Mirror of ssm_gla_args in include/ssm_scan.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dstate", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("feature_map", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("log_f", ctypes.c_void_p), ("in_gate", ctypes.c_void_p),
+        ("h0", ctypes.c_void_p), ("hT", ctypes.c_void_p), ("y", ctypes.c_void_p),
+    ]
+
+
 # Gradient outputs of the backward: name of the input they belong to -> struct field.
 GRAD_FIELDS = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
                "delta_bias": "ddelta_bias", "h0": "dh0"}
@@ -120,6 +132,8 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_bwd_plan.restype = ctypes.c_int64
         L.ssm_ssd_fwd.argtypes = [ctypes.POINTER(SsdArgs), ctypes.c_void_p]
         L.ssm_ssd_fwd.restype = ctypes.c_int
+        L.ssm_gla_fwd.argtypes = [ctypes.POINTER(GlaArgs), ctypes.c_void_p]
+        L.ssm_gla_fwd.restype = ctypes.c_int
         L.ssm_conv1d_silu_fwd.argtypes = [ctypes.POINTER(ConvArgs), ctypes.c_void_p]
         L.ssm_conv1d_silu_fwd.restype = ctypes.c_int
         L.ssm_scan_strerror.argtypes = [ctypes.c_int]
@@ -418,5 +432,52 @@ def ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, h0=None, *, return_final_state
     return y
 
 
-__all__ = ["scan_fwd", "scan_bwd", "conv1d_silu", "ssd_fwd", "make_ssd_args", "SsdArgs", "make_conv_args", "ConvArgs", "make_args", "make_bwd_args", "plan", "bwd_plan", "workspace_bytes",
+def make_gla_args(q, k, v, log_f=None, in_gate=None, h0=None, hT=None, y=None, feature_map=False) -> GlaArgs:
+    """Check shapes/dtypes/devices and fill an ssm_gla_args."""
+    if v.dim() != 4 or k.dim() != 4:
+        raise ValueError("v must be (B, L, H, P) and q, k (B, L, G, N)")
+    bsz, L, H, P = v.shape
+    G, N = k.shape[2], k.shape[3]
+    bf, f32, dev = torch.bfloat16, torch.float32, v.device
+    _check("q", q, (bsz, L, G, N), bf, dev)
+    _check("k", k, (bsz, L, G, N), bf, dev)
+    _check("v", v, (bsz, L, H, P), bf, dev)
+    _check("log_f", log_f, (bsz, L, H), f32, dev)
+    _check("in_gate", in_gate, (bsz, L, H), f32, dev)
+    _check("h0", h0, (bsz, H, P, N), f32, dev)
+    _check("hT", hT, (bsz, H, P, N), f32, dev)
+    _check("y", y, (bsz, L, H, P), bf, dev)
+    a = GlaArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.ngroups, a.dstate = bsz, L, H, P, G, N
+    a.dtype, a.feature_map = DTYPE_BF16, int(bool(feature_map))
+    a.q, a.k, a.v, a.log_f, a.in_gate = _ptr(q), _ptr(k), _ptr(v), _ptr(log_f), _ptr(in_gate)
+    a.h0, a.hT, a.y = _ptr(h0), _ptr(hT), _ptr(y)
+    return a
+
+
+def gla_fwd(q, k, v, log_f=None, in_gate=None, h0=None, *, feature_map=False, return_final_state=False, out=None,
+            final_state_out=None):
+    """Gated linear attention / mLSTM matrix-state recurrence on the GPU:
+    S_t = exp(log_f) S_{t-1} + in_gate v_t phi(k_t)^T, y_t = S_t phi(q_t), phi the
+    identity or elu + 1 (feature_map=True).  Returns y, or (y, hT) with
+    return_final_state=True.  Launches on torch's current HIP stream and does
+    not synchronise."""
+    if not v.is_cuda:
+        raise ValueError("gla_fwd runs on the GPU only: move the tensors to a HIP device")
+    L_ = lib()
+    y = out if out is not None else torch.empty_like(v)
+    hT = final_state_out
+    if hT is None and return_final_state:
+        hT = torch.empty((v.shape[0], v.shape[2], v.shape[3], k.shape[3]), dtype=torch.float32, device=v.device)
+    args = make_gla_args(q, k, v, log_f, in_gate, h0, hT, y, feature_map)
+    stream = torch.cuda.current_stream(v.device).cuda_stream
+    rc = L_.ssm_gla_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise RuntimeError(f"ssm_gla_fwd: {strerror(rc)}")
+    if return_final_state or final_state_out is not None:
+        return y, hT
+    return y
+
+
+__all__ = ["scan_fwd", "scan_bwd", "conv1d_silu", "ssd_fwd", "gla_fwd", "make_gla_args", "GlaArgs", "make_ssd_args", "SsdArgs", "make_conv_args", "ConvArgs", "make_args", "make_bwd_args", "plan", "bwd_plan", "workspace_bytes",
            "bwd_workspace_bytes", "lib", "strerror", "ScanArgs", "ScanBwdArgs", "EXPORTS"]

@@ -290,6 +290,36 @@ int validate_ssd(const ssm_ssd_args* a) {
   return SSM_OK;
 }
 
+// ---- gated linear attention / mLSTM ------------------------------------------------------
+
+int validate_gla(const ssm_gla_args* a) {
+  if (!a) return SSM_ERR_NULL;
+  if (a->batch < 0 || a->seqlen < 0 || a->nheads < 1 || a->headdim < 1 || a->ngroups < 1 || a->dstate < 1)
+    return SSM_ERR_SHAPE;
+  if (a->dtype != SSM_DTYPE_BF16) return a->dtype == SSM_DTYPE_F32 ? SSM_ERR_VARIANT : SSM_ERR_DTYPE;
+  if (a->feature_map < 0 || a->feature_map > 1 || a->headdim != 64 || a->nheads % a->ngroups != 0)
+    return SSM_ERR_VARIANT;
+  if (a->dstate != 64 && a->dstate != 128 && a->dstate != 256) return SSM_ERR_VARIANT;
+  if (a->batch > 65535 || a->nheads > 65535) return SSM_ERR_SHAPE;
+  int64_t bl, blh, ve, qk, st, tmp;
+  if (!mul_ok(a->batch, a->seqlen, &bl) || !mul_ok(bl, a->nheads, &blh) || !mul_ok(blh, a->headdim, &ve) ||
+      !mul_ok(bl, a->ngroups * a->dstate, &qk) || !mul_ok(a->batch * a->nheads, a->headdim * a->dstate, &st) ||
+      !mul_ok(ve, 2, &tmp) || !mul_ok(st, 4, &tmp) || !mul_ok(qk, 2, &tmp) || !mul_ok(blh, 4, &tmp))
+    return SSM_ERR_SHAPE;
+  if (bl > 0 && (!a->q || !a->k || !a->v || !a->y)) return SSM_ERR_NULL;
+  const void* ptrs[] = {a->q, a->k, a->v, a->log_f, a->in_gate, a->h0, a->hT, a->y};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return SSM_ERR_ALIGN;
+  const void* ins[] = {a->q, a->k, a->v, a->log_f, a->in_gate, a->h0};
+  const int64_t insz[] = {qk * 2, qk * 2, ve * 2, blh * 4, blh * 4, st * 4};
+  for (int i = 0; i < 6; ++i) {
+    if (overlaps(a->y, ve * 2, ins[i], insz[i])) return SSM_ERR_ALIAS;
+    if (overlaps(a->hT, st * 4, ins[i], insz[i])) return SSM_ERR_ALIAS;
+  }
+  if (overlaps(a->hT, st * 4, a->y, ve * 2)) return SSM_ERR_ALIAS;
+  return SSM_OK;
+}
+
 // ---- conv1d + SiLU prologue ---------------------------------------------------------------
 
 int validate_conv(const ssm_conv_args* a) {
@@ -522,6 +552,34 @@ int ssm_ssd_fwd(const ssm_ssd_args* a, void* stream) {
   p.C = a->C;
   p.D = a->D;
   p.dt_bias = a->dt_bias;
+  p.h0 = a->h0;
+  p.hT = a->hT;
+  p.y = a->y;
+  const hipError_t e = ssm::launch_ssd(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
+}
+
+int ssm_gla_fwd(const ssm_gla_args* a, void* stream) {
+  const int rc = validate_gla(a);
+  if (rc != SSM_OK) return rc;
+  if (a->batch == 0) return SSM_OK;
+  ssm::SsdProblem p;
+  p.batch = a->batch;
+  p.seqlen = a->seqlen;
+  p.nheads = a->nheads;
+  p.headdim = a->headdim;
+  p.ngroups = a->ngroups;
+  p.dstate = a->dstate;
+  p.mode = 1 + a->feature_map;
+  p.x = a->v;  // values play the role of x, keys of B, queries of C
+  p.dt = nullptr;
+  p.A = nullptr;
+  p.B = a->k;
+  p.C = a->q;
+  p.D = nullptr;
+  p.dt_bias = nullptr;
+  p.log_f = a->log_f;
+  p.in_gate = a->in_gate;
   p.h0 = a->h0;
   p.hT = a->hT;
   p.y = a->y;

@@ -152,8 +152,15 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wi = wave_id();
   const int w = wi & 3, k = wi >> 2;  // channel slice, n part
   const int lr = lane & 15, lg = lane >> 4;
-  const int64_t b = blockIdx.y, L = a.L;
-  const int h = blockIdx.x;
+  // XCD-aware order: the hardware deals workgroups to the 8 XCDs round-robin, so
+  // every 8th workgroup takes the next head.  The heads of a batch row then run
+  // on one XCD and share its L2 for B, C and the cache lines of their per-token
+  // inputs (one line holds the values of many heads).
+  const int nwg = gridDim.x * gridDim.y;
+  int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  if (nwg % 8 == 0) lin = (lin % 8) * (nwg / 8) + lin / 8;
+  const int64_t b = lin / a.H, L = a.L;
+  const int h = lin % a.H;
   const int g = h / (a.H / a.G);
   const int64_t xrow = static_cast<int64_t>(a.H) * kP;  // elements between tokens in x / y
   const int64_t brow = static_cast<int64_t>(a.G) * N;   // elements between tokens in B / C

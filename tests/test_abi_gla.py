@@ -1,0 +1,64 @@
+"""The gated-linear-attention entry point's C ABI on the CPU: argument checks
+that fail on the host before any HIP call (fake, aligned, never dereferenced
+pointers)."""
+import ctypes
+
+import pytest
+
+import mamba_selective_scan_06_amd as ssm
+
+FAKE = 0x7F0000000000
+
+
+def _args(**kw):
+    a = ssm.GlaArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.ngroups, a.dstate = kw.pop("shape", (2, 64, 8, 64, 2, 128))
+    a.dtype = kw.pop("dtype", 1)
+    a.feature_map = kw.pop("feature_map", 0)
+    base = FAKE
+    for name in ("q", "k", "v", "log_f", "in_gate", "h0", "hT", "y"):
+        setattr(a, name, kw.pop(name, base))
+        base += 1 << 32
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _gla(a):
+    return ssm.lib().ssm_gla_fwd(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("mut,code", [
+    (dict(shape=(-1, 64, 8, 64, 2, 128)), -2),
+    (dict(shape=(2, 64, 0, 64, 1, 128)), -2),
+    (dict(shape=(70000, 64, 8, 64, 2, 128)), -2),
+    (dict(shape=(2**40, 2**20, 2**10, 64, 1, 128)), -2),
+    (dict(dtype=0), -9),              # fp32 not in this version
+    (dict(dtype=5), -4),
+    (dict(feature_map=2), -9),
+    (dict(feature_map=-1), -9),
+    (dict(shape=(2, 64, 8, 128, 2, 128)), -9),  # headdim 128
+    (dict(shape=(2, 64, 8, 64, 3, 128)), -9),   # groups must divide heads
+    (dict(shape=(2, 64, 8, 64, 2, 32)), -9),    # dstate 32
+    (dict(q=0), -1), (dict(k=0), -1), (dict(v=0), -1), (dict(y=0), -1),
+    (dict(v=FAKE + 2), -5), (dict(log_f=FAKE + 4), -5), (dict(hT=FAKE + 8), -5),
+])
+def test_invalid_arguments_rejected_on_host(mut, code):
+    assert _gla(_args(**mut)) == code
+
+
+def test_optional_inputs_may_be_null():
+    # with no tokens nothing is launched, so fake pointers and NULL gates pass the checks
+    assert _gla(_args(shape=(0, 64, 8, 64, 2, 128), log_f=0, in_gate=0, h0=0, hT=0)) == 0
+
+
+def test_aliasing_rejected():
+    for src, dst in (("v", "y"), ("q", "y"), ("log_f", "y"), ("h0", "hT"), ("in_gate", "hT"), ("y", "hT")):
+        a = _args()
+        setattr(a, dst, getattr(a, src))
+        assert _gla(a) == -6, (src, dst)
+
+
+def test_null_args_and_empty_batch():
+    assert ssm.lib().ssm_gla_fwd(None, None) == -1
+    assert _gla(_args(shape=(0, 64, 8, 64, 2, 128))) == 0

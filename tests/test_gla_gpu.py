@@ -1,0 +1,138 @@
+"""Gated linear attention / mLSTM recurrence on the GPU (ssm_gla_fwd through the
+C ABI, the chunked matrix form of the SSD kernel on bf16 MFMA) against the fp64
+oracle's recurrence.
+
+Tolerance: 2e-2 floored max relative error (bf16 inputs, workloads.rel_err), as
+for the SSD layer: the kernel rounds three MFMA operands to hi + lo bf16 pairs
+and y once to bf16.  With the elu + 1 feature map, phi(q) and phi(k) are also
+rounded to bf16 (a relative 2^-9 per element) before the products.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import mamba_selective_scan_06_amd as ssm
+import oracle
+import workloads
+from tests.gpu_helpers import DEV, check
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a HIP GPU"),
+]
+
+GW = workloads.GLA_WORKLOADS
+TENS = ("q", "k", "v", "log_f", "in_gate", "h0")
+
+
+def gpu_gla(inp, feature_map=False):
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    y, hT = ssm.gla_fwd(*(d[k] for k in TENS), feature_map=feature_map, return_final_state=True)
+    torch.cuda.synchronize()
+    return y.float().cpu().double().numpy(), hT.cpu().double().numpy()
+
+
+def oracle_gla(inp, feature_map=False):
+    return oracle.gla(inp["q"], inp["k"], inp["v"], log_f=inp["log_f"], in_gate=inp["in_gate"], s0=inp["h0"],
+                      feature_map=feature_map)
+
+
+CASES = [
+    dict(dstate=64, ngroups=2, seqlen=200),
+    dict(dstate=128, ngroups=1, seqlen=200),
+    dict(dstate=256, ngroups=4, seqlen=130),
+    dict(dstate=128, ngroups=2, seqlen=64),   # exactly one chunk
+    dict(dstate=128, ngroups=2, seqlen=65),   # one token into the second chunk
+    dict(dstate=64, ngroups=1, seqlen=1),
+    dict(dstate=256, ngroups=1, seqlen=63),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"N{c['dstate']}-G{c['ngroups']}-L{c['seqlen']}" for c in CASES])
+@pytest.mark.parametrize("mode", ["gated", "gated-h0", "linear", "linear-elu", "gated-elu-h0"])
+def test_gla_small_all_elements(case, mode):
+    inp = workloads.make_gla_inputs(GW[0], gated=mode.startswith("gated"), with_h0=mode.endswith("h0"), **case)
+    fm = "elu" in mode
+    y, hT = gpu_gla(inp, fm)
+    yr, hr = oracle_gla(inp, fm)
+    check("y", y, yr, torch.bfloat16)
+    check("hT", hT, hr, torch.bfloat16)
+
+
+def test_gla_one_gate_only():
+    """Forget gate without input gate, then input gate without forget gate."""
+    base = workloads.make_gla_inputs(GW[0], dstate=128, seqlen=150, with_h0=True)
+    for drop in ("in_gate", "log_f"):
+        inp = dict(base, **{drop: None})
+        y, hT = gpu_gla(inp)
+        yr, hr = oracle_gla(inp)
+        check(f"y without {drop}", y, yr, torch.bfloat16)
+        check(f"hT without {drop}", hT, hr, torch.bfloat16)
+
+
+def test_gla_chained_calls():
+    """A sequence fed as three calls through the carried state matches the
+    oracle's single call."""
+    inp = workloads.make_gla_inputs(GW[0], dstate=128, seqlen=300, with_h0=True)
+    yr, hr = oracle_gla(inp, True)
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    h = d["h0"]
+    ys = []
+    for a, b in [(0, 70), (70, 192), (192, 300)]:
+        sl = slice(a, b)
+        y, h = ssm.gla_fwd(*(d[k][:, sl].contiguous() for k in ("q", "k", "v", "log_f", "in_gate")), h,
+                           feature_map=True, return_final_state=True)
+        ys.append(y)
+    torch.cuda.synchronize()
+    check("y chained", torch.cat(ys, dim=1).float().cpu().double().numpy(), yr, torch.bfloat16)
+    check("hT chained", h.cpu().double().numpy(), hr, torch.bfloat16)
+
+
+def test_gla_matches_ssd_kernel_with_ssd_gates():
+    """log f = delta A and in_gate = delta reproduce ssm_ssd_fwd without D."""
+    sw = workloads.SSD_WORKLOADS[0]
+    inp = workloads.make_ssd_inputs(sw, dstate=128, seqlen=200, with_h0=True)
+    delta = torch.nn.functional.softplus(inp["dt"].float() + inp["dt_bias"][None, None, :])
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    y1, h1 = ssm.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], None, d["dt_bias"], d["h0"],
+                         return_final_state=True)
+    y2, h2 = ssm.gla_fwd(d["C"], d["B"], d["x"], (delta * inp["A"][None, None, :]).to(DEV), delta.to(DEV), d["h0"],
+                         return_final_state=True)
+    torch.cuda.synchronize()
+    # the two differ only in how delta is computed (device softplus vs torch's)
+    check("y gla vs ssd", y2.float().cpu().double().numpy(), y1.float().cpu().double().numpy(), torch.bfloat16)
+    check("hT gla vs ssd", h2.cpu().double().numpy(), h1.cpu().double().numpy(), torch.bfloat16)
+
+
+def test_gla_empty_sequence_passes_state():
+    inp = workloads.make_gla_inputs(GW[0], dstate=64, seqlen=0, with_h0=True)
+    y, hT = gpu_gla(inp)
+    assert y.shape[1] == 0
+    assert np.array_equal(hT, inp["h0"].double().numpy())
+
+
+def test_gla_deterministic():
+    inp = workloads.make_gla_inputs(GW[0], dstate=128, seqlen=200)
+    y1, h1 = gpu_gla(inp, True)
+    y2, h2 = gpu_gla(inp, True)
+    assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
+
+
+@pytest.mark.parametrize("wi", [1, 2], ids=["mlstm", "linattn-elu"])
+def test_gla_full_size_sampled_heads(wi):
+    """B4 L8192 H64 P64 N128 as the bench launches it; heads are independent, so
+    two heads of every batch row are checked against the oracle."""
+    w = GW[wi]
+    inp = workloads.make_gla_inputs(w)
+    y, hT = gpu_gla(inp, w.feature_map)
+    for hsel in (0, 41):
+        hi = torch.tensor([hsel])
+        sub = dict(inp, v=inp["v"].index_select(2, hi).contiguous())
+        for k in ("log_f", "in_gate"):
+            if inp[k] is not None:
+                sub[k] = inp[k].index_select(2, hi).contiguous()
+        yr, hr = oracle_gla(sub, w.feature_map)
+        check(f"y head {hsel}", y[:, :, hsel:hsel + 1], yr, torch.bfloat16)
+        check(f"hT head {hsel}", hT[:, hsel:hsel + 1], hr, torch.bfloat16)

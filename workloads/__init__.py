@@ -229,6 +229,72 @@ def make_ssd_inputs(w: SsdWorkload, *, batch=None, seqlen=None, nheads=None, ngr
     }
 
 
+@dataclasses.dataclass(frozen=True)
+class GlaWorkload:
+    """A gated-linear-attention / mLSTM layer: v (B, L, H, P), q/k (B, L, G, N),
+    per-token forget and input gates (gated) or none (plain linear attention),
+    optionally the elu + 1 feature map on q and k."""
+    index: int
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    dstate: int
+    gated: bool
+    feature_map: bool
+
+    @property
+    def elems(self) -> int:
+        """B*L*H*P*N state updates of the whole workload."""
+        return self.batch * self.seqlen * self.nheads * self.headdim * self.dstate
+
+    def describe(self) -> str:
+        kind = "gated (forget/input gates)" if self.gated else "ungated linear attention"
+        fm = ", elu+1 feature map" if self.feature_map else ""
+        return (f"{self.name}: B={self.batch} L={self.seqlen} H={self.nheads} P={self.headdim} "
+                f"G={self.ngroups} N={self.dstate} bf16, {kind}{fm}")
+
+
+# An mLSTM-style gated layer at the token count and head layout of the Mamba-2
+# workload (64 heads, values of 64, keys/queries of 128 shared by one group), the
+# same with plain linear attention and the elu + 1 feature map, and small cases.
+GLA_WORKLOADS = [
+    GlaWorkload(110, "gla_small_B2_L200_H4_P64_G2_N64", 2, 200, 4, 64, 2, 64, True, False),
+    GlaWorkload(111, "mlstm_B4_L8192_H64_P64_N128", 4, 8192, 64, 64, 1, 128, True, False),
+    GlaWorkload(112, "linattn_elu_B4_L8192_H64_P64_N128", 4, 8192, 64, 64, 1, 128, False, True),
+]
+GLA_BY_NAME = {w.name: w for w in GLA_WORKLOADS}
+
+
+def make_gla_inputs(w: GlaWorkload, *, batch=None, seqlen=None, nheads=None, ngroups=None, dstate=None,
+                    gated=None, with_h0=False, seed_extra=()):
+    """Seeded CPU tensors of one call: q, v bf16 ~ N(0, 1); k bf16 ~ N(0, 1/N) (keys
+    scaled by N^-1/2); gated: log_f = log sigmoid(u), u ~ N(3, 1) (forget gates
+    near 0.95) and in_gate = sigmoid(N(0, 1)), both fp32, else None; h0 fp32
+    ~ N(0, 0.1) or None."""
+    bsz = batch or w.batch
+    L = seqlen if seqlen is not None else w.seqlen
+    H = nheads or w.nheads
+    G = ngroups or w.ngroups
+    N = dstate or w.dstate
+    P = w.headdim
+    gated = w.gated if gated is None else gated
+    g = _streams(w.index, seed_extra)
+    f32 = np.float32
+    bf = torch.bfloat16
+    sig = lambda a: 1.0 / (1.0 + np.exp(-a))
+    return {
+        "q": _cast(g[0].standard_normal((bsz, L, G, N), dtype=f32), bf),
+        "k": _cast(g[1].standard_normal((bsz, L, G, N), dtype=f32) / math.sqrt(N), bf),
+        "v": _cast(g[2].standard_normal((bsz, L, H, P), dtype=f32), bf),
+        "log_f": torch.from_numpy(np.log(sig(g[3].normal(3.0, 1.0, (bsz, L, H)))).astype(f32)) if gated else None,
+        "in_gate": torch.from_numpy(sig(g[4].standard_normal((bsz, L, H))).astype(f32)) if gated else None,
+        "h0": torch.from_numpy((g[5].standard_normal((bsz, H, P, N)) * 0.1).astype(f32)) if with_h0 else None,
+    }
+
+
 def tolerance(dtype: torch.dtype) -> float:
     """Max floored relative error allowed: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs."""
     return 1e-4 if dtype == torch.float32 else 2e-2
