@@ -90,6 +90,8 @@ class Oracle:
         self._lib = ctypes.CDLL(path)
         self._lib.oracle_scan_f64.argtypes = [ctypes.POINTER(_Args), ctypes.c_int]
         self._lib.oracle_scan_f64.restype = ctypes.c_int
+        self._lib.oracle_scan_zoh_f64.argtypes = [ctypes.POINTER(_Args), ctypes.c_int]
+        self._lib.oracle_scan_zoh_f64.restype = ctypes.c_int
         self._lib.oracle_assoc_scan_f64.argtypes = [ctypes.POINTER(_Args)]
         self._lib.oracle_assoc_scan_f64.restype = ctypes.c_int
         self._lib.oracle_scan_bwd_f64.argtypes = [ctypes.POINTER(_Args), ctypes.POINTER(_Grads)]
@@ -138,14 +140,16 @@ class Oracle:
 
     # -- entry points --------------------------------------------------------
     def scan(self, x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
-             threads: int | None = None, timing: dict | None = None):
+             threads: int | None = None, timing: dict | None = None, zoh: bool = False):
         """Sequential fp64 scan.  Returns (y, hT) as float64 numpy arrays.
+        zoh=True uses the zero-order-hold input term instead of the Euler one.
         If `timing` is a dict, the wall time of the C call alone (inputs already
         widened to fp64) and the thread count are stored in it."""
         args, keep, y, hT = self._pack(x, delta, A, B, C, D, z, delta_bias, h0, True)
         nt = threads if threads is not None else (os.cpu_count() or 1)
         t0 = time.perf_counter()
-        rc = self._lib.oracle_scan_f64(ctypes.byref(args), int(nt))
+        fn = self._lib.oracle_scan_zoh_f64 if zoh else self._lib.oracle_scan_f64
+        rc = fn(ctypes.byref(args), int(nt))
         t1 = time.perf_counter()
         if rc != 0:
             raise RuntimeError("oracle_scan_f64 failed")

@@ -10,8 +10,9 @@
  * Transformer를 넘어서", youngju.dev):
  *   - discretisation, section 2.2: Abar = exp(delta * A) per (d, n); the
  *     input term is the Euler form delta * B * x that the section 3.3
- *     selective_scan listing materialises as deltaB * x (the ZOH form of the
- *     same section is not used; see the readings in the design notes);
+ *     selective_scan listing materialises as deltaB * x, or, in
+ *     oracle_scan_zoh_f64, the zero-order hold of section 2.2,
+ *     (exp(delta A) - 1) / A * B * x;
  *   - recurrence and readout, section 2.2: h_t = Abar h_{t-1} + Bbar x_t,
  *     y_t = C h_t, with the state updated before it is read (section 3.3);
  *   - selection, section 3.1: delta_t = softplus(raw delta + bias), B_t and
@@ -82,8 +83,24 @@ static double silu(double z) {
 /* SiLU of the conv prologue, separate from the gate's so that each has its own pins. */
 static double silu_plain(double v) { return v / (1.0 + exp(-v)); }
 
-/* One independent chain: batch row b, channel d, all N states, t = 0..L-1. */
-static void scan_channel(const oracle_args *a, int64_t b, int64_t d, double *h) {
+/* Input coefficient of state n under zero-order hold (page youngju.dev
+ * section 2.2: Bbar = (delta A)^-1 (exp(delta A) - I) delta B, which for a
+ * diagonal A is (exp(delta A_n) - 1) / A_n times B_n; at A_n = 0 it is its limit,
+ * delta).  expm1 keeps the relative accuracy when delta A_n is small. */
+static double zoh_coef(double dt, double An) {
+#if ORACLE_MUTANT == 26
+  (void)An;
+  return dt; /* Euler input term in place of the hold */
+#elif ORACLE_MUTANT == 27
+  return An != 0.0 ? expm1(dt * An) : dt; /* division by A_n missing */
+#else
+  return An != 0.0 ? expm1(dt * An) / An : dt;
+#endif
+}
+
+/* One independent chain: batch row b, channel d, all N states, t = 0..L-1;
+ * zoh selects the zero-order-hold input term instead of the Euler one. */
+static void scan_channel(const oracle_args *a, int64_t b, int64_t d, double *h, int zoh) {
   const int64_t L = a->seqlen, D = a->dim, N = a->dstate;
   for (int64_t n = 0; n < N; ++n) h[n] = a->h0 ? a->h0[(b * D + d) * N + n] : 0.0;
 #if ORACLE_MUTANT == 4
@@ -121,7 +138,7 @@ static void scan_channel(const oracle_args *a, int64_t b, int64_t d, double *h) 
 #elif ORACLE_MUTANT == 10
       const double bx = Bt[n] * xt; /* delta missing from the input term */
 #else
-      const double bx = dt * Bt[n] * xt;
+      const double bx = (zoh ? zoh_coef(dt, a->A[d * N + n]) : dt) * Bt[n] * xt;
 #endif
       h[n] = abar * h[n] + bx;
     }
@@ -154,6 +171,7 @@ static void scan_channel(const oracle_args *a, int64_t b, int64_t d, double *h) 
 typedef struct {
   const oracle_args *a;
   int64_t first, last; /* chain range [first, last) over b * D + d */
+  int zoh;
   int status;
 } worker_t;
 
@@ -161,7 +179,7 @@ static void *worker(void *p) {
   worker_t *w = (worker_t *)p;
   double *h = (double *)malloc(sizeof(double) * (size_t)w->a->dstate);
   if (!h) { w->status = -1; return NULL; }
-  for (int64_t c = w->first; c < w->last; ++c) scan_channel(w->a, c / w->a->dim, c % w->a->dim, h);
+  for (int64_t c = w->first; c < w->last; ++c) scan_channel(w->a, c / w->a->dim, c % w->a->dim, h, w->zoh);
   free(h);
   w->status = 0;
   return NULL;
@@ -171,7 +189,15 @@ static void *worker(void *p) {
  * spread over `nthreads` POSIX threads; each chain is still one plain loop
  * over t in increasing order and over n in increasing order.
  * Returns 0, or -1 on bad arguments / allocation failure. */
-int oracle_scan_f64(const oracle_args *a, int nthreads) {
+static int scan_threads(const oracle_args *a, int nthreads, int zoh);
+
+int oracle_scan_f64(const oracle_args *a, int nthreads) { return scan_threads(a, nthreads, 0); }
+
+/* The same scan with the zero-order-hold input term (section 2.2) in place of
+ * the Euler one: h_t = exp(delta A) h_{t-1} + (exp(delta A) - 1) / A * B_t x_t. */
+int oracle_scan_zoh_f64(const oracle_args *a, int nthreads) { return scan_threads(a, nthreads, 1); }
+
+static int scan_threads(const oracle_args *a, int nthreads, int zoh) {
   if (!a || !a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->y) return -1;
   if (a->batch < 0 || a->seqlen < 0 || a->dim < 0 || a->dstate <= 0) return -1;
   const int64_t chains = a->batch * a->dim;
@@ -185,6 +211,7 @@ int oracle_scan_f64(const oracle_args *a, int nthreads) {
     ws[k].a = a;
     ws[k].first = chains * k / nthreads;
     ws[k].last = chains * (k + 1) / nthreads;
+    ws[k].zoh = zoh;
     ws[k].status = 0;
   }
   for (int k = 1; k < nthreads; ++k) {

@@ -12,7 +12,7 @@ import pytest
 import oracle
 from tests import oracle_pins
 
-MUTANTS = list(range(1, 15))  # forward mutants; 15-18: backward (test_oracle_bwd.py); 19-20: conv prologue (test_oracle_conv.py); 21-22: SSD (test_oracle_ssd.py); 23-25: gated linear attention (test_oracle_gla.py)
+MUTANTS = list(range(1, 15))  # forward mutants; 15-18: backward (test_oracle_bwd.py); 19-20: conv prologue (test_oracle_conv.py); 21-22: SSD (test_oracle_ssd.py); 23-25: gated linear attention (test_oracle_gla.py); 26-27: zero-order hold (test_oracle_zoh.py)
 
 
 @pytest.fixture(scope="module")
