@@ -93,14 +93,14 @@ def stored_traffic(workload_name: str):
         return None
 
 
-def cpu_baseline(w, inp, max_threads=16):
+def cpu_baseline(w, inp, max_threads=16, zoh=False):
     """The fp64 oracle over the whole workload (every batch row, channel and
     token), threaded over independent channels; only the C call is timed."""
     import oracle
     threads = max(1, min(os.cpu_count() or 1, max_threads))
     timing = {}
     oracle.scan(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["delta_bias"],
-                inp.get("h0"), threads=threads, timing=timing)
+                inp.get("h0"), threads=threads, timing=timing, zoh=zoh)
     elems = w.elems
     return {
         "value": round(elems / timing["seconds"] / 1e9, 4),
@@ -524,6 +524,7 @@ def main():
     ap.add_argument("--variant", default="auto")
     ap.add_argument("--time-splits", type=int, default=0)
     ap.add_argument("--generic-a", action="store_true", help="never take the structured-decay path")
+    ap.add_argument("--zoh", action="store_true", help="zero-order-hold input term instead of the Euler one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true", help="time ssm_scan_bwd (all gradients) instead")
     ap.add_argument("--prologue", action="store_true", help="time the conv1d + SiLU prologue on x instead")
@@ -599,7 +600,7 @@ def main():
     y = [torch.empty_like(d1["x"]) for _ in sets]
     hT = [torch.empty(w.batch, w.dim, w.dstate, dtype=torch.float32, device=dev) for _ in sets]
     a0 = ssm.make_args(d1["x"], d1["delta"], d1["A"], d1["B"], d1["C"], d1["D"], d1["z"], d1["delta_bias"],
-                       d1["h0"], hT[0], y[0], None, args.variant, args.time_splits, args.generic_a)
+                       d1["h0"], hT[0], y[0], None, args.variant, args.time_splits, args.generic_a, args.zoh)
     nbytes = ssm.workspace_bytes(a0)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
     a0.workspace = None if ws is None else ws.data_ptr()
@@ -611,7 +612,7 @@ def main():
         s = sets[i % 2]
         ssm.scan_fwd(s["x"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], s["delta_bias"], s["h0"],
                      out=y[i % 2], final_state_out=hT[i % 2], workspace=ws, variant=args.variant,
-                     time_splits=args.time_splits, generic_a=args.generic_a)
+                     time_splits=args.time_splits, generic_a=args.generic_a, zoh=args.zoh)
 
     for i in range(args.warmup):
         step(i)
@@ -636,7 +637,7 @@ def main():
     kern_avg_s = float(np.mean(kern_ms)) * 1e-3
     alg = algorithmic_bytes(w)
     achieved = alg / kern_avg_s / 1e9
-    traffic = stored_traffic(w.name)
+    traffic = None if args.zoh else stored_traffic(w.name)  # counters were taken on the Euler kernel
     out = {
         "metric": "scan GElem/s (B*L*D*N) + % HBM roofline, B4 L8192 D4096 N16 bf16",
         "value": round(value, 2),
@@ -654,6 +655,7 @@ def main():
             "workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
             "io_dtype": str(w.dtype).replace("torch.", ""), "gate": w.gate, "final_state": w.final_state,
             "plan": {"variant": plan[0], "time_splits": plan[1], "generic_a": args.generic_a},
+            "discretisation": "zoh" if args.zoh else "euler",
         },
         "roofline": {
             "bound": "hbm",
@@ -669,7 +671,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        out["cpu_baseline"] = cpu_baseline(w, inp)
+        out["cpu_baseline"] = cpu_baseline(w, inp, zoh=args.zoh)
         log(f"cpu baseline {out['cpu_baseline']['value']} GElem/s on {out['cpu_baseline']['cores']} threads")
     print(json.dumps(out), flush=True)
 

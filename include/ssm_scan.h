@@ -64,6 +64,11 @@ enum ssm_flags {
    * (n+1)-th power of the decay of state 0 when A[d,n] == (n+1) A[d,0] holds
    * exactly for a channel block); every Abar is then its own exp. */
   SSM_FLAG_GENERIC_A = 1,
+  /* Zero-order-hold input term (section 2.2: Bbar = (delta A)^-1
+   * (exp(delta A) - I) delta B) instead of the Euler term delta B: state n
+   * receives (exp(delta A[d,n]) - 1) / A[d,n] * B[n] * x (delta * B[n] * x where
+   * A[d,n] == 0).  Forward only: ssm_scan_bwd rejects it (SSM_ERR_VARIANT). */
+  SSM_FLAG_ZOH = 2,
 };
 
 typedef struct ssm_scan_args {

@@ -29,6 +29,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 VARIANTS = {"auto": 0, "nsplit": 1, "lane": 2, "decode": 3}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 FLAG_GENERIC_A = 1
+FLAG_ZOH = 2
 
 # Exported symbols the header declares (checked by the tests).
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_scan_bwd",
@@ -170,8 +171,9 @@ def _check(name, t, shape, dtype, device):
 
 
 def make_args(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, hT=None, y=None,
-              workspace=None, variant="auto", time_splits=0, generic_a=False) -> ScanArgs:
-    """Check shapes/dtypes/devices of torch tensors and fill an ssm_scan_args."""
+              workspace=None, variant="auto", time_splits=0, generic_a=False, zoh=False) -> ScanArgs:
+    """Check shapes/dtypes/devices of torch tensors and fill an ssm_scan_args
+    (zoh: zero-order-hold input term instead of the Euler one)."""
     if x.dim() != 3:
         raise ValueError("x must be (B, L, D)")
     bsz, L, dim = x.shape
@@ -199,7 +201,7 @@ def make_args(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, hT=No
     a = ScanArgs()
     a.batch, a.seqlen, a.dim, a.dstate = bsz, L, dim, N
     a.dtype = DTYPE_F32 if io == torch.float32 else DTYPE_BF16
-    a.flags = FLAG_GENERIC_A if generic_a else 0
+    a.flags = (FLAG_GENERIC_A if generic_a else 0) | (FLAG_ZOH if zoh else 0)
     a.x, a.delta, a.A, a.B, a.C = _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C)
     a.D, a.z, a.delta_bias, a.h0, a.hT, a.y = _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(hT), _ptr(y)
     a.workspace = _ptr(workspace)
@@ -226,10 +228,12 @@ def workspace_bytes(args: ScanArgs) -> int:
 
 def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
              return_final_state=False, out=None, final_state_out=None, workspace=None,
-             variant="auto", time_splits=0, generic_a=False):
+             variant="auto", time_splits=0, generic_a=False, zoh=False):
     """Selective scan forward on the GPU.  Returns y, or (y, hT) with
     return_final_state=True.  `final_state_out` may be h0 itself (in-place state
-    update).  Launches on torch's current HIP stream and does not synchronise."""
+    update).  zoh=True discretises the input term with the zero-order hold,
+    (exp(delta A) - 1) / A * B x, instead of delta B x.  Launches on torch's
+    current HIP stream and does not synchronise."""
     if not x.is_cuda:
         raise ValueError("scan_fwd runs on the GPU only: move the tensors to a HIP device")
     L_ = lib()
@@ -237,7 +241,7 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
     hT = final_state_out
     if hT is None and return_final_state:
         hT = torch.empty((x.shape[0], x.shape[2], A.shape[1]), dtype=torch.float32, device=x.device)
-    args = make_args(x, delta, A, B, C, D, z, delta_bias, h0, hT, y, None, variant, time_splits, generic_a)
+    args = make_args(x, delta, A, B, C, D, z, delta_bias, h0, hT, y, None, variant, time_splits, generic_a, zoh)
     if workspace is None:
         nbytes = L_.ssm_scan_workspace_bytes(ctypes.byref(args))
         if nbytes < 0:

@@ -67,7 +67,7 @@ int validate(const ssm_scan_args* a, int64_t* n_bld, int64_t* n_bln, int64_t* n_
   const int64_t es = a->dtype == SSM_DTYPE_F32 ? 4 : 2;
   int64_t tmp;
   if (!mul_ok(bld, es, &tmp) || !mul_ok(bdn, 4, &tmp) || !mul_ok(bln, es, &tmp)) return SSM_ERR_SHAPE;
-  if (a->flags & ~static_cast<int32_t>(SSM_FLAG_GENERIC_A)) return SSM_ERR_VARIANT;
+  if (a->flags & ~static_cast<int32_t>(SSM_FLAG_GENERIC_A | SSM_FLAG_ZOH)) return SSM_ERR_VARIANT;
   if (a->variant < SSM_VARIANT_AUTO || a->variant > SSM_VARIANT_DECODE) return SSM_ERR_VARIANT;
   if (a->time_splits < 0) return SSM_ERR_VARIANT;
   *n_bld = bld;

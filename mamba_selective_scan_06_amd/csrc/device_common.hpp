@@ -51,6 +51,39 @@ __device__ __forceinline__ float silu_f32(float z) {
   return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
 }
 
+// Zero-order-hold input coefficient of one state (page youngju.dev section
+// 2.2: Bbar = (delta A)^-1 (exp(delta A) - I) delta B; for a diagonal A the
+// factor multiplying B_n x is (exp(delta A_n) - 1) / A_n, with limit delta at
+// A_n = 0).  `a` is exp(delta A_n) as computed for the decay.  Near a = 1 the
+// difference a - 1 loses relative accuracy, so for |z| < 1/32, z = delta A_n,
+// the factor is the series delta (1 + z/2 + z^2/6 + z^3/24) (truncation below
+// 1e-8 relative); above it a - 1 is accurate to ~2e-6.  A_n = 0 always takes
+// the series (inv_An is then unused).
+//
+// The choice is one v_cmp + v_cndmask written together, after both sides are
+// computed: left to itself the compiler turns it into a branch per element.
+__device__ __forceinline__ float select_small_z(float z, float if_small, float otherwise) {
+  float r;
+  asm("v_cmp_gt_f32_e64 vcc, %4, |%1|\n\tv_cndmask_b32_e32 %0, %3, %2, vcc"
+      : "=v"(r)
+      : "v"(z), "v"(if_small), "v"(otherwise), "s"(0.03125f)
+      : "vcc");
+  return r;
+}
+
+__device__ __forceinline__ float zoh_coef(float dt, float An, float inv_An, float a) {
+  const float z = dt * An;
+  const float series =
+      dt * __builtin_fmaf(z, __builtin_fmaf(z, __builtin_fmaf(z, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), 1.0f);
+  return select_small_z(z, series, (a - 1.0f) * inv_An);
+}
+
+// expm1(z) for z <= 0, with `a` = exp(z): the same series / difference split.
+__device__ __forceinline__ float expm1_neg(float z, float a) {
+  const float series = z * __builtin_fmaf(z, __builtin_fmaf(z, __builtin_fmaf(z, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), 1.0f);
+  return select_small_z(z, series, a - 1.0f);
+}
+
 // Wave index inside the workgroup as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 

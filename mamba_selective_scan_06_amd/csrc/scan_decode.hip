@@ -38,7 +38,7 @@ __device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float out[4])
 // issued first.
 constexpr int kDecodeRows = SSM_DECODE_ROWS;
 
-template <typename S, int Q>
+template <typename S, int Q, bool ZOH>
 __global__ __launch_bounds__(256) void scan_decode_kernel(
     const S* __restrict__ x, const S* __restrict__ dl, const float* __restrict__ A,
     const S* __restrict__ Bm, const S* __restrict__ Cm, const float* __restrict__ Dsk,
@@ -51,10 +51,15 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(
   const int64_t dq = static_cast<int64_t>(blockIdx.x) * CH + threadIdx.x / Q;
   const bool dact = dq < D;
   const int64_t d = dact ? dq : D - 1;  // inactive lanes read a valid channel, write nothing
-  float a[4];
+  float a[4], an[4], ia[4];
   {
     const float4 av = *reinterpret_cast<const float4*>(A + d * N + 4 * q);
-    a[0] = av.x * kLog2e; a[1] = av.y * kLog2e; a[2] = av.z * kLog2e; a[3] = av.w * kLog2e;
+    an[0] = av.x; an[1] = av.y; an[2] = av.z; an[3] = av.w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a[k] = an[k] * kLog2e;
+      ia[k] = ZOH ? 1.0f / an[k] : 0.0f;
+    }
   }
   const float bias_d = bias ? bias[d] : 0.0f;
   const float D_d = Dsk ? Dsk[d] : 0.0f;
@@ -89,7 +94,10 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float ab = fast_exp2(dt * a[k]);
-      hv[r][k] = __builtin_fmaf(ab, hv[r][k], u * Bv[k]);
+      if constexpr (ZOH)  // zero-order-hold input term: (exp(dt A) - 1) / A * B x
+        hv[r][k] = __builtin_fmaf(ab, hv[r][k], (zoh_coef(dt, an[k], ia[k], ab) * xv[r]) * Bv[k]);
+      else
+        hv[r][k] = __builtin_fmaf(ab, hv[r][k], u * Bv[k]);
       acc = __builtin_fmaf(Cv[k], hv[r][k], acc);
     }
     // Sum the Q partial readouts of this channel (lanes q = 0..Q-1 are adjacent).
@@ -107,17 +115,22 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(
   }
 }
 
-template <typename S, int Q>
-hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
+template <typename S, int Q, bool ZOH>
+hipError_t launch_decode_z(const Problem& p, hipStream_t stream) {
   constexpr int CH = 256 / Q;
   dim3 grid(static_cast<unsigned>((p.dim + CH - 1) / CH),
             static_cast<unsigned>((p.batch + kDecodeRows - 1) / kDecodeRows));
-  hipLaunchKernelGGL((scan_decode_kernel<S, Q>), grid, dim3(256), 0, stream,
+  hipLaunchKernelGGL((scan_decode_kernel<S, Q, ZOH>), grid, dim3(256), 0, stream,
                      static_cast<const S*>(p.x), static_cast<const S*>(p.delta), p.A,
                      static_cast<const S*>(p.B), static_cast<const S*>(p.C), p.D,
                      static_cast<const S*>(p.z), p.delta_bias, p.h0, p.hT, static_cast<S*>(p.y), p.batch,
                      p.dim);
   return hipGetLastError();
+}
+
+template <typename S, int Q>
+hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
+  return (p.flags & kFlagZoh) ? launch_decode_z<S, Q, true>(p, stream) : launch_decode_z<S, Q, false>(p, stream);
 }
 
 template <typename S>

@@ -30,6 +30,7 @@ struct Problem {
 };
 
 constexpr int kFlagGenericA = 1;
+constexpr int kFlagZoh = 2;
 
 // Tile length (timesteps) of the NSPLIT family; segment lengths are multiples of it.
 constexpr int kNsplitTile = 16;

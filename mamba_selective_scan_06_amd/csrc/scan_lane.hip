@@ -15,7 +15,7 @@
 namespace ssm {
 namespace {
 
-template <typename S, int NMAX>
+template <typename S, int NMAX, bool ZOH>
 __global__ __launch_bounds__(64) void scan_lane_kernel(
     const S* __restrict__ x, const S* __restrict__ dl, const float* __restrict__ A,
     const S* __restrict__ Bm, const S* __restrict__ Cm, const float* __restrict__ Dsk,
@@ -29,16 +29,13 @@ __global__ __launch_bounds__(64) void scan_lane_kernel(
   const uint32_t lo = active ? lane : static_cast<uint32_t>(D - 1 - d0);
   const int64_t d = d0 + lo;
 
-  float A2[NMAX], h[NMAX];
+  float A2[NMAX], h[NMAX], An[ZOH ? NMAX : 1], iA[ZOH ? NMAX : 1];
 #pragma unroll
   for (int n = 0; n < NMAX; ++n) {
-    if (n < N) {
-      A2[n] = A[d * N + n] * kLog2e;
-      h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0f;
-    } else {
-      A2[n] = 0.0f;
-      h[n] = 0.0f;
-    }
+    const float av = n < N ? A[d * N + n] : 0.0f;
+    A2[n] = av * kLog2e;
+    h[n] = n < N && h0 ? h0[(b * D + d) * N + n] : 0.0f;
+    if constexpr (ZOH) An[n] = av, iA[n] = 1.0f / av;
   }
   const float bs = bias ? bias[d] : 0.0f;
   const float Dd = Dsk ? Dsk[d] : 0.0f;
@@ -57,7 +54,10 @@ __global__ __launch_bounds__(64) void scan_lane_kernel(
     for (int n = 0; n < NMAX; ++n) {
       if (n < N) {
         const float a = fast_exp2(dt * A2[n]);
-        h[n] = __builtin_fmaf(a, h[n], u * to_f32(Bt[n]));
+        if constexpr (ZOH)  // zero-order-hold input term: (exp(dt A) - 1) / A * B x
+          h[n] = __builtin_fmaf(a, h[n], (zoh_coef(dt, An[n], iA[n], a) * xv) * to_f32(Bt[n]));
+        else
+          h[n] = __builtin_fmaf(a, h[n], u * to_f32(Bt[n]));
         acc = __builtin_fmaf(to_f32(Ct[n]), h[n], acc);
       }
     }
@@ -72,15 +72,20 @@ __global__ __launch_bounds__(64) void scan_lane_kernel(
   }
 }
 
-template <typename S, int NMAX>
-hipError_t launch_lane_t(const Problem& p, hipStream_t stream) {
+template <typename S, int NMAX, bool ZOH>
+hipError_t launch_lane_z(const Problem& p, hipStream_t stream) {
   dim3 grid(static_cast<unsigned>((p.dim + 63) / 64), static_cast<unsigned>(p.batch));
-  hipLaunchKernelGGL((scan_lane_kernel<S, NMAX>), grid, dim3(64), 0, stream,
+  hipLaunchKernelGGL((scan_lane_kernel<S, NMAX, ZOH>), grid, dim3(64), 0, stream,
                      static_cast<const S*>(p.x), static_cast<const S*>(p.delta), p.A,
                      static_cast<const S*>(p.B), static_cast<const S*>(p.C), p.D,
                      static_cast<const S*>(p.z), p.delta_bias, p.h0, p.hT, static_cast<S*>(p.y),
                      p.seqlen, p.dim, static_cast<int>(p.dstate));
   return hipGetLastError();
+}
+
+template <typename S, int NMAX>
+hipError_t launch_lane_t(const Problem& p, hipStream_t stream) {
+  return (p.flags & kFlagZoh) ? launch_lane_z<S, NMAX, true>(p, stream) : launch_lane_z<S, NMAX, false>(p, stream);
 }
 
 template <typename S>

@@ -40,7 +40,8 @@ def _bwd(a):
     (dict(x=0), -1), (dict(delta=0), -1), (dict(A=0), -1), (dict(B=0), -1), (dict(C=0), -1), (dict(dy=0), -1),
     (dict(z=0), -1),  # dz is given, so z is needed
     (dict(dx=FAKE + 4), -5), (dict(dhT=FAKE + 8), -5), (dict(workspace=FAKE + 2), -5),
-    (dict(flags=2), -9), (dict(time_splits=-1), -9), (dict(reserved=1), -9),
+    (dict(flags=2), -9),  # the zero-order hold is forward only
+    (dict(flags=4), -9), (dict(time_splits=-1), -9), (dict(reserved=1), -9),
     (dict(workspace=0), -7),
     (dict(workspace_bytes=16), -7),
 ])
