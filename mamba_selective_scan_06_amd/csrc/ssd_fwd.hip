@@ -109,14 +109,18 @@ __device__ __forceinline__ void write_perm(uint16_t* row, int n0, const uint32_t
 
 template <int N, int NW>
 struct alignas(16) SsdSmem {
-  uint16_t M[2][kQ][kQ + kPad];   // masked decayed C B^T (+ D on the diagonal), hi and lo: [t][s]
-  uint16_t xt[kP][kQ + kPad];     // x transposed: [p][s]
-  uint16_t xw[2][kP][kQ + kPad];  // x o w transposed, hi and lo: [p][s]
+  // Chunk-major [k / 8][row][8] arrays: the 16 lanes that read one 16-byte
+  // chunk of 16 consecutive rows read 256 contiguous bytes (no bank conflict),
+  // and a lane that owns a row writes its 8 values as one 16-byte store.
+  uint16_t M[2][kQ / 8][kQ][8];   // masked decayed C B^T (+ D on the diagonal), hi and lo: [s/8][t][s%8]
+  uint16_t xt[kQ / 8][kP][8];     // x: [s/8][p][s%8]
+  uint16_t xw[2][kQ / 8][kP][8];  // x o w, hi and lo: [s/8][p][s%8]
   uint16_t bt[N][kQ + kPad];      // B transposed: [n][s]
   uint16_t bn[kQ][N + kPad];      // B, n permuted: [s][n]
   uint16_t cn[kQ][N + kPad];      // C, n permuted: [t][n]
   float dl[kQ];                   // input scale i per token (0 past L)
   float cs[kQ];                   // running sum of the log decay inside the chunk
+  float ww[kQ];                   // weight of each token in the chunk's state update: exp(cs_end - cs) i
   float4 xch[NW > 4 ? NW : 1][2][64];  // halves of C H^T handed to the slice's other wave
 };
 
@@ -141,8 +145,7 @@ struct KArgs {
 template <int N, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
   constexpr int NK = NW / 4;          // parts of the n range, one per wave of a channel slice
-  constexpr int XC = 8 / NK;          // x channels per staging thread (2 tokens each)
-  constexpr int XG = kP / XC;         // x channel groups
+  constexpr int XT = kQ / NW;         // x tokens per staging lane (one channel each)
   constexpr int TPT = N / (8 * NW);   // tokens per staging thread for B and C (8 n each)
   constexpr int TG = kQ / TPT;        // token groups per n group
   constexpr int NMK = N / 32 / NK;    // 32-wide k steps over the wave's n part
@@ -174,8 +177,8 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
     bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
     Dh = a.D ? a.D[h] : 0.0f;
   }
-  // staging roles: x as 2 tokens x XC channels, B and C as TPT tokens x 8 n
-  const int xpg = tid % XG, xtq = tid / XG;
+  // staging roles: x as one channel (the lane) x XT tokens (8 x wave index ...),
+  // B and C as TPT tokens x 8 n
   const int btq = tid % TG, bng = tid / TG;
   // buffer descriptor over the rows [t0, min(t0 + 64, L)) of a (tokens x row) tensor;
   // empty (every access out of range) past the end or for an absent input
@@ -196,21 +199,13 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
   }
 
   // raw data of the next chunk, loaded one chunk ahead
-  uint32_t xr[2][XC / 2], br[TPT][4], cr[TPT][4];
+  uint32_t xr[XT], br[TPT][4], cr[TPT][4];
   uint32_t traw = 0, tlf = 0, tig = 0;  // the lane's per-token inputs (raw bits): dt, or log_f and in_gate
-  auto load_x = [&](int64_t t0) {
+  auto load_x = [&](int64_t t0) {  // 16-bit loads: a wave instruction reads one 128-byte token row
     const auto r = rows_buf(xb + t0 * xrow, t0, xrow * 2, kP * 2);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t off = static_cast<uint32_t>((2 * xtq + j) * xrow * 2 + XC * xpg * 2);
-      if constexpr (XC == 8) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-        xr[j][0] = v.x, xr[j][1] = v.y, xr[j][2] = v.z, xr[j][3] = v.w;
-      } else {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-        xr[j][0] = v.x, xr[j][1] = v.y;
-      }
-    }
+    for (int j = 0; j < XT; ++j)
+      xr[j] = __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<uint32_t>((XT * wi + j) * xrow * 2 + lane * 2), 0, 0);
   };
   auto load_bc = [&](int64_t t0) {
     const auto rb = rows_buf(Bb + t0 * brow, t0, brow * 2, N * 2);
@@ -265,10 +260,14 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
       }
       sm.dl[lane] = d;
       sm.cs[lane] = s;
+      const float s_end = __shfl(s, kQ - 1, 64);
+      sm.ww[lane] = fast_exp2((s_end - s) * kLog2e) * d;
     }
 #pragma unroll
-    for (int e = 0; e < XC; ++e)
-      *reinterpret_cast<uint32_t*>(&sm.xt[XC * xpg + e][2 * xtq]) = elem(xr[0], e) | (elem(xr[1], e) << 16);
+    for (int q = 0; q < XT / 8; ++q)
+      *reinterpret_cast<uint4*>(&sm.xt[XT / 8 * wi + q][lane][0]) =
+          make_uint4(xr[8 * q] | (xr[8 * q + 1] << 16), xr[8 * q + 2] | (xr[8 * q + 3] << 16),
+                     xr[8 * q + 4] | (xr[8 * q + 5] << 16), xr[8 * q + 6] | (xr[8 * q + 7] << 16));
     if constexpr (MODE == 2) {
 #pragma unroll
       for (int j = 0; j < TPT; ++j) feature_map(br[j]), feature_map(cr[j]);
@@ -298,17 +297,18 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
 
     // ---- B. x o w; masked G^T tiles into M; the wave's part of C H^T
     const float cs_end = sm.cs[kQ - 1];
-    {
-      const int t = 2 * xtq;
-      const float w0 = fast_exp2((cs_end - sm.cs[t]) * kLog2e) * sm.dl[t];
-      const float w1 = fast_exp2((cs_end - sm.cs[t + 1]) * kLog2e) * sm.dl[t + 1];
 #pragma unroll
-      for (int e = 0; e < XC; ++e) {
-        uint32_t hi, lo;
-        split2(w0 * bits_f32(elem(xr[0], e)), w1 * bits_f32(elem(xr[1], e)), hi, lo);
-        *reinterpret_cast<uint32_t*>(&sm.xw[0][XC * xpg + e][t]) = hi;
-        *reinterpret_cast<uint32_t*>(&sm.xw[1][XC * xpg + e][t]) = lo;
-      }
+    for (int q = 0; q < XT / 8; ++q) {  // x o w for the lane's channel and 8 tokens
+      const int c8 = XT / 8 * wi + q;
+      const float4 w0 = *reinterpret_cast<const float4*>(&sm.ww[8 * c8]);
+      const float4 w1 = *reinterpret_cast<const float4*>(&sm.ww[8 * c8 + 4]);
+      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        split2(wv[e] * bits_f32(xr[8 * q + e]), wv[e + 1] * bits_f32(xr[8 * q + e + 1]), hi[e / 2], lo[e / 2]);
+      *reinterpret_cast<uint4*>(&sm.xw[0][c8][lane][0]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(&sm.xw[1][c8][lane][0]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
     load_x(t0 + kQ);
 #pragma unroll
@@ -346,8 +346,8 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
         split2(v[0], v[1], hw.x, lw.x);
         split2(v[2], v[3], hw.y, lw.y);
       }
-      *reinterpret_cast<uint2*>(&sm.M[0][t][s0]) = hw;
-      *reinterpret_cast<uint2*>(&sm.M[1][t][s0]) = lw;
+      *reinterpret_cast<uint2*>(&sm.M[0][s0 / 8][t][s0 % 8]) = hw;
+      *reinterpret_cast<uint2*>(&sm.M[1][s0 / 8][t][s0 % 8]) = lw;
     }
     f32x4 yo[4] = {};
 #pragma unroll
@@ -384,9 +384,9 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
       f32x4 acc = {};
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        const bf16x8 xa = lds8(&sm.xt[16 * w + lr][32 * kk + 8 * lg]);
-        acc = mfma(xa, lds8(&sm.M[0][16 * i + lr][32 * kk + 8 * lg]), acc);
-        acc = mfma(xa, lds8(&sm.M[1][16 * i + lr][32 * kk + 8 * lg]), acc);
+        const bf16x8 xa = lds8(&sm.xt[4 * kk + lg][16 * w + lr][0]);
+        acc = mfma(xa, lds8(&sm.M[0][4 * kk + lg][16 * i + lr][0]), acc);
+        acc = mfma(xa, lds8(&sm.M[1][4 * kk + lg][16 * i + lr][0]), acc);
       }
       const int t = 16 * i + lr;
       const float e = fast_exp2(sm.cs[t] * kLog2e);
@@ -433,8 +433,8 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
       bf16x8 xh[2], xl[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        xh[kk] = lds8(&sm.xw[0][16 * w + lr][32 * kk + 8 * lg]);
-        xl[kk] = lds8(&sm.xw[1][16 * w + lr][32 * kk + 8 * lg]);
+        xh[kk] = lds8(&sm.xw[0][4 * kk + lg][16 * w + lr][0]);
+        xl[kk] = lds8(&sm.xw[1][4 * kk + lg][16 * w + lr][0]);
       }
 #pragma unroll
       for (int j = 0; j < NJK; ++j) {
