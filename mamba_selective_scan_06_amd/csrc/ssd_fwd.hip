@@ -141,7 +141,6 @@ struct KArgs {
   int H, G;
 };
 
-
 template <int N, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
   constexpr int NK = NW / 4;          // parts of the n range, one per wave of a channel slice
@@ -177,7 +176,7 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
     bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
     Dh = a.D ? a.D[h] : 0.0f;
   }
-  // staging roles: x as one channel (the lane) x XT tokens (8 x wave index ...),
+  // staging roles: x as the lane's channel over the XT tokens [XT wi, XT wi + XT);
   // B and C as TPT tokens x 8 n
   const int btq = tid % TG, bng = tid / TG;
   // buffer descriptor over the rows [t0, min(t0 + 64, L)) of a (tokens x row) tensor;
@@ -293,7 +292,7 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
     }
     load_bc(t0 + kQ);  // past the last chunk these read nothing
     load_tok(t0 + kQ);
-    __syncthreads();  // dl, cs, xt, bt, bn, cn complete
+    __syncthreads();  // dl, cs, ww, xt, bt, bn, cn complete
 
     // ---- B. x o w; masked G^T tiles into M; the wave's part of C H^T
     const float cs_end = sm.cs[kQ - 1];
