@@ -227,6 +227,28 @@ def bench_decode(w, args, ssm, torch):
     elapsed = time.perf_counter() - t0
     step_ms = [a.elapsed_time(b) for e in evs for a, b in e]
     per_step_s = float(np.mean(step_ms)) * 1e-3
+    # The same pass captured once in a HIP graph and replayed: the launches of the
+    # decode steps leave the host path (the library allocates nothing and issues no
+    # memset, so the chain can be captured).
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_pass()
+    torch.cuda.synchronize()
+    for _ in range(max(args.warmup, 1)):
+        graph.replay()
+    torch.cuda.synchronize()
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(passes)]
+    t0 = time.perf_counter()
+    for i in range(passes):
+        gev[i][0].record(stream)
+        graph.replay()
+        gev[i][1].record(stream)
+    torch.cuda.synchronize()
+    graph_ms_per_pass = (time.perf_counter() - t0) * 1e3 / passes
+    # kernel time per decode step: the replayed steps run back to back with no
+    # host work or event between them, so this is the kernel's own duration
+    # (events around each eager step add a few microseconds to each)
+    graph_step_s = float(np.mean([a.elapsed_time(b) for a, b in gev])) * 1e-3 / w.steps
     es = 2 if "bfloat16" in str(w.dtype) else 4
     bd = w.batch * w.dim
     step_bytes = (4 if w.gate else 3) * bd * es + 2 * w.batch * w.dstate * es + w.dim * w.dstate * 4 + \
@@ -240,9 +262,14 @@ def bench_decode(w, args, ssm, torch):
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
                    "io_dtype": str(w.dtype).replace("torch.", ""), "gate": w.gate, "decode_steps": w.steps,
                    "plan": {"variant": "decode", "in_place": True}},
-        "per_step_kernel_us": round(per_step_s * 1e6, 2),
+        "per_step_kernel_us": round(graph_step_s * 1e6, 2),
+        "per_step_eager_event_us": round(per_step_s * 1e6, 2),
         "wall_us_per_decode_step": round(ms_per_pass * 1e3 / w.steps, 2),
-        "roofline": _roofline(step_bytes, per_step_s, "scan_decode_kernel"),
+        "graph": {"ms_per_pass": round(graph_ms_per_pass, 5),
+                  "wall_us_per_decode_step": round(graph_ms_per_pass * 1e3 / w.steps, 2),
+                  "value": round(w.elems / (graph_ms_per_pass * 1e-3) / 1e9, 2),
+                  "note": "one pass of the decode steps captured in a HIP graph and replayed"},
+        "roofline": _roofline(step_bytes, graph_step_s, "scan_decode_kernel"),
     }
 
 
