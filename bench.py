@@ -145,7 +145,7 @@ def bench_chunked(w, args, ssm, torch):
             if events is not None:
                 events[c][0].record(stream)
             ssm.scan_fwd(ch["x"], ch["delta"], A, ch["B"], ch["C"], D, ch["z"], bias,
-                         h_in if c > 0 else None, out=ys[c], final_state_out=h_out)
+                         h_in if c > 0 else None, out=ys[c], final_state_out=h_out, time_splits=args.time_splits)
             if events is not None:
                 events[c][1].record(stream)
 
@@ -167,7 +167,7 @@ def bench_chunked(w, args, ssm, torch):
     state = w.batch * w.dim * w.dstate * 4
     call_bytes = (4 if w.gate else 3) * bld * es + 2 * bln * es + w.dim * w.dstate * 4 + 2 * w.dim * 4 + 2 * state
     probe = ssm.make_args(chunks[1]["x"], chunks[1]["delta"], A, chunks[1]["B"], chunks[1]["C"], D,
-                          chunks[1]["z"], bias, hs[0], hs[1], ys[1])
+                          chunks[1]["z"], bias, hs[0], hs[1], ys[1], None, "auto", args.time_splits)
     nbytes = ssm.workspace_bytes(probe)
     if nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)

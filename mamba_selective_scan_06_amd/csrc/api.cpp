@@ -122,10 +122,15 @@ int make_plan(const ssm_scan_args* a, bool have_workspace_info, Plan* pl) {
       if (in_place) return SSM_ERR_VARIANT;  // later segments read h0 after the last one wrote hT
       splits = a->time_splits;
     } else if (a->time_splits == 0 && !in_place) {
-      // Split until every one of the 1024 SIMDs has a wave, keeping segments
-      // at least 256 tokens long (a split costs an extra state-only pass).
-      const int64_t waves = 4 * ((a->dim + 63) / 64) * a->batch;
-      while (waves * splits < 1024 && L / (2 * splits) >= 256 && splits < 64) splits *= 2;
+      // One 8-wave block runs per compute unit at a time.  Splitting costs an
+      // extra state-only pass over all but the last segment, and pays only while
+      // every segment's block still finds a compute unit of its own: double the
+      // segments while blocks x segments fits the 256 compute units, keeping
+      // segments at least 256 tokens long.  (B8 L2048 D1536, 192 blocks, ran
+      // 25% slower with 2 segments than with 1: the second round of blocks.)
+      constexpr int64_t kComputeUnits = 256;
+      const int64_t blocks = ((a->dim + 63) / 64) * a->batch;
+      while (blocks * splits * 2 <= kComputeUnits && L / (2 * splits) >= 256 && splits < 64) splits *= 2;
     }
   }
   int64_t seg_len = L;
