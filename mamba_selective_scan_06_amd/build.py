@@ -24,14 +24,15 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 # (source, extra defines, object name)
-NSPLIT_INST = [(s, k) for s in ("float", "uint16_t") for k in (1, 2, 4, 8, 16)]
+NSPLIT_INST = [(s, k, w) for s in ("float", "uint16_t") for k in (1, 2, 4, 8, 16) for w in (0, 1)]
 UNITS = [("api.cpp", [], "api"), ("nsplit_dispatch.cpp", [], "nsplit_dispatch"),
          ("scan_lane.hip", [], "scan_lane"), ("scan_decode.hip", [], "scan_decode"),
          ("scan_bwd.hip", [], "scan_bwd"), ("conv_prologue.hip", [], "conv_prologue"),
          ("ssd_fwd.hip", [], "ssd_fwd"),
          ("scan_bwd_inst.hip", ["-DBWD_S=float"], "bwd_f32"), ("scan_bwd_inst.hip", ["-DBWD_S=uint16_t"], "bwd_bf16")] + [
-    ("nsplit_inst.hip", [f"-DNSPLIT_S={s}", f"-DNSPLIT_K={k}"], f"nsplit_{'f32' if s == 'float' else 'bf16'}_k{k}")
-    for s, k in NSPLIT_INST]
+    ("nsplit_inst.hip", [f"-DNSPLIT_S={s}", f"-DNSPLIT_K={k}", f"-DNSPLIT_WIN={w}"],
+     f"nsplit_{'f32' if s == 'float' else 'bf16'}_k{k}{'_win' if w else ''}")
+    for s, k, w in NSPLIT_INST]
 SOURCES = sorted({u[0] for u in UNITS})
 HEADERS = ["buffer_io.hpp", "device_common.hpp", "scan_bwd_impl.hpp", "scan_internal.hpp", "scan_nsplit_impl.hpp"]
 

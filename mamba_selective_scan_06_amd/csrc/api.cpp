@@ -35,13 +35,24 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool nsplit_ok(int64_t n) { return n == 4 || n == 8 || n == 16 || n == 32 || n == 64; }
 
-// The NSPLIT kernels address one batch row of a tensor through a buffer
-// descriptor with 32-bit byte offsets: every row must stay below 2 GiB.
-bool row_fits_32(const ssm_scan_args* a) {
-  const int64_t lim = (int64_t{1} << 31) - 1;
+// The NSPLIT kernels count tokens in 32 bits and address a batch row through
+// buffer descriptors with 32-bit byte offsets.  A row whose accesses (up to
+// 144 tokens past its end, for the prefetch) fit one 2 GiB descriptor uses
+// fixed descriptors; a longer row is addressed through windows that move along
+// it, with offsets under 144 tokens from the window start.  So a token of a
+// row must stay below 2 GiB / 144 (D up to about 7.4 million bf16 channels);
+// the row length itself is free.
+int64_t nsplit_token_bytes(const ssm_scan_args* a) {
   const int64_t es = a->dtype == SSM_DTYPE_F32 ? 4 : 2;
-  const int64_t dmax = (a->dim > a->dstate ? a->dim : a->dstate) * es;
-  return dmax > 0 && a->seqlen <= lim / dmax;
+  return (a->dim > a->dstate ? a->dim : a->dstate) * es;
+}
+bool nsplit_fits(const ssm_scan_args* a) {
+  const int64_t lim = (int64_t{1} << 31) - 1;
+  const int64_t tok = nsplit_token_bytes(a);
+  return tok > 0 && tok <= lim / 144 && a->seqlen <= lim - 1024;
+}
+bool nsplit_windowed(const ssm_scan_args* a) {
+  return (a->seqlen + 144) * nsplit_token_bytes(a) > (int64_t{1} << 31) - 1;
 }
 
 struct Plan {
@@ -105,14 +116,14 @@ int make_plan(const ssm_scan_args* a, bool have_workspace_info, Plan* pl) {
   if (variant == SSM_VARIANT_AUTO) {
     if (L == 1 && nsplit_ok(N))
       variant = SSM_VARIANT_DECODE;
-    else if (nsplit_ok(N) && row_fits_32(a))
+    else if (nsplit_ok(N) && nsplit_fits(a))
       variant = SSM_VARIANT_NSPLIT;
     else
       variant = SSM_VARIANT_LANE;
   }
   if ((variant == SSM_VARIANT_NSPLIT || variant == SSM_VARIANT_DECODE) && !nsplit_ok(N)) return SSM_ERR_VARIANT;
   if (variant == SSM_VARIANT_DECODE && L != 1) return SSM_ERR_VARIANT;
-  if (variant == SSM_VARIANT_NSPLIT && !row_fits_32(a)) return SSM_ERR_VARIANT;
+  if (variant == SSM_VARIANT_NSPLIT && !nsplit_fits(a)) return SSM_ERR_VARIANT;
   if (variant != SSM_VARIANT_NSPLIT && a->time_splits > 1) return SSM_ERR_VARIANT;
 
   int splits = 1;
@@ -425,6 +436,7 @@ int ssm_scan_fwd(const ssm_scan_args* a, void* stream) {
   p.y = a->y;
   p.splits = pl.splits;
   p.seg_len = pl.seg_len;
+  p.windowed = pl.variant == SSM_VARIANT_NSPLIT && nsplit_windowed(a);
   p.ws_state = pl.splits > 1 ? static_cast<float*>(a->workspace) : nullptr;
   p.ws_dsum = pl.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pl.ws_state_bytes) : nullptr;
 

@@ -1,10 +1,10 @@
 // Raw buffer access for the NSPLIT kernels (gfx950).
 //
-// A buffer descriptor covers one batch row of a tensor; the whole byte offset
-// goes in the VGPR operand, which is the part the hardware range check covers
-// on this GPU family.  Loads past the end return 0 and stores past the end are
-// dropped, which lets the kernels prefetch past the end of a sequence and run
-// padded tiles without bounds branches.
+// A buffer descriptor covers part of one batch row of a tensor (under 2 GiB);
+// the whole byte offset goes in the VGPR operand, which is the part the
+// hardware range check covers on this GPU family.  Loads past the end return 0
+// and stores past the end are dropped, which lets the kernels prefetch past the
+// end of a sequence and run padded tiles without bounds branches.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,9 +16,13 @@ namespace ssm {
 // Word 3 of a raw buffer descriptor on the gfx9 family: 32-bit data format.
 constexpr int kRawBufferFlags = 0x00020000;
 
-// Offset that fails the range check of every descriptor used here (each
-// covers less than 2 GiB).
+// Largest byte count a descriptor here covers, and an offset that fails the
+// range check of every such descriptor.
+constexpr int64_t kMaxRecords = 0x7FFFFFFF;
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+// A base offset past every window: adding any in-window offset (below 2^31)
+// neither wraps nor comes back into range.
+constexpr uint32_t kPastWindow = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buf(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRawBufferFlags);

@@ -27,6 +27,7 @@ struct Problem {
   int64_t seg_len;   // timesteps per segment (multiple of the tile length)
   float* ws_state;   // (B, splits, D, N) segment end states from a zero start
   float* ws_dsum;    // (B, splits, D) sum of softplus(delta) over each segment
+  bool windowed;     // a row of x or B spans 2 GiB or more: move the descriptors along it
 };
 
 constexpr int kFlagGenericA = 1;

@@ -128,6 +128,28 @@ def test_plan_and_workspace_queries():
     assert ssm.plan(_args(shape=(2, 64, 128, 16), variant=2)) == ("lane", 1)
 
 
+def test_plan_long_rows_stay_on_the_main_kernel():
+    """Rows past 2^31 and 2^32 bytes plan the main kernel (its descriptor
+    windows move along the row); only a token wider than a window allows, or a
+    row longer than 32-bit token counts allow, falls back to LANE."""
+    def big(shape, dtype):
+        a = _args(shape=shape, dtype=dtype)
+        base = FAKE
+        for name in ("x", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0", "hT", "y"):
+            setattr(a, name, base)
+            base += 1 << 40  # disjoint 1 TiB windows
+        return a
+    assert ssm.plan(big((1, 262_152, 4104, 16), 1)) == ("nsplit", 1)   # 2.15 GB bf16 row
+    assert ssm.plan(big((1, 270_008, 4104, 16), 0)) == ("nsplit", 1)   # 4.43 GB fp32 row
+    assert ssm.plan(big((1, 2**31 - 1025, 64, 16), 1)) == ("nsplit", 1)
+    assert ssm.plan(big((1, 2**31 - 1024, 64, 16), 1)) == ("lane", 1)
+    lim = (2**31 - 1) // 144
+    assert ssm.plan(big((1, 64, lim // 2, 16), 1)) == ("nsplit", 1)
+    assert ssm.plan(big((1, 64, lim // 2 + 1, 16), 1)) == ("lane", 1)
+    assert ssm.plan(big((1, 64, lim // 4, 16), 0)) == ("nsplit", 1)
+    assert ssm.plan(big((1, 64, lim // 4 + 1, 16), 0)) == ("lane", 1)
+
+
 def test_zoh_flag_accepted():
     """SSM_FLAG_ZOH (alone or with SSM_FLAG_GENERIC_A) passes the host checks;
     with batch 0 nothing is launched."""

@@ -1,0 +1,64 @@
+"""Maximum sizes: batch rows of more than 2 and 4 GiB per tensor, in one call.
+
+The main kernel addresses a row through buffer descriptors with 32-bit byte
+offsets; its windows move along the row so that offsets stay small whatever
+the row length.  These cases put rows past 2^31 and 2^32 bytes through it,
+unsplit and with forced time segments that start gigabytes into the row, and
+compare sampled channels (each a whole independent chain over every token)
+with the fp64 oracle.  Every y must also be finite.
+"""
+from __future__ import annotations
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import mamba_selective_scan_06_amd as ssm
+import workloads
+from tests.gpu_helpers import DEV, check, oracle_scan, sample_channels, select
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a HIP GPU"),
+]
+
+CASES = [
+    # (workload index for dtype and recipe, B, L, D): D ragged against 64-channel
+    # blocks, L ragged against 16-token tiles
+    (1, 1, 262_152, 4104),   # bf16: 2.15 GB per row (> 2^31 bytes)
+    (0, 1, 270_008, 4104),   # fp32: 4.43 GB per row (> 2^32 bytes)
+]
+
+
+@pytest.mark.parametrize("wi,bsz,L,dim", CASES, ids=["bf16-row2.15GB", "fp32-row4.43GB"])
+def test_rows_beyond_32bit_offsets(wi, bsz, L, dim):
+    w = workloads.WORKLOADS[wi]
+    inp = workloads.make_large_inputs(w, batch=bsz, seqlen=L, dim=dim)
+    row_bytes = L * dim * inp["x"].element_size()
+    print(f"  B={bsz} L={L} D={dim} {w.dtype}: {row_bytes / 2**30:.2f} GiB per row", flush=True)
+    chans = sample_channels(dim, k=12, seed=L)
+    sub = select(inp, list(range(bsz)), chans)
+    yr, hr = oracle_scan(sub)
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    del inp
+    gc.collect()
+    y = torch.empty_like(d["x"])
+    hT = torch.empty((bsz, dim, w.dstate), dtype=torch.float32, device=DEV)
+    a = ssm.make_args(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["delta_bias"], None, hT, y)
+    assert ssm.plan(a)[0] == "nsplit"
+    ci = torch.as_tensor(chans, device=DEV)
+    for splits in (0, 4):
+        y.fill_(float("nan"))
+        ssm.scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["delta_bias"],
+                     out=y, final_state_out=hT, time_splits=splits)
+        torch.cuda.synchronize()
+        print(f"  time_splits={splits}", flush=True)
+        assert bool(torch.isfinite(y).all())
+        ys = y.index_select(2, ci).float().cpu().double().numpy()
+        hs = hT.index_select(1, ci).cpu().double().numpy()
+        check(f"y splits={splits}", ys, yr, w.dtype)
+        check(f"hT splits={splits}", hs, hr, w.dtype)
+    del d, y, hT
+    torch.cuda.empty_cache()

@@ -126,6 +126,36 @@ def make_inputs(w: Workload, *, batch: int | None = None, seqlen: int | None = N
     return out
 
 
+def make_large_inputs(w: Workload, *, batch: int, seqlen: int, dim: int, seed_extra=(), rows_per_draw=8192):
+    """Seeded inputs too large for make_inputs' numpy fp32 intermediates (rows
+    of several GiB): the same distributions, drawn rows_per_draw tokens at a time
+    by torch's CPU generator (seeded from the workload's SeedSequence, one
+    generator per tensor) straight into tensors of the workload's dtype.
+    x, delta, z ~ N(0, 1) (z only for gated workloads), B, C ~ N(0, 1), no h0;
+    A, D, delta_bias from make_params."""
+    N = w.dstate
+    ss = np.random.SeedSequence([ROOT_SEED, int(w.index), *[int(e) for e in seed_extra], 1])
+    seeds = [int(c.generate_state(1, dtype=np.uint64)[0] >> np.uint64(1)) for c in ss.spawn(5)]
+    gens = [torch.Generator().manual_seed(sd) for sd in seeds]
+
+    def draw(i, shape):
+        return torch.randn(shape, generator=gens[i], dtype=torch.float32).to(w.dtype)
+
+    out = {"x": torch.empty((batch, seqlen, dim), dtype=w.dtype),
+           "delta": torch.empty((batch, seqlen, dim), dtype=w.dtype),
+           "z": torch.empty((batch, seqlen, dim), dtype=w.dtype) if w.gate else None,
+           "B": draw(2, (batch, seqlen, N)), "C": draw(3, (batch, seqlen, N)), "h0": None}
+    for key, i in (("x", 0), ("delta", 1), ("z", 4)):
+        if out[key] is None:
+            continue
+        for b in range(batch):
+            for t0 in range(0, seqlen, rows_per_draw):
+                rows = min(rows_per_draw, seqlen - t0)
+                out[key][b, t0:t0 + rows] = draw(i, (rows, dim))
+    out.update(make_params(w, dim, N, seed_extra=seed_extra))
+    return out
+
+
 def make_decode_step(w: Workload, step: int, *, batch: int | None = None, dim: int | None = None):
     """Fresh per-step tensors (x, delta, B, C, z) of a decode workload, L = 1."""
     bsz = batch or w.batch
