@@ -14,6 +14,8 @@ Recipe (the five workloads; every tensor is synthetic, no dataset or weights):
   * bf16 tensors are fp32 draws rounded to nearest-even by torch.
 Seeds: numpy PCG64 seeded from SeedSequence([20261203, workload_index, *extra]),
 one spawned stream per tensor in the fixed order x, delta, B, C, z, u, D, h0.
+Inputs of several GiB per tensor (make_large_inputs) are drawn by torch's CPU
+generator, seeded from the same SeedSequence, in blocks of tokens.
 """
 from __future__ import annotations
 
