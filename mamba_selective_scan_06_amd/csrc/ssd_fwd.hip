@@ -107,20 +107,28 @@ __device__ __forceinline__ void write_perm(uint16_t* row, int n0, const uint32_t
   *reinterpret_cast<uint2*>(row + pp + 8) = make_uint2(v[2], v[3]);
 }
 
+// Arrays that phase C of a chunk reads and phase A of the next one writes
+// (x^T, B^T, the per-token scalars) are double-buffered by chunk parity when
+// the LDS allows it (N <= 128): the barrier at the end of a chunk then goes,
+// and the next chunk's staging overlaps the slower waves' last products.
+template <int N>
+constexpr int kSsdStageBufs = N <= 128 ? 2 : 1;
+
 template <int N, int NW>
 struct alignas(16) SsdSmem {
+  static constexpr int NB = kSsdStageBufs<N>;
   // Chunk-major [k / 8][row][8] arrays: the 16 lanes that read one 16-byte
   // chunk of 16 consecutive rows read 256 contiguous bytes (no bank conflict),
   // and a lane that owns a row writes its 8 values as one 16-byte store.
   uint16_t M[2][kQ / 8][kQ][8];   // masked decayed C B^T (+ D on the diagonal), hi and lo: [s/8][t][s%8]
-  uint16_t xt[kQ / 8][kP][8];     // x: [s/8][p][s%8]
+  uint16_t xt[NB][kQ / 8][kP][8]; // x: [s/8][p][s%8]
   uint16_t xw[2][kQ / 8][kP][8];  // x o w, hi and lo: [s/8][p][s%8]
-  uint16_t bt[N][kQ + kPad];      // B transposed: [n][s]
+  uint16_t bt[NB][N][kQ + kPad];  // B transposed: [n][s]
   uint16_t bn[kQ][N + kPad];      // B, n permuted: [s][n]
   uint16_t cn[kQ][N + kPad];      // C, n permuted: [t][n]
-  float dl[kQ];                   // input scale i per token (0 past L)
-  float cs[kQ];                   // running sum of the log decay inside the chunk
-  float ww[kQ];                   // weight of each token in the chunk's state update: exp(cs_end - cs) i
+  float dl[NB][kQ];               // input scale i per token (0 past L)
+  float cs[NB][kQ];               // running sum of the log decay inside the chunk
+  float ww[NB][kQ];               // weight of each token in the chunk's state update: exp(cs_end - cs) i
   float4 xch[NW > 4 ? NW : 1][2][64];  // halves of C H^T handed to the slice's other wave
 };
 
@@ -240,6 +248,7 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t t0 = c * kQ;
+    const int cb = kSsdStageBufs<N> == 2 ? static_cast<int>(c & 1) : 0;  // staging buffer of this chunk
     // ---- A. per-token scalars (wave 0, one token per lane); x^T, B^T, B, C into LDS
     if (wi == 0) {
       const bool valid = t0 + lane < L;
@@ -257,14 +266,14 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
         const float o = __shfl_up(s, off, 64);
         if (lane >= off) s += o;
       }
-      sm.dl[lane] = d;
-      sm.cs[lane] = s;
+      sm.dl[cb][lane] = d;
+      sm.cs[cb][lane] = s;
       const float s_end = __shfl(s, kQ - 1, 64);
-      sm.ww[lane] = fast_exp2((s_end - s) * kLog2e) * d;
+      sm.ww[cb][lane] = fast_exp2((s_end - s) * kLog2e) * d;
     }
 #pragma unroll
     for (int q = 0; q < XT / 8; ++q)
-      *reinterpret_cast<uint4*>(&sm.xt[XT / 8 * wi + q][lane][0]) =
+      *reinterpret_cast<uint4*>(&sm.xt[cb][XT / 8 * wi + q][lane][0]) =
           make_uint4(xr[8 * q] | (xr[8 * q + 1] << 16), xr[8 * q + 2] | (xr[8 * q + 3] << 16),
                      xr[8 * q + 4] | (xr[8 * q + 5] << 16), xr[8 * q + 6] | (xr[8 * q + 7] << 16));
     if constexpr (MODE == 2) {
@@ -273,7 +282,7 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      uint16_t* dst = &sm.bt[8 * bng + e][TPT * btq];
+      uint16_t* dst = &sm.bt[cb][8 * bng + e][TPT * btq];
       if constexpr (TPT == 1) {
         *dst = static_cast<uint16_t>(elem(br[0], e));
       } else {
@@ -295,12 +304,12 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
     __syncthreads();  // dl, cs, ww, xt, bt, bn, cn complete
 
     // ---- B. x o w; masked G^T tiles into M; the wave's part of C H^T
-    const float cs_end = sm.cs[kQ - 1];
+    const float cs_end = sm.cs[cb][kQ - 1];
 #pragma unroll
     for (int q = 0; q < XT / 8; ++q) {  // x o w for the lane's channel and 8 tokens
       const int c8 = XT / 8 * wi + q;
-      const float4 w0 = *reinterpret_cast<const float4*>(&sm.ww[8 * c8]);
-      const float4 w1 = *reinterpret_cast<const float4*>(&sm.ww[8 * c8 + 4]);
+      const float4 w0 = *reinterpret_cast<const float4*>(&sm.ww[cb][8 * c8]);
+      const float4 w1 = *reinterpret_cast<const float4*>(&sm.ww[cb][8 * c8 + 4]);
       const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
       uint32_t hi[4], lo[4];
 #pragma unroll
@@ -330,9 +339,9 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
 #pragma unroll
         for (int m = 0; m < N / 32; ++m)
           acc = mfma(lds8(&sm.bn[16 * si + lr][32 * m + 8 * lg]), lds8(&sm.cn[t][32 * m + 8 * lg]), acc);
-        const float cst = sm.cs[t];
-        const float4 css = *reinterpret_cast<const float4*>(&sm.cs[s0]);
-        const float4 dls = *reinterpret_cast<const float4*>(&sm.dl[s0]);
+        const float cst = sm.cs[cb][t];
+        const float4 css = *reinterpret_cast<const float4*>(&sm.cs[cb][s0]);
+        const float4 dls = *reinterpret_cast<const float4*>(&sm.dl[cb][s0]);
         const float csv[4] = {css.x, css.y, css.z, css.w}, dlv[4] = {dls.x, dls.y, dls.z, dls.w};
         float v[4];
 #pragma unroll
@@ -383,12 +392,12 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
       f32x4 acc = {};
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        const bf16x8 xa = lds8(&sm.xt[4 * kk + lg][16 * w + lr][0]);
+        const bf16x8 xa = lds8(&sm.xt[cb][4 * kk + lg][16 * w + lr][0]);
         acc = mfma(xa, lds8(&sm.M[0][4 * kk + lg][16 * i + lr][0]), acc);
         acc = mfma(xa, lds8(&sm.M[1][4 * kk + lg][16 * i + lr][0]), acc);
       }
       const int t = 16 * i + lr;
-      const float e = fast_exp2(sm.cs[t] * kLog2e);
+      const float e = fast_exp2(sm.cs[cb][t] * kLog2e);
       out = (u32x2){pack_bf16(__builtin_fmaf(e, yt[0], acc[0]), __builtin_fmaf(e, yt[1], acc[1])),
                     pack_bf16(__builtin_fmaf(e, yt[2], acc[2]), __builtin_fmaf(e, yt[3], acc[3]))};
     };
@@ -440,7 +449,7 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
         f32x4 sacc = {};
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 bb = lds8(&sm.bt[16 * (k * NJK + j) + lr][32 * kk + 8 * lg]);
+          const bf16x8 bb = lds8(&sm.bt[cb][16 * (k * NJK + j) + lr][32 * kk + 8 * lg]);
           sacc = mfma(bb, xh[kk], sacc);
           sacc = mfma(bb, xl[kk], sacc);
         }
@@ -448,7 +457,11 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
         for (int r = 0; r < 4; ++r) Hs[j][r] = __builtin_fmaf(dec, Hs[j][r], sacc[r]);
       }
     }
-    __syncthreads();  // LDS free for the next chunk
+    // single staging buffers: LDS free for the next chunk.  Double buffers: the
+    // next chunk's phase A writes the other x^T, B^T and scalars, and M, x o w
+    // and the exchange are written only after its first barrier, which every
+    // wave reaches after finishing this chunk.
+    if constexpr (kSsdStageBufs<N> == 1) __syncthreads();
   }
   if (a.hT) {
 #pragma unroll
