@@ -9,6 +9,7 @@ shapes stay small enough for the oracle to finish in well under a second.
   segments.
 - Backward: the same families of options.
 - SSD and gated linear attention: state sizes, groups, heads and lengths.
+- conv1d + SiLU prologue: widths 1..4, carried state and bias on or off.
 The case's parameters are printed before it runs.
 """
 from __future__ import annotations
@@ -132,3 +133,28 @@ def test_random_gla(seed):
                         feature_map=fm)
     check("y", y.float().cpu().double().numpy(), yr, torch.bfloat16)
     check("hT", hT.cpu().double().numpy(), hr, torch.bfloat16)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_conv_prologue(seed):
+    g = np.random.default_rng([20261203, 80, seed])
+    dtype = torch.float32 if g.random() < 0.5 else torch.bfloat16
+    w = W[0] if dtype == torch.float32 else W[1]
+    bsz, L, dim, width = int(g.integers(1, 5)), int(g.integers(1, 600)), int(g.integers(1, 300)), int(g.integers(1, 5))
+    with_state, with_bias = bool(g.random() < 0.5), bool(g.random() < 0.7)
+    print(f"  seed={seed} {str(dtype)[6:]} B{bsz} L{L} D{dim} W{width} state={with_state} bias={with_bias}", flush=True)
+    x = workloads.make_inputs(w, batch=bsz, seqlen=L, dim=dim, seed_extra=(80, seed))["x"]
+    prm = workloads.make_conv_params(w, dim=dim, width=width, seed_extra=(80, seed))
+    bias = prm["bias"] if with_bias else None
+    state = None
+    if with_state:
+        prev = workloads.make_inputs(w, batch=bsz, seqlen=max(width - 1, 1), dim=dim, seed_extra=(80, seed, 1))["x"]
+        state = prev[:, :width - 1].contiguous()
+    dv = lambda t: None if t is None else t.to(DEV)
+    u, so = ssm.conv1d_silu(dv(x), dv(prm["weight"]), dv(bias), dv(state), return_state=True)
+    torch.cuda.synchronize()
+    ur, _, _ = oracle.conv1d_silu(x, prm["weight"], bias, state)
+    check("u", u.float().cpu().double().numpy(), ur, dtype)
+    # the carried state is the last W-1 input rows, earlier rows coming from `state`
+    full = torch.cat([state if state is not None else torch.zeros(bsz, width - 1, dim, dtype=dtype), x], dim=1)
+    assert torch.equal(so.cpu(), full[:, full.shape[1] - (width - 1):, :]), "state_out is not the last W-1 input rows"
