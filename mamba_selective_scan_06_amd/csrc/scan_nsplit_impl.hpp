@@ -1,14 +1,20 @@
 // NSPLIT family: the main forward scan on gfx950.
 //
-// Work decomposition.  A workgroup is 4 waves (256 lanes) and owns 64
+// Work decomposition.  A workgroup is 8 waves (512 lanes) and owns 64
 // consecutive channels d of one batch row b, over one time segment.  Lane l of
-// every wave stands for channel d0 + l; wave w holds the K = N/4 states
-// n = wK .. wK+K-1 of that channel in fp32 registers.  So the 16 states of a
-// channel at N = 16 live in 4 lanes of 4 different waves, and one workgroup
-// keeps 64 x N independent recurrence chains on chip for the whole segment.
-// This gives 4 waves per 64 channels (one per SIMD) instead of one, which the
-// channel count of a Mamba layer needs to fill 1024 SIMDs without splitting
-// time.
+// every wave stands for channel d0 + l.  The waves are specialised, and wave w
+// runs on SIMD w mod 4, so every SIMD holds one wave of each role:
+//   scan waves 0..3: wave w holds the K = N/4 states n = wK .. wK+K-1 of its
+//     channel in fp32 registers and advances them through every token (the 16
+//     states of a channel at N = 16 live in 4 lanes of 4 waves);
+//   owner waves 4..7: owner o does the per-(t, d) scalar work of the tokens
+//     j = o (mod 4) of each tile for all 64 channels: loading and widening x,
+//     delta and z, softplus, u = delta x, the decay terms, D x and SiLU(z).
+//     It publishes (decay terms, u) in LDS and, a tile later, adds the scan
+//     waves' partial readouts, D x and the gate, rounds once and stores y_t.
+// One workgroup keeps 64 x N independent recurrence chains on chip for the
+// whole segment, and 64 channels of a Mamba layer give 4 scan waves, one per
+// SIMD, which the channel count needs to fill 1024 SIMDs without splitting time.
 //
 // Per token and channel (page youngju.dev "Mamba 논문 리뷰"):
 //   delta = softplus(raw + bias)                       section 3.1
@@ -16,17 +22,12 @@
 //   h_n  <- Abar_n h_n + (delta x) B_t[n]              sections 2.2, 3.3 (Euler input term)
 //   y     = sum_n C_t[n] h_n + D[d] x, y *= SiLU(z)    sections 2.2, 3.4
 //
-// Time is walked in tiles of 16 tokens with three phases and two barriers:
-//   O  "owner" phase: token t of the tile is owned by wave (t mod 4), which
-//      does that token's per-(t, d) scalar work exactly once for the 64
-//      channels: widening, softplus, u = delta x, the decay terms, D x and
-//      SiLU(z).  It publishes (decay terms, u) to LDS.
-//   S  scan phase: every wave advances its K states through the 16 tokens,
-//      reading the shared per-token terms from LDS, and writes its partial
-//      readout sum_{n in wave} C_t[n] h_n to LDS.
-//   Y  the owner wave adds the 4 partial sums, D x, applies the gate, rounds
-//      once and stores y_t for its tokens.
-//
+// Time is walked in tiles of 16 tokens with one barrier per tile and the LDS
+// terms double-buffered: in iteration k the scan waves consume tile k (reading
+// its per-token terms, writing their partial readouts sum_{n in wave} C_t[n] h_n)
+// while the owners compute tile k+1's terms into the other buffer and finish
+// tile k-1 from the partials left there.
+
 // Memory.  All loads are raw buffer loads with the whole byte offset in the
 // VGPR offset (the part the range check covers), through a descriptor over one
 // batch row, so loads past the row end return 0 (prefetching past the end of
