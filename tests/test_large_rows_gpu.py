@@ -6,6 +6,11 @@ the row length.  These cases put rows past 2^31 and 2^32 bytes through it,
 unsplit and with forced time segments that start gigabytes into the row, and
 compare sampled channels (each a whole independent chain over every token)
 with the fp64 oracle.  Every y must also be finite.
+
+The backward cuts such rows into segments whose spans fit its 32-bit offsets.
+Its per-channel gradients (dx, ddelta, dz, dA, dD, ddelta_bias, dh0) are
+compared on sampled channels.  dB and dC are sums over every channel, out of
+the oracle's reach at this size, and are checked to be finite.
 """
 from __future__ import annotations
 
@@ -17,12 +22,15 @@ import torch
 
 import mamba_selective_scan_06_amd as ssm
 import workloads
+import oracle
 from tests.gpu_helpers import DEV, check, oracle_scan, sample_channels, select
 
 pytestmark = [
     pytest.mark.gpu,
     pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a HIP GPU"),
 ]
+
+TENS = ("x", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0")
 
 CASES = [
     # (workload index for dtype and recipe, B, L, D): D ragged against 64-channel
@@ -61,4 +69,32 @@ def test_rows_beyond_32bit_offsets(wi, bsz, L, dim):
         check(f"y splits={splits}", ys, yr, w.dtype)
         check(f"hT splits={splits}", hs, hr, w.dtype)
     del d, y, hT
+    torch.cuda.empty_cache()
+
+
+def test_backward_row_beyond_2gib():
+    w = workloads.WORKLOADS[1]
+    bsz, L, dim = 1, 262_152, 4104
+    inp = workloads.make_large_inputs(w, batch=bsz, seqlen=L, dim=dim)
+    inp["h0"] = torch.randn(bsz, dim, w.dstate, generator=torch.Generator().manual_seed(5)) * 0.5
+    cot = workloads.make_large_cotangents(w, batch=bsz, seqlen=L, dim=dim)
+    print(f"  backward B={bsz} L={L} D={dim} bf16: {L * dim * 2 / 2**30:.2f} GiB per row", flush=True)
+    chans = sample_channels(dim, k=8, seed=L + 1)
+    sub = select(inp, [0], chans)
+    ref = oracle.scan_bwd(*(sub.get(k) for k in TENS), dy=cot["dy"].index_select(2, torch.as_tensor(chans)),
+                          dhT=cot["dhT"].index_select(1, torch.as_tensor(chans)))
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    dy, dhT = cot["dy"].to(DEV), cot["dhT"].to(DEV)
+    del inp, cot
+    gc.collect()
+    g = ssm.scan_bwd(*(d.get(k) for k in TENS), dy=dy, dhT=dhT)
+    torch.cuda.synchronize()
+    ci = torch.as_tensor(chans, device=DEV)
+    per_channel = {"x": 2, "delta": 2, "z": 2, "A": 0, "D": 0, "delta_bias": 0, "h0": 1}
+    for k, axis in per_channel.items():
+        got = g[k].index_select(axis, ci).float().cpu().double().numpy()
+        check("d" + k, got, ref[k], w.dtype)
+    for k in ("B", "C"):
+        assert bool(torch.isfinite(g[k]).all()), f"d{k} has non-finite entries"
+    del d, dy, dhT, g
     torch.cuda.empty_cache()

@@ -158,6 +158,20 @@ def make_large_inputs(w: Workload, *, batch: int, seqlen: int, dim: int, seed_ex
     return out
 
 
+def make_large_cotangents(w: Workload, *, batch: int, seqlen: int, dim: int, seed_extra=(), rows_per_draw=8192):
+    """make_cotangents' recipe (dy, dhT ~ N(0, 1)) for inputs of several GiB, drawn
+    like make_large_inputs by torch's CPU generator in blocks of tokens."""
+    ss = np.random.SeedSequence([ROOT_SEED, int(w.index), 2000, *[int(e) for e in seed_extra], 1])
+    gens = [torch.Generator().manual_seed(int(c.generate_state(1, dtype=np.uint64)[0] >> np.uint64(1)))
+            for c in ss.spawn(2)]
+    dy = torch.empty((batch, seqlen, dim), dtype=w.dtype)
+    for b in range(batch):
+        for t0 in range(0, seqlen, rows_per_draw):
+            rows = min(rows_per_draw, seqlen - t0)
+            dy[b, t0:t0 + rows] = torch.randn((rows, dim), generator=gens[0], dtype=torch.float32).to(w.dtype)
+    return {"dy": dy, "dhT": torch.randn((batch, dim, w.dstate), generator=gens[1], dtype=torch.float32)}
+
+
 def make_decode_step(w: Workload, step: int, *, batch: int | None = None, dim: int | None = None):
     """Fresh per-step tensors (x, delta, B, C, z) of a decode workload, L = 1."""
     bsz = batch or w.batch
