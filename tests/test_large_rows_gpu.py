@@ -7,6 +7,10 @@ unsplit and with forced time segments that start gigabytes into the row, and
 compare sampled channels (each a whole independent chain over every token)
 with the fp64 oracle.  Every y must also be finite.
 
+The SSD layer's x and y pass 2 GiB per batch row at L = 262208 (64 heads of
+64 channels); three sampled heads are compared, since the heads of a group are
+independent given the shared B and C.
+
 The backward cuts such rows into segments whose spans fit its 32-bit offsets.
 Its per-channel gradients (dx, ddelta, dz, dA, dD, ddelta_bias, dh0) are
 compared on sampled channels.  dB and dC are sums over every channel, out of
@@ -97,4 +101,29 @@ def test_backward_row_beyond_2gib():
     for k in ("B", "C"):
         assert bool(torch.isfinite(g[k]).all()), f"d{k} has non-finite entries"
     del d, dy, dhT, g
+    torch.cuda.empty_cache()
+
+
+def test_ssd_sequence_beyond_2gib():
+    w = workloads.SSD_WORKLOADS[1]
+    L = 262_208
+    inp = workloads.make_ssd_inputs(w, batch=1, seqlen=L, with_h0=True, seed_extra=(9,))
+    print(f"  SSD B=1 L={L} H={w.nheads} P={w.headdim} N={w.dstate}: "
+          f"{inp['x'].numel() * 2 / 2**30:.2f} GiB of x per row", flush=True)
+    heads = [0, 37, w.nheads - 1]
+    hi = torch.as_tensor(heads)
+    sub = {"x": inp["x"].index_select(2, hi), "dt": inp["dt"].index_select(2, hi), "A": inp["A"][hi],
+           "B": inp["B"], "C": inp["C"], "D": inp["D"][hi], "dt_bias": inp["dt_bias"][hi],
+           "h0": inp["h0"].index_select(1, hi)}
+    yr, hr = oracle.ssd(*(sub[k] for k in ("x", "dt", "A", "B", "C")), D=sub["D"], dt_bias=sub["dt_bias"],
+                        s0=sub["h0"])
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    del inp
+    gc.collect()
+    y, hT = ssm.ssd_fwd(*(d[k] for k in ("x", "dt", "A", "B", "C", "D", "dt_bias", "h0")), return_final_state=True)
+    torch.cuda.synchronize()
+    hd = hi.to(DEV)
+    check("y", y.index_select(2, hd).float().cpu().double().numpy(), yr, torch.bfloat16)
+    check("hT", hT.index_select(1, hd).cpu().double().numpy(), hr, torch.bfloat16)
+    del d, y, hT
     torch.cuda.empty_cache()
