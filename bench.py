@@ -490,10 +490,14 @@ def bench_gla(args, ssm, torch):
     ys = [torch.empty_like(vs[0]) for _ in vs]
     hT = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    # the feature map's once-per-call pass needs a workspace; allocated here, outside the timed region
+    nws = ssm.gla_workspace_bytes(ssm.make_gla_args(d["q"], d["k"], vs[0], d["log_f"], d["in_gate"], None, hT,
+                                                    ys[0], w.feature_map))
+    ws = torch.empty(max(nws, 0), dtype=torch.uint8, device=dev)
 
     def step(i):
         ssm.gla_fwd(d["q"], d["k"], vs[i % 2], d["log_f"], d["in_gate"], None, feature_map=w.feature_map,
-                    out=ys[i % 2], final_state_out=hT)
+                    out=ys[i % 2], final_state_out=hT, workspace=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -524,7 +528,8 @@ def bench_gla(args, ssm, torch):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
                    "headdim": w.headdim, "ngroups": w.ngroups, "dstate": w.dstate, "gated": w.gated,
-                   "feature_map": "elu+1" if w.feature_map else None, "chunk": Q},
+                   "feature_map": "elu+1" if w.feature_map else None, "chunk": Q,
+                   **({"feature_map_pass": "once per call, into the workspace"} if w.feature_map else {})},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 1
+#define SSM_SCAN_ABI_VERSION 2
 
 /* Element type of x, delta, B, C, z and y.  A, D, delta_bias, h0, hT are
  * always fp32, and all arithmetic (state, accumulation) is fp32. */
@@ -266,7 +266,11 @@ int ssm_ssd_fwd(const ssm_ssd_args *args, void *stream);
  * forget gate in (0, 1]); larger values can overflow fp32.
  * Layouts: q, k (B, L, G, N); v, y (B, L, H, P) in bf16; log_f, in_gate
  * (B, L, H) and the state S0 / ST (B, H, P, N) fp32.  feature_map = 1 rounds
- * phi(q) and phi(k) to bf16 before the products.
+ * phi(q) and phi(k) to bf16 before the products.  With feature_map = 1 and a
+ * workspace of ssm_gla_workspace_bytes bytes, phi is applied once per call, by
+ * an elementwise pass that writes phi(k) and phi(q) to the workspace; without
+ * one (NULL or too small) every head's workgroup applies it to its group's
+ * keys and queries again.  Both give bitwise the same results.
  * Limits of this version: dtype SSM_DTYPE_BF16, headdim P = 64,
  * dstate N in {64, 128, 256} (SSM_ERR_VARIANT otherwise). */
 typedef struct ssm_gla_args {
@@ -283,12 +287,20 @@ typedef struct ssm_gla_args {
   const float *h0;            /* (B, H, P, N) initial state or NULL (zeros)            */
   float *hT;                  /* (B, H, P, N) final state out or NULL                  */
   void *y;                    /* (B, L, H, P) out                            required */
+  void *workspace;            /* device scratch for phi(k), phi(q), or NULL; 16-byte
+                                 aligned, overwritten, must not overlap any tensor  */
+  int64_t workspace_bytes;    /* its size in bytes                                     */
 } ssm_gla_args;
 
 /* Errors as for ssm_ssd_fwd (SSM_ERR_VARIANT also for feature_map outside
  * {0, 1}); y and hT must not overlap any input or each other.  With L == 0,
  * hT receives h0 (or zeros). */
 int ssm_gla_fwd(const ssm_gla_args *args, void *stream);
+
+/* Bytes of workspace ssm_gla_fwd uses to apply the feature map once per call
+ * (0 without a feature map).  Host-only; negative SSM_ERR_* for invalid
+ * arguments (the workspace fields are not checked here). */
+int64_t ssm_gla_workspace_bytes(const ssm_gla_args *args);
 
 /* Static, human-readable text for a status code. */
 const char *ssm_scan_strerror(int code);

@@ -34,7 +34,7 @@ FLAG_ZOH = 2
 # Exported symbols the header declares (checked by the tests).
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_scan_bwd",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd_plan", "ssm_conv1d_silu_fwd", "ssm_ssd_fwd",
-           "ssm_gla_fwd", "ssm_scan_strerror", "ssm_scan_abi_version")
+           "ssm_gla_fwd", "ssm_gla_workspace_bytes", "ssm_scan_strerror", "ssm_scan_abi_version")
 
 
 class ScanArgs(ctypes.Structure):
@@ -99,6 +99,7 @@ class GlaArgs(ctypes.Structure):
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("log_f", ctypes.c_void_p), ("in_gate", ctypes.c_void_p),
         ("h0", ctypes.c_void_p), ("hT", ctypes.c_void_p), ("y", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -135,13 +136,15 @@ def lib() -> ctypes.CDLL:
         L.ssm_ssd_fwd.restype = ctypes.c_int
         L.ssm_gla_fwd.argtypes = [ctypes.POINTER(GlaArgs), ctypes.c_void_p]
         L.ssm_gla_fwd.restype = ctypes.c_int
+        L.ssm_gla_workspace_bytes.argtypes = [ctypes.POINTER(GlaArgs)]
+        L.ssm_gla_workspace_bytes.restype = ctypes.c_int64
         L.ssm_conv1d_silu_fwd.argtypes = [ctypes.POINTER(ConvArgs), ctypes.c_void_p]
         L.ssm_conv1d_silu_fwd.restype = ctypes.c_int
         L.ssm_scan_strerror.argtypes = [ctypes.c_int]
         L.ssm_scan_strerror.restype = ctypes.c_char_p
         L.ssm_scan_abi_version.argtypes = []
         L.ssm_scan_abi_version.restype = ctypes.c_int
-        if L.ssm_scan_abi_version() != 1:
+        if L.ssm_scan_abi_version() != 2:
             raise RuntimeError("libssm_scan ABI version mismatch")
         _lib = L
     return _lib
@@ -459,13 +462,22 @@ def make_gla_args(q, k, v, log_f=None, in_gate=None, h0=None, hT=None, y=None, f
     return a
 
 
+def gla_workspace_bytes(args: GlaArgs) -> int:
+    """Bytes of workspace ssm_gla_fwd uses to apply the feature map once per call."""
+    r = lib().ssm_gla_workspace_bytes(ctypes.byref(args))
+    if r < 0:
+        raise RuntimeError(f"ssm_gla_workspace_bytes: {strerror(int(r))}")
+    return int(r)
+
+
 def gla_fwd(q, k, v, log_f=None, in_gate=None, h0=None, *, feature_map=False, return_final_state=False, out=None,
-            final_state_out=None):
+            final_state_out=None, workspace=None):
     """Gated linear attention / mLSTM matrix-state recurrence on the GPU:
     S_t = exp(log_f) S_{t-1} + in_gate v_t phi(k_t)^T, y_t = S_t phi(q_t), phi the
     identity or elu + 1 (feature_map=True).  Returns y, or (y, hT) with
-    return_final_state=True.  Launches on torch's current HIP stream and does
-    not synchronise."""
+    return_final_state=True.  With the feature map, a workspace (allocated here
+    when None; an empty tensor declines it) lets the library apply phi once per
+    call.  Launches on torch's current HIP stream and does not synchronise."""
     if not v.is_cuda:
         raise ValueError("gla_fwd runs on the GPU only: move the tensors to a HIP device")
     L_ = lib()
@@ -474,6 +486,15 @@ def gla_fwd(q, k, v, log_f=None, in_gate=None, h0=None, *, feature_map=False, re
     if hT is None and return_final_state:
         hT = torch.empty((v.shape[0], v.shape[2], v.shape[3], k.shape[3]), dtype=torch.float32, device=v.device)
     args = make_gla_args(q, k, v, log_f, in_gate, h0, hT, y, feature_map)
+    if workspace is None:
+        nbytes = L_.ssm_gla_workspace_bytes(ctypes.byref(args))
+        if nbytes < 0:
+            raise RuntimeError(f"ssm_gla_fwd: {strerror(int(nbytes))}")
+        if nbytes > 0:
+            workspace = torch.empty(int(nbytes), dtype=torch.uint8, device=v.device)
+    if workspace is not None and workspace.numel() > 0:
+        args.workspace = _ptr(workspace)
+        args.workspace_bytes = workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(v.device).cuda_stream
     rc = L_.ssm_gla_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
     if rc != 0:
@@ -483,5 +504,5 @@ def gla_fwd(q, k, v, log_f=None, in_gate=None, h0=None, *, feature_map=False, re
     return y
 
 
-__all__ = ["scan_fwd", "scan_bwd", "conv1d_silu", "ssd_fwd", "gla_fwd", "make_gla_args", "GlaArgs", "make_ssd_args", "SsdArgs", "make_conv_args", "ConvArgs", "make_args", "make_bwd_args", "plan", "bwd_plan", "workspace_bytes",
+__all__ = ["scan_fwd", "scan_bwd", "conv1d_silu", "ssd_fwd", "gla_fwd", "make_gla_args", "GlaArgs", "gla_workspace_bytes", "make_ssd_args", "SsdArgs", "make_conv_args", "ConvArgs", "make_args", "make_bwd_args", "plan", "bwd_plan", "workspace_bytes",
            "bwd_workspace_bytes", "lib", "strerror", "ScanArgs", "ScanBwdArgs", "EXPORTS"]

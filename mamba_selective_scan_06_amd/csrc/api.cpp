@@ -308,7 +308,11 @@ int validate_ssd(const ssm_ssd_args* a) {
 
 // ---- gated linear attention / mLSTM ------------------------------------------------------
 
-int validate_gla(const ssm_gla_args* a) {
+// Workspace bytes for phi(k) and phi(q): each (B, L, G, N) bf16, the second
+// starting at a 256-byte boundary.
+int64_t gla_ws_part(const ssm_gla_args* a) { return round_up(a->batch * a->seqlen * a->ngroups * a->dstate * 2, 256); }
+
+int validate_gla(const ssm_gla_args* a, bool check_workspace = true) {
   if (!a) return SSM_ERR_NULL;
   if (a->batch < 0 || a->seqlen < 0 || a->nheads < 1 || a->headdim < 1 || a->ngroups < 1 || a->dstate < 1)
     return SSM_ERR_SHAPE;
@@ -333,6 +337,13 @@ int validate_gla(const ssm_gla_args* a) {
     if (overlaps(a->hT, st * 4, ins[i], insz[i])) return SSM_ERR_ALIAS;
   }
   if (overlaps(a->hT, st * 4, a->y, ve * 2)) return SSM_ERR_ALIAS;
+  if (check_workspace && a->workspace) {
+    if (!aligned16(a->workspace) || a->workspace_bytes < 0) return SSM_ERR_ALIGN;
+    const int64_t wb = a->workspace_bytes;
+    for (int i = 0; i < 6; ++i)
+      if (overlaps(a->workspace, wb, ins[i], insz[i])) return SSM_ERR_ALIAS;
+    if (overlaps(a->workspace, wb, a->y, ve * 2) || overlaps(a->workspace, wb, a->hT, st * 4)) return SSM_ERR_ALIAS;
+  }
   return SSM_OK;
 }
 
@@ -580,6 +591,21 @@ int ssm_gla_fwd(const ssm_gla_args* a, void* stream) {
   const int rc = validate_gla(a);
   if (rc != SSM_OK) return rc;
   if (a->batch == 0) return SSM_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // feature map applied once per call into the workspace when one is given
+  const int64_t part = gla_ws_part(a);
+  const bool prepass = a->feature_map == 1 && a->seqlen > 0 && a->workspace && a->workspace_bytes >= 2 * part;
+  const void* keys = a->k;
+  const void* queries = a->q;
+  if (prepass) {
+    void* pk = a->workspace;
+    void* pq = static_cast<char*>(a->workspace) + part;
+    const int64_t n = a->batch * a->seqlen * a->ngroups * a->dstate;
+    const hipError_t fe = ssm::launch_gla_feature_map(a->k, a->q, pk, pq, n, s);
+    if (fe != hipSuccess) return SSM_ERR_LAUNCH;
+    keys = pk;
+    queries = pq;
+  }
   ssm::SsdProblem p;
   p.batch = a->batch;
   p.seqlen = a->seqlen;
@@ -587,12 +613,12 @@ int ssm_gla_fwd(const ssm_gla_args* a, void* stream) {
   p.headdim = a->headdim;
   p.ngroups = a->ngroups;
   p.dstate = a->dstate;
-  p.mode = 1 + a->feature_map;
+  p.mode = prepass ? 1 : 1 + a->feature_map;
   p.x = a->v;  // values play the role of x, keys of B, queries of C
   p.dt = nullptr;
   p.A = nullptr;
-  p.B = a->k;
-  p.C = a->q;
+  p.B = keys;
+  p.C = queries;
   p.D = nullptr;
   p.dt_bias = nullptr;
   p.log_f = a->log_f;
@@ -600,8 +626,14 @@ int ssm_gla_fwd(const ssm_gla_args* a, void* stream) {
   p.h0 = a->h0;
   p.hT = a->hT;
   p.y = a->y;
-  const hipError_t e = ssm::launch_ssd(p, static_cast<hipStream_t>(stream));
+  const hipError_t e = ssm::launch_ssd(p, s);
   return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
+}
+
+int64_t ssm_gla_workspace_bytes(const ssm_gla_args* a) {
+  const int rc = validate_gla(a, false);
+  if (rc != SSM_OK) return rc;
+  return a->feature_map == 1 && a->batch > 0 && a->seqlen > 0 ? 2 * gla_ws_part(a) : 0;
 }
 
 }  // extern "C"

@@ -150,5 +150,9 @@ struct SsdProblem {
 };
 
 hipError_t launch_ssd(const SsdProblem& p, hipStream_t stream);
+// phi(u) = elu(u) + 1 of n bf16 keys and n bf16 queries (n a multiple of 8,
+// all four buffers 16-byte aligned), rounded to bf16 as the SSD kernel's own
+// feature map rounds them.
+hipError_t launch_gla_feature_map(const void* k, const void* q, void* pk, void* pq, int64_t n, hipStream_t stream);
 
 }  // namespace ssm

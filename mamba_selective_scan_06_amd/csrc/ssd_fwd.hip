@@ -503,7 +503,31 @@ hipError_t launch_ssd_m(const SsdProblem& p, hipStream_t stream) {
   }
 }
 
+// The feature map once per call: 8 bf16 per thread, the same arithmetic and
+// rounding as feature_map() in the kernel's staging.
+__global__ __launch_bounds__(256) void gla_feature_map_kernel(const uint4* __restrict__ k, const uint4* __restrict__ q,
+                                                               uint4* __restrict__ pk, uint4* __restrict__ pq,
+                                                               int64_t n8) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const uint4 a = k[i], b = q[i];
+  uint32_t va[4] = {a.x, a.y, a.z, a.w}, vb[4] = {b.x, b.y, b.z, b.w};
+  feature_map(va);
+  feature_map(vb);
+  pk[i] = make_uint4(va[0], va[1], va[2], va[3]);
+  pq[i] = make_uint4(vb[0], vb[1], vb[2], vb[3]);
+}
+
 }  // namespace
+
+hipError_t launch_gla_feature_map(const void* k, const void* q, void* pk, void* pq, int64_t n, hipStream_t stream) {
+  const int64_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  hipLaunchKernelGGL(gla_feature_map_kernel, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const uint4*>(k), static_cast<const uint4*>(q), static_cast<uint4*>(pk),
+                     static_cast<uint4*>(pq), n8);
+  return hipGetLastError();
+}
 
 hipError_t launch_ssd(const SsdProblem& p, hipStream_t stream) {
   switch (p.mode) {

@@ -38,7 +38,7 @@ def test_library_loads_and_exports_header_symbols():
     assert set(declared) == set(ssm.EXPORTS), declared
     for name in declared:
         assert hasattr(L, name), f"{name} not exported"
-    assert L.ssm_scan_abi_version() == 1
+    assert L.ssm_scan_abi_version() == 2
 
 
 def test_strerror_covers_codes():

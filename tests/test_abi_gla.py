@@ -62,3 +62,28 @@ def test_aliasing_rejected():
 def test_null_args_and_empty_batch():
     assert ssm.lib().ssm_gla_fwd(None, None) == -1
     assert _gla(_args(shape=(0, 64, 8, 64, 2, 128))) == 0
+
+
+def _ws_bytes(a):
+    return ssm.lib().ssm_gla_workspace_bytes(ctypes.byref(a))
+
+
+def test_workspace_query():
+    """phi(k) and phi(q), each (B, L, G, N) bf16 rounded up to 256 bytes; none
+    without the feature map or with nothing to do."""
+    assert _ws_bytes(_args()) == 0
+    n = 2 * 64 * 2 * 128 * 2
+    assert _ws_bytes(_args(feature_map=1)) == 2 * ((n + 255) // 256 * 256)
+    assert _ws_bytes(_args(feature_map=1, shape=(2, 0, 8, 64, 2, 128))) == 0
+    assert _ws_bytes(_args(feature_map=2)) == -9
+
+
+def test_workspace_checked_on_host():
+    far = FAKE + (40 << 32)
+    big = 1 << 20
+    # misaligned workspace
+    assert _gla(_args(feature_map=1, workspace=far + 8, workspace_bytes=big)) == -5
+    # a workspace overlapping an input or an output
+    assert _gla(_args(feature_map=1, workspace=FAKE + (2 << 32), workspace_bytes=big)) == -6   # v
+    assert _gla(_args(feature_map=1, workspace=FAKE + (7 << 32), workspace_bytes=big)) == -6   # y
+    assert _gla(_args(feature_map=1, workspace=FAKE - 256, workspace_bytes=big)) == -6         # q

@@ -136,3 +136,21 @@ def test_gla_full_size_sampled_heads(wi):
         yr, hr = oracle_gla(sub, w.feature_map)
         check(f"y head {hsel}", y[:, :, hsel:hsel + 1], yr, torch.bfloat16)
         check(f"hT head {hsel}", hT[:, hsel:hsel + 1], hr, torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", [dict(dstate=64, ngroups=2, seqlen=200), dict(dstate=256, ngroups=1, seqlen=130),
+                                  dict(dstate=128, ngroups=4, seqlen=1)], ids=["N64-G2", "N256-G1", "N128-L1"])
+def test_feature_map_pass_matches_in_kernel_map(case):
+    """phi applied once per call into the workspace, or by every head's
+    workgroup in its staging: bitwise the same y and state."""
+    inp = workloads.make_gla_inputs(GW[0], gated=True, with_h0=True, **case)
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    args = [d[k] for k in TENS]
+    y1, h1 = ssm.gla_fwd(*args, feature_map=True, return_final_state=True)  # workspace: the pass
+    y2, h2 = ssm.gla_fwd(*args, feature_map=True, return_final_state=True,
+                         workspace=torch.empty(0, dtype=torch.uint8, device=DEV))  # declined: in the kernel
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    yr, hr = oracle_gla(inp, True)
+    check("y", y1.float().cpu().double().numpy(), yr, torch.bfloat16)
+    check("hT", h1.cpu().double().numpy(), hr, torch.bfloat16)
