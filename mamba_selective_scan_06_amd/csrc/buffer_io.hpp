@@ -28,13 +28,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buf(const void* base, uin
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRawBufferFlags);
 }
 
+// Cache-policy operand of the buffer intrinsics that sets the non-temporal
+// bit (`nt`) on gfx950: the token tensors these helpers move (x, delta, z in,
+// y out) are touched once, so they stream past the caches (1% faster on the
+// forward scan).
+constexpr int kStreamPolicy = 2;
+
 // One element's raw bits (bf16 zero-extended, or fp32) at byte offset `off`.
 template <typename S>
 __device__ __forceinline__ uint32_t load_bits(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   if constexpr (sizeof(S) == 4)
-    return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, kStreamPolicy);
   else
-    return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, kStreamPolicy);
 }
 
 template <typename S>
@@ -47,10 +53,10 @@ __device__ __forceinline__ float bits_to_f32(uint32_t v) {
 template <typename S>
 __device__ __forceinline__ void store_val(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
   if constexpr (sizeof(S) == 4) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(off), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(off), 0, kStreamPolicy);
   } else {
     __hip_bfloat16 hb = __float2bfloat16(v);
-    __builtin_amdgcn_raw_buffer_store_b16(__bfloat16_as_ushort(hb), r, static_cast<int>(off), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(__bfloat16_as_ushort(hb), r, static_cast<int>(off), 0, kStreamPolicy);
   }
 }
 
