@@ -31,11 +31,12 @@ __device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float out[4])
 }
 
 #ifndef SSM_DECODE_ROWS
-#define SSM_DECODE_ROWS 2
+#define SSM_DECODE_ROWS 1
 #endif
-// Batch rows per thread: every thread keeps R independent state float4 loads
-// in flight (the step is bound by that traffic), with the row's scalar loads
-// issued first.
+// Batch rows per thread (R): with R > 1 every thread keeps R independent state
+// loads in flight.  With the state's non-temporal loads, one row per thread
+// (more threads) measured fastest: 34.2-34.4 us per step against 35.4-35.6
+// for two rows and 36.6 for four.
 constexpr int kDecodeRows = SSM_DECODE_ROWS;
 
 // The state is streamed: read once and written once per step, so its accesses
