@@ -53,7 +53,8 @@ enum ssm_status {
 /* Kernel family (SSM_VARIANT_AUTO picks one from the problem shape). */
 enum ssm_variant {
   SSM_VARIANT_AUTO = 0,
-  SSM_VARIANT_NSPLIT = 1, /* 4 waves share 64 channels, each wave owns N/4 states (N % 4 == 0) */
+  SSM_VARIANT_NSPLIT = 1, /* 8 waves share 64 channels: 4 hold N/4 states each, 4 do the per-token
+                             work (N in {4, 8, 16, 32, 64}; time splitting)                      */
   SSM_VARIANT_LANE = 2,   /* one lane owns one channel and all N states; any N <= 64           */
   SSM_VARIANT_DECODE = 3, /* seqlen == 1 only: N/4 lanes per channel (N % 4 == 0)              */
 };
@@ -132,9 +133,9 @@ int64_t ssm_scan_plan(const ssm_scan_args *args);
  * inputs that were not given (D, z, delta_bias, h0 NULL) are those of a zero
  * input: dz needs z, the others are still defined.
  *
- * Limits of this version: dstate N in 1..16 (SSM_ERR_DSTATE otherwise). */
+ * Limits of this version: dstate N in 1..64 (SSM_ERR_DSTATE otherwise). */
 typedef struct ssm_scan_bwd_args {
-  int64_t batch, seqlen, dim, dstate; /* as ssm_scan_args; N <= 16           */
+  int64_t batch, seqlen, dim, dstate; /* as ssm_scan_args; N <= 64           */
   int32_t dtype;                      /* ssm_dtype of x, delta, B, C, z, dy and the (B, L, .) gradients */
   int32_t flags;                      /* ssm_flags: SSM_FLAG_GENERIC_A as for the forward */
   const void *x;           /* (B, L, D)                                        required */

@@ -387,7 +387,7 @@ const char* ssm_scan_strerror(int code) {
     case SSM_OK: return "success";
     case SSM_ERR_NULL: return "a required pointer is NULL (or dz given without z)";
     case SSM_ERR_SHAPE: return "invalid shape (negative extent, batch > 65535, or size overflow)";
-    case SSM_ERR_DSTATE: return "dstate out of range (1..64 forward, 1..16 backward)";
+    case SSM_ERR_DSTATE: return "dstate out of range (1..64)";
     case SSM_ERR_DTYPE: return "dtype must be SSM_DTYPE_F32 or SSM_DTYPE_BF16";
     case SSM_ERR_ALIGN: return "every tensor base address must be 16-byte aligned";
     case SSM_ERR_ALIAS: return "an output overlaps an input or another output (hT may equal h0)";
