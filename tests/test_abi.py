@@ -103,7 +103,7 @@ def test_empty_problems_are_noops():
 
 def test_plan_and_workspace_queries():
     lib = ssm.lib()
-    # the benchmark layer: 64 channel blocks x 4 batch rows x 4 waves fills the GPU unsplit
+    # the benchmark layer: 64 channel blocks x 4 batch rows = 256 blocks, one per compute unit, unsplit
     a = _args(shape=(4, 8192, 4096, 16))
     assert ssm.plan(a) == ("nsplit", 1)
     assert lib.ssm_scan_workspace_bytes(ctypes.byref(a)) == 0
