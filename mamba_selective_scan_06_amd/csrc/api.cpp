@@ -135,13 +135,18 @@ int make_plan(const ssm_scan_args* a, bool have_workspace_info, Plan* pl) {
     } else if (a->time_splits == 0 && !in_place) {
       // One 8-wave block runs per compute unit at a time.  Splitting costs an
       // extra state-only pass over all but the last segment, and pays only while
-      // every segment's block still finds a compute unit of its own: double the
-      // segments while blocks x segments fits the 256 compute units, keeping
-      // segments at least 256 tokens long.  (B8 L2048 D1536, 192 blocks, ran
-      // 25% slower with 2 segments than with 1: the second round of blocks.)
+      // every segment's block still finds a compute unit of its own: take the
+      // most segments for which blocks x segments fits the 256 compute units,
+      // keeping segments at least 256 tokens long.  (B8 L2048 D1536, 192 blocks,
+      // ran 25% slower with 2 segments than with 1: the second round of blocks.
+      // B1 L8192 D1536, 24 blocks: 10 segments 97 us, 8 segments 110 us, 12
+      // segments 138 us.)
       constexpr int64_t kComputeUnits = 256;
       const int64_t blocks = ((a->dim + 63) / 64) * a->batch;
-      while (blocks * splits * 2 <= kComputeUnits && L / (2 * splits) >= 256 && splits < 64) splits *= 2;
+      int64_t fit = kComputeUnits / blocks;
+      if (fit > L / 256) fit = L / 256;
+      if (fit > 64) fit = 64;
+      if (fit > 1) splits = static_cast<int>(fit);
     }
   }
   int64_t seg_len = L;

@@ -114,7 +114,7 @@ def test_plan_and_workspace_queries():
     assert ssm.plan(a) == ("nsplit", 1)  # no workspace: runs unsplit
     a.workspace, a.workspace_bytes = FAKE + (64 << 32), nbytes
     v, s = ssm.plan(a)
-    assert v == "nsplit" and s == 8  # 24 blocks x 8 segments fill the 256 compute units
+    assert v == "nsplit" and s == 10  # 24 blocks x 10 segments: the most that fit the 256 compute units
     # 192 blocks: a second segment would need a second round of blocks, so none
     b = _args(shape=(8, 2048, 1536, 16))
     b.workspace, b.workspace_bytes = FAKE + (64 << 32), 1 << 30
