@@ -76,6 +76,33 @@ def test_rows_beyond_32bit_offsets(wi, bsz, L, dim):
     torch.cuda.empty_cache()
 
 
+def test_row_beyond_2gib_zoh_generic_decays():
+    """The windowed instantiation with the zero-order hold and every decay its
+    own exp (random decay rates, generic path forced), unsplit and in 3 segments."""
+    w = workloads.WORKLOADS[1]
+    bsz, L, dim = 1, 262_152, 4104
+    inp = workloads.make_large_inputs(w, batch=bsz, seqlen=L, dim=dim, seed_extra=(3,))
+    inp["A"] = -torch.rand(dim, w.dstate, generator=torch.Generator().manual_seed(3)) * 3 - 0.05
+    inp["h0"] = torch.randn(bsz, dim, w.dstate, generator=torch.Generator().manual_seed(4)) * 0.5
+    print(f"  ZOH, generic decays: B={bsz} L={L} D={dim} bf16", flush=True)
+    chans = sample_channels(dim, k=8, seed=L + 2)
+    yr, hr = oracle.scan(*(select(inp, [0], chans).get(k) for k in TENS), zoh=True)
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    del inp
+    gc.collect()
+    ci = torch.as_tensor(chans, device=DEV)
+    for splits in (0, 3):
+        y, hT = ssm.scan_fwd(*(d.get(k) for k in TENS), return_final_state=True, zoh=True, generic_a=True,
+                             time_splits=splits)
+        torch.cuda.synchronize()
+        print(f"  time_splits={splits}", flush=True)
+        check(f"y splits={splits}", y.index_select(2, ci).float().cpu().double().numpy(), yr, w.dtype)
+        check(f"hT splits={splits}", hT.index_select(1, ci).cpu().double().numpy(), hr, w.dtype)
+        del y, hT
+    del d
+    torch.cuda.empty_cache()
+
+
 def test_backward_row_beyond_2gib():
     w = workloads.WORKLOADS[1]
     bsz, L, dim = 1, 262_152, 4104
