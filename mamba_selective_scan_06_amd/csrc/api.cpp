@@ -37,10 +37,10 @@ bool nsplit_ok(int64_t n) { return n == 4 || n == 8 || n == 16 || n == 32 || n =
 
 // The NSPLIT kernels count tokens in 32 bits and address a batch row through
 // buffer descriptors with 32-bit byte offsets.  A row whose accesses (up to
-// 144 tokens past its end, for the prefetch) fit one 2 GiB descriptor uses
+// 288 tokens past its end, for the prefetch) fit one 2 GiB descriptor uses
 // fixed descriptors; a longer row is addressed through windows that move along
-// it, with offsets under 144 tokens from the window start.  So a token of a
-// row must stay below 2 GiB / 144 (D up to about 7.4 million bf16 channels);
+// it, with offsets under 288 tokens from the window start.  So a token of a
+// row must stay below 2 GiB / 288 (D up to about 3.7 million bf16 channels);
 // the row length itself is free.
 int64_t nsplit_token_bytes(const ssm_scan_args* a) {
   const int64_t es = a->dtype == SSM_DTYPE_F32 ? 4 : 2;
@@ -49,10 +49,10 @@ int64_t nsplit_token_bytes(const ssm_scan_args* a) {
 bool nsplit_fits(const ssm_scan_args* a) {
   const int64_t lim = (int64_t{1} << 31) - 1;
   const int64_t tok = nsplit_token_bytes(a);
-  return tok > 0 && tok <= lim / 144 && a->seqlen <= lim - 1024;
+  return tok > 0 && tok <= lim / ssm::kNsplitReach && a->seqlen <= lim - 1024;
 }
 bool nsplit_windowed(const ssm_scan_args* a) {
-  return (a->seqlen + 144) * nsplit_token_bytes(a) > (int64_t{1} << 31) - 1;
+  return (a->seqlen + ssm::kNsplitReach) * nsplit_token_bytes(a) > (int64_t{1} << 31) - 1;
 }
 
 struct Plan {
@@ -128,7 +128,9 @@ int make_plan(const ssm_scan_args* a, bool have_workspace_info, Plan* pl) {
 
   int splits = 1;
   const bool in_place = a->h0 && a->hT && a->h0 == a->hT;
-  if (variant == SSM_VARIANT_NSPLIT && L > 0) {
+  // no chain (batch or dim 0): nothing runs, one segment and no workspace
+  const bool has_chains = a->batch > 0 && a->dim > 0;
+  if (variant == SSM_VARIANT_NSPLIT && L > 0 && has_chains) {
     if (a->time_splits > 1) {
       if (in_place) return SSM_ERR_VARIANT;  // later segments read h0 after the last one wrote hT
       splits = a->time_splits;
@@ -151,7 +153,10 @@ int make_plan(const ssm_scan_args* a, bool have_workspace_info, Plan* pl) {
   }
   int64_t seg_len = L;
   if (variant == SSM_VARIANT_NSPLIT && splits > 1) {
-    seg_len = round_up((L + splits - 1) / splits, ssm::kNsplitTile);
+    // an explicit split count is honoured (segments of whole tiles); automatic
+    // splitting uses segments of whole half turns, which waste no padded tiles
+    const int64_t unit = a->time_splits > 1 ? ssm::kNsplitTile : ssm::kNsplitTile * ssm::kNsplitTurn / 2;
+    seg_len = round_up((L + splits - 1) / splits, unit);
     splits = static_cast<int>((L + seg_len - 1) / seg_len);
   }
   pl->variant = variant;

@@ -35,6 +35,12 @@ constexpr int kFlagZoh = 2;
 
 // Tile length (timesteps) of the NSPLIT family; segment lengths are multiples of it.
 constexpr int kNsplitTile = 16;
+// Tokens past the current position (the end of a row, or the start of a
+// descriptor window) that the NSPLIT kernels' prefetching loads can reach.
+constexpr int64_t kNsplitReach = 288;
+// Tiles per loop turn of the NSPLIT kernels; a segment runs whole turns and
+// at most one half turn, so its padded length is a multiple of half a turn.
+constexpr int kNsplitTurn = 8;
 
 // Each launcher enqueues its kernels on `stream` and returns hipGetLastError().
 hipError_t launch_nsplit(const Problem& p, hipStream_t stream);

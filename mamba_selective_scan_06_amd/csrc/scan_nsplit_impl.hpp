@@ -7,11 +7,13 @@
 //   scan waves 0..3: wave w holds the K = N/4 states n = wK .. wK+K-1 of its
 //     channel in fp32 registers and advances them through every token (the 16
 //     states of a channel at N = 16 live in 4 lanes of 4 waves);
-//   owner waves 4..7: owner o does the per-(t, d) scalar work of the tokens
-//     j = o (mod 4) of each tile for all 64 channels: loading and widening x,
-//     delta and z, softplus, u = delta x, the decay terms, D x and SiLU(z).
-//     It publishes (decay terms, u) in LDS and, a tile later, adds the scan
-//     waves' partial readouts, D x and the gate, rounds once and stores y_t.
+//   owner waves 4..7: owner o does the per-(t, d) scalar work of 4 tokens of
+//     each tile for all 64 channels: loading and widening x, delta and z,
+//     softplus, u = delta x, the decay terms, D x and SiLU(z).  It publishes
+//     (decay terms, u) in LDS and, later, adds the scan waves' partial
+//     readouts, D x and the gate, rounds once and stores y_t.  When D is a
+//     multiple of 4, an owner lane handles 4 channels of one token (one 8- or
+//     16-byte access per tensor and tile); otherwise one channel of 4 tokens.
 // One workgroup keeps 64 x N independent recurrence chains on chip for the
 // whole segment, and 64 channels of a Mamba layer give 4 scan waves, one per
 // SIMD, which the channel count needs to fill 1024 SIMDs without splitting time.
@@ -22,11 +24,14 @@
 //   h_n  <- Abar_n h_n + (delta x) B_t[n]              sections 2.2, 3.3 (Euler input term)
 //   y     = sum_n C_t[n] h_n + D[d] x, y *= SiLU(z)    sections 2.2, 3.4
 //
-// Time is walked in tiles of 16 tokens with one barrier per tile and the LDS
-// terms double-buffered: in iteration k the scan waves consume tile k (reading
-// its per-token terms, writing their partial readouts sum_{n in wave} C_t[n] h_n)
-// while the owners compute tile k+1's terms into the other buffer and finish
-// tile k-1 from the partials left there.
+// Time is walked in tiles of 16 tokens with one barrier per tile.  In
+// iteration k the scan waves consume tile k (its per-token terms already in
+// registers, writing their partial readouts sum_{n in wave} C_t[n] h_n) and
+// read tile k+1's terms from LDS into registers, while the owners compute
+// tile k+2's terms (4 term buffers) and finish tile k-1 from the partials
+// (2 buffers).  So no scan wave waits on LDS data inside a tile.  The loop
+// runs turns of 8 tiles (and at most one half turn), which keeps every ring
+// index a compile-time constant.
 
 // Memory.  All loads are raw buffer loads with the whole byte offset in the
 // VGPR offset (the part the range check covers), through a descriptor over one
@@ -35,13 +40,17 @@
 // tile before the segment and ends with it, and a lane whose store must not
 // happen gets an offset past it.  Offsets are 32-bit: for rows of 2 GiB or
 // more (WIN) the descriptors instead cover windows that start a few tiles
-// behind the accesses and move forward every NS_PF tiles, so offsets stay
-// below 144 tokens of a row whatever its length.
-// Every input a tile needs (x, delta, z of the owned tokens, and this wave's
-// slices of B_t and C_t for all 16 tokens) is loaded NS_PF tiles ahead into a
-// register ring; one wave per SIMD cannot hide HBM latency by switching waves,
-// and every iteration issues the same memory operations, so each wait covers
-// only the oldest tile.
+// behind the accesses and move forward every turn, so offsets stay below 288
+// tokens of a row whatever its length.
+// Every input a tile needs is loaded ahead into register rings: x, delta and
+// z of the owners' tokens 8 tiles ahead (4 for one-channel owners: the
+// gfx9 vmcnt counter holds at most 63 loads in flight, so narrow loads cannot
+// go deeper), this wave's slices of B_t and C_t 4 tiles ahead.  The owners'
+// streams are latency-bound: measured alone, the owner waves took 441 us per
+// launch with one channel per lane and 4 tiles in flight, 304 us with 4
+// channels per lane and 8 tiles.  Every iteration issues the same memory
+// operations, and each ring word passes through an empty asm where it is
+// consumed, so each wait covers only the oldest tile.
 //
 // B_t and C_t are the same for all 64 channels of a wave.  A tile's slices
 // are loaded so that every 16-lane row of the wave holds the same 16 words,
@@ -80,7 +89,19 @@ namespace nsplit_detail {
 
 constexpr int NS_T = kNsplitTile;  // tokens per tile
 constexpr int NS_OWN = NS_T / 4;   // tokens owned by each wave per tile
-constexpr int NS_PF = 4;           // prefetch depth in tiles (register ring slots)
+constexpr int NS_PF = 4;           // prefetch depth in tiles of the scan waves and one-channel owners
+constexpr int NS_PFO = 8;          // prefetch depth in tiles of the wide-layout owners
+constexpr int NS_TURN = 8;         // tiles per loop iteration (a multiple of every ring depth)
+
+// f(integral_constant<int, i>) for i = 0 .. n-1, unrolled.
+template <int... Is, typename F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, Is...>, F&& f) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int n, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, n>{}, f);
+}
 
 // Broadcast lane LANE of every 16-lane row to the whole row.
 template <int LANE>
@@ -166,10 +187,14 @@ struct BCLayout {
   static constexpr bool odd_half(int k) { return kPairs && (k & 1); }
 };
 
+// The owners compute a tile's terms two tiles ahead of the scan waves, which
+// read a tile's terms into registers while they scan the tile before it: the
+// terms rotate through NS_EB buffers, the partial readouts through two.
+constexpr int NS_EB = 4;
 struct Smem {
-  float E[2][NS_T][4][64];  // decay terms: chain start per scan wave (structured) or delta in slot 0
-  float U[2][NS_T][64];     // u = delta * x
-  float P[2][NS_T][4][64];  // partial readouts per scan wave
+  float E[NS_EB][NS_T][4][64];  // decay terms: chain start per scan wave (structured) or delta in slot 0
+  float U[NS_EB][NS_T][64];     // u = delta * x
+  float P[2][NS_T][4][64];      // partial readouts per scan wave
 };
 constexpr int kSmemBytes = static_cast<int>(sizeof(Smem));
 
@@ -178,7 +203,7 @@ constexpr int kSmemBytes = static_cast<int>(sizeof(Smem));
 struct SegCtx {
   int32_t L;               // tokens of a batch row
   int32_t t_begin, t_end;  // token range of the segment
-  int32_t ntiles;          // tiles in the segment, rounded up to a multiple of NS_PF
+  int32_t ntiles;          // tiles in the segment, rounded up to a multiple of NS_TURN / 2
   uint32_t D, d0;          // channels, first channel of the block
   int w, lane;             // wave (0..7) and lane
   bool active;             // lane's channel < D
@@ -209,7 +234,7 @@ __device__ __forceinline__ uint32_t ring_word(uint32_t v) {
 // the part shared by the tensors of one layout (byte offset of W, and the
 // bytes to the end capped below 2 GiB at cap_tokens = kMaxRecords / tok_bytes
 // tokens), then one descriptor per tensor.  Every offset the loops use is
-// under 144 tokens from W; the planner keeps that under 2 GiB, so a capped
+// under 288 tokens from W; the planner keeps that under 2 GiB, so a capped
 // window still covers it.  W may be one tile before the row start (the first
 // store window): the base is formed as an integer address, and nothing before
 // the row is accessed.
@@ -361,7 +386,7 @@ __device__ __forceinline__ void owner_loop(Smem& sm, const S* xrow, const S* dlr
     }
   };
 
-  static_assert(NS_PF == 4, "the ring code below is written for 4 slots");
+  static_assert(NS_PF == 4 && NS_TURN % NS_PF == 0 && NS_EB == 4, "the ring code below is written for 4 slots");
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -372,33 +397,262 @@ __device__ __forceinline__ void owner_loop(Smem& sm, const S* xrow, const S* dlr
   load_tile(I3{}, c.t_begin + 3 * NS_T);
   compute_tile(I0{}, 0, c.t_begin);
   load_tile(I0{}, c.t_begin + NS_PF * NS_T);
+  compute_tile(I1{}, 1, c.t_begin + NS_T);
+  load_tile(I1{}, c.t_begin + (NS_PF + 1) * NS_T);
   __syncthreads();
-  // iteration k (tile k scanned meanwhile): compute tile k+1, finish tile k-1
-  for (int32_t k0 = 0; k0 < c.ntiles; k0 += NS_PF) {
-    if constexpr (WIN) {  // this turn loads tiles k0+5..k0+8 and stores tiles k0-1..k0+2
+  // iteration k (tile k scanned meanwhile): compute tile k+2, finish tile k-1
+  int32_t k0 = 0;
+  auto turn_start = [&]() {
+    if constexpr (WIN) {  // this turn loads tiles k0+6..k0+13 and stores tiles k0-1..k0+6
       W = opaque_sgpr(c.t_begin + k0 * NS_T);
       Wy = W - NS_T;
       set_windows();
     }
-    auto step = [&](auto kc, auto next_c, auto prev_c) {
-      constexpr int kk = decltype(kc)::value;  // k0 + kk is the tile being scanned
-      const int32_t tk = c.t_begin + (k0 + kk) * NS_T;
-      if constexpr (!STATE_ONLY) read_partials((kk + 1) & 1);
-      compute_tile(next_c, (kk + 1) & 1, tk + NS_T);
-      load_tile(next_c, tk + NS_T + NS_PF * NS_T);
-      if constexpr (!STATE_ONLY) finish_tile(prev_c, tk - NS_T);
-      __syncthreads();
-    };
-    // ring slot of tile m is m % 4; k0 is a multiple of 4
-    step(I0{}, I1{}, I3{});
-    step(I1{}, I2{}, I0{});
-    step(I2{}, I3{}, I1{});
-    step(I3{}, I0{}, I2{});
+  };
+  // ring slot and term buffer of tile m are m % 4; k0 is a multiple of 4
+  auto step = [&](auto kc) {
+    constexpr int kk = decltype(kc)::value;  // k0 + kk is the tile being scanned
+    const int32_t tk = c.t_begin + (k0 + kk) * NS_T;
+    using Ahead = std::integral_constant<int, (kk + 2) % NS_PF>;
+    if constexpr (!STATE_ONLY) read_partials((kk + 1) & 1);
+    compute_tile(Ahead{}, (kk + 2) % NS_EB, tk + 2 * NS_T);
+    load_tile(Ahead{}, tk + 2 * NS_T + NS_PF * NS_T);
+    if constexpr (!STATE_ONLY) finish_tile(std::integral_constant<int, (kk + NS_PF - 1) % NS_PF>{}, tk - NS_T);
+    __syncthreads();
+  };
+  for (; k0 + NS_TURN <= c.ntiles; k0 += NS_TURN) {
+    turn_start();
+    static_for<NS_TURN>(step);
+  }
+  if (k0 < c.ntiles) {  // a half turn: ntiles is a multiple of NS_TURN / 2
+    turn_start();
+    static_for<NS_TURN / 2>(step);
   }
   // the last scanned tile (ntiles-1 has slot 3)
   if constexpr (!STATE_ONLY) {
     read_partials((c.ntiles - 1) & 1);
     finish_tile(I3{}, c.t_begin + (c.ntiles - 1) * NS_T);
+  }
+}
+
+// ---- owner waves, wide layout (channel counts that are multiples of 4) -------
+// The same role with 4-channel vectors: lane l of owner o handles token
+// j = 4o + (l / 16) of every tile and the 4 channels 4 (l % 16) .. +3, so one
+// 8-byte (bf16) or 16-byte (fp32) load brings a tile's x (delta, z) for the
+// owner's 4 tokens, one store writes its y, and the LDS terms move as float4
+// (16 lanes cover a token's 64 channels, 256 contiguous bytes).  Four times
+// fewer memory and LDS instructions than one channel per lane.
+template <typename S>
+struct WideVec;
+template <>
+struct WideVec<uint16_t> {
+  typedef unsigned int T __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, kStreamPolicy);
+  }
+  static __device__ __forceinline__ float get(const T& v, int k) {
+    const uint32_t w = v[k >> 1];
+    return __uint_as_float((k & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&y)[4]) {
+    typedef float F2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 H2 __attribute__((ext_vector_type(2)));
+    const F2 lo = {y[0], y[1]}, hi = {y[2], y[3]};  // rounded to nearest even (v_cvt_pk_bf16_f32)
+    const T v = {__builtin_bit_cast(unsigned int, __builtin_convertvector(lo, H2)),
+                 __builtin_bit_cast(unsigned int, __builtin_convertvector(hi, H2))};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, static_cast<int>(off), 0, kStreamPolicy);
+  }
+};
+template <>
+struct WideVec<float> {
+  typedef unsigned int T __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kStreamPolicy);
+  }
+  static __device__ __forceinline__ float get(const T& v, int k) { return __uint_as_float(v[k]); }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&y)[4]) {
+    const T v = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), 0, kStreamPolicy);
+  }
+};
+
+// Per-channel constants of the 4 channels a wide-layout owner lane handles.
+struct WideChan {
+  float A2_0[4], A_0[4], invA_0[4], bias[4], Dd[4];
+};
+
+template <typename S, int K, bool STATE_ONLY, bool STRUCT, bool GATE, bool ZOH, bool WIN>
+__device__ __forceinline__ void owner_loop_wide(Smem& sm, const S* xrow, const S* dlrow, const S* zrow, S* yrow,
+                                                const SegCtx& c, const WideChan& ch, float (&dsum)[4]) {
+  using WV = WideVec<S>;
+  using V = typename WV::T;
+  constexpr uint32_t ES = sizeof(S);
+  constexpr bool kLoadZ = !STATE_ONLY && GATE;
+  const int o = c.w - 4;
+  const int ti = c.lane >> 4;          // token of the quad
+  const int cg = (c.lane & 15) * 4;    // first of the lane's 4 channels in the block
+  const int jl = 4 * o + ti;           // the lane's token inside a tile
+  const uint32_t xo = (c.d0 + cg) * ES;
+  // channel groups past D store from a base past every window (D % 4 == 0:
+  // a group is wholly inside or wholly outside)
+  const uint32_t yo = (c.d0 + cg < c.D) ? xo : kPastWindow;
+
+  V xr[NS_PFO], dr[NS_PFO], zr[NS_PFO];
+  float keep_dx[NS_PFO][4], keep_g[NS_PFO][4];
+  // a ring word, marked as used here: its load's wait stays at the tile that
+  // needs it (hoisted to the top of a turn, it would drain the whole ring)
+  auto pin = [](V v) {
+#pragma unroll
+    for (int q = 0; q < static_cast<int>(sizeof(V) / 4); ++q) {
+      uint32_t w = v[q];
+      asm volatile("" : "+v"(w));
+      v[q] = w;
+    }
+    return v;
+  };
+
+  int32_t W = WIN ? c.t_begin : 0, Wy = c.t_begin - NS_T;
+  __amdgpu_buffer_rsrc_t bx, bdl, bz, by;
+  const uint32_t tok_bytes = c.D * ES;
+  const int32_t cap_tokens = static_cast<int32_t>(kMaxRecords / tok_bytes);
+  auto set_windows = [&]() {
+    const WinSpan in = win_span(W, c.L, tok_bytes, cap_tokens);
+    bx = window(xrow, in);
+    bdl = window(dlrow, in);
+    if constexpr (kLoadZ) bz = window(zrow, in);
+    if constexpr (!STATE_ONLY) by = window(yrow, win_span(Wy, c.t_end, tok_bytes, cap_tokens));
+  };
+  set_windows();
+
+  auto load_tile = [&](auto slot_c, int32_t t0) {
+    constexpr int slot = decltype(slot_c)::value;
+    const uint32_t off = xo + static_cast<uint32_t>(t0 + jl - W) * c.D * ES;
+    xr[slot] = WV::load(bx, off);
+    dr[slot] = WV::load(bdl, off);
+    if constexpr (kLoadZ) zr[slot] = WV::load(bz, off);
+  };
+
+  auto compute_tile = [&](auto slot_c, int buf, int32_t t0) {
+    constexpr int slot = decltype(slot_c)::value;
+    // tokens at or past the segment end become neutral steps: delta = 0 gives
+    // decay 1 (or exp(0) - 1 = 0 under the hold) and, with x = 0, no input
+    const bool tail = t0 + 4 * o + 3 >= c.t_end;  // wave-uniform
+    const bool valid = t0 + jl < c.t_end;
+    float e0[4], e1[4], e2[4], e3[4], uu[4];
+    const V xw = pin(xr[slot]), dw = pin(dr[slot]);
+    V zw;
+    if constexpr (kLoadZ) zw = pin(zr[slot]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float xv = WV::get(xw, k);
+      float dt = softplus_f32(WV::get(dw, k) + ch.bias[k]);
+      if (tail) {
+        dt = valid ? dt : 0.0f;
+        xv = valid ? xv : 0.0f;
+      }
+      if constexpr (STATE_ONLY) {
+        dsum[k] += dt;
+      } else {
+        keep_dx[slot][k] = ch.Dd[k] * xv;
+        if constexpr (GATE) keep_g[slot][k] = silu_f32(WV::get(zw, k));
+      }
+      if constexpr (STRUCT && ZOH) {
+        const float r = fast_exp2(dt * ch.A2_0[k]);
+        const float E1 = expm1_neg(dt * ch.A_0[k], r);
+        float rk = r, EK = E1;
+#pragma unroll
+        for (int q = 1; q < K; q <<= 1) EK = EK * (EK + 2.0f), rk *= rk;
+        e0[k] = E1;
+        e1[k] = __builtin_fmaf(EK, r, E1);
+        e2[k] = __builtin_fmaf(e1[k], rk, EK);
+        e3[k] = __builtin_fmaf(e2[k], rk, EK);
+      } else if constexpr (STRUCT) {
+        const float r = fast_exp2(dt * ch.A2_0[k]);
+        float rk = r;
+#pragma unroll
+        for (int q = 1; q < K; q <<= 1) rk *= rk;
+        e0[k] = r;
+        e1[k] = e0[k] * rk;
+        e2[k] = e1[k] * rk;
+        e3[k] = e2[k] * rk;
+      } else {
+        e0[k] = dt;
+      }
+      uu[k] = ZOH ? (STRUCT ? xv * ch.invA_0[k] : xv) : dt * xv;
+    }
+    *reinterpret_cast<float4*>(&sm.E[buf][jl][0][cg]) = make_float4(e0[0], e0[1], e0[2], e0[3]);
+    if constexpr (STRUCT) {
+      *reinterpret_cast<float4*>(&sm.E[buf][jl][1][cg]) = make_float4(e1[0], e1[1], e1[2], e1[3]);
+      *reinterpret_cast<float4*>(&sm.E[buf][jl][2][cg]) = make_float4(e2[0], e2[1], e2[2], e2[3]);
+      *reinterpret_cast<float4*>(&sm.E[buf][jl][3][cg]) = make_float4(e3[0], e3[1], e3[2], e3[3]);
+    }
+    *reinterpret_cast<float4*>(&sm.U[buf][jl][cg]) = make_float4(uu[0], uu[1], uu[2], uu[3]);
+  };
+
+  float4 pr[4];
+  auto read_partials = [&](int buf) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) pr[w] = *reinterpret_cast<const float4*>(&sm.P[buf][jl][w][cg]);
+  };
+  auto finish_tile = [&](auto slot_c, int32_t t0) {
+    constexpr int slot = decltype(slot_c)::value;
+    const float p0[4] = {pr[0].x, pr[0].y, pr[0].z, pr[0].w};
+    const float p1[4] = {pr[1].x, pr[1].y, pr[1].z, pr[1].w};
+    const float p2[4] = {pr[2].x, pr[2].y, pr[2].z, pr[2].w};
+    const float p3[4] = {pr[3].x, pr[3].y, pr[3].z, pr[3].w};
+    float yv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      yv[k] = ((p0[k] + p1[k]) + p2[k]) + p3[k];
+      yv[k] += keep_dx[slot][k];
+      if constexpr (GATE) yv[k] *= keep_g[slot][k];
+    }
+    const int32_t tj = t0 + jl;
+    const uint32_t off = (tj >= c.t_begin ? yo : kPastWindow) + static_cast<uint32_t>(tj - Wy) * c.D * ES;
+    WV::store(by, off, yv);
+  };
+
+  static_assert(NS_TURN % NS_PFO == 0 && NS_TURN % NS_EB == 0, "a turn covers whole rings");
+  static_for<NS_PFO>([&](auto sc) { load_tile(sc, c.t_begin + decltype(sc)::value * NS_T); });
+  compute_tile(std::integral_constant<int, 0>{}, 0, c.t_begin);
+  load_tile(std::integral_constant<int, 0>{}, c.t_begin + NS_PFO * NS_T);
+  compute_tile(std::integral_constant<int, 1>{}, 1, c.t_begin + NS_T);
+  load_tile(std::integral_constant<int, 1>{}, c.t_begin + (NS_PFO + 1) * NS_T);
+  __syncthreads();
+  // iteration k (tile k scanned meanwhile): compute tile k+2, load tile
+  // k+2+NS_PFO into its slot, finish tile k-1
+  int32_t k0 = 0;
+  auto turn_start = [&]() {
+    if constexpr (WIN) {  // this turn loads tiles k0+10..k0+17 and stores tiles k0-1..k0+6
+      W = opaque_sgpr(c.t_begin + k0 * NS_T);
+      Wy = W - NS_T;
+      set_windows();
+    }
+  };
+  auto step = [&](auto kc) {
+    constexpr int kk = decltype(kc)::value;
+    const int32_t tk = c.t_begin + (k0 + kk) * NS_T;
+    using Ahead = std::integral_constant<int, (kk + 2) % NS_PFO>;
+    if constexpr (!STATE_ONLY) read_partials((kk + 1) & 1);
+    compute_tile(Ahead{}, (kk + 2) % NS_EB, tk + 2 * NS_T);
+    load_tile(Ahead{}, tk + 2 * NS_T + NS_PFO * NS_T);
+    if constexpr (!STATE_ONLY) finish_tile(std::integral_constant<int, (kk + NS_PFO - 1) % NS_PFO>{}, tk - NS_T);
+    __syncthreads();
+  };
+  for (; k0 + NS_TURN <= c.ntiles; k0 += NS_TURN) {
+    turn_start();
+    static_for<NS_TURN>(step);
+  }
+  if (k0 < c.ntiles) {  // a half turn: ntiles is a multiple of NS_TURN / 2
+    turn_start();
+    static_for<NS_TURN / 2>(step);
+  }
+  if constexpr (!STATE_ONLY) {  // the last scanned tile has slot NS_PFO - 1, or NS_PFO / 2 - 1 after a half turn
+    read_partials((c.ntiles - 1) & 1);
+    if (c.ntiles % NS_PFO == 0)
+      finish_tile(std::integral_constant<int, NS_PFO - 1>{}, c.t_begin + (c.ntiles - 1) * NS_T);
+    else
+      finish_tile(std::integral_constant<int, NS_PFO / 2 - 1>{}, c.t_begin + (c.ntiles - 1) * NS_T);
   }
 }
 
@@ -453,8 +707,26 @@ __device__ __forceinline__ void scan_loop(Smem& sm, const S* Brow, const S* Crow
     }
   };
 
-  auto scan_tile = [&](auto slot_c, int buf) {
+  // A tile's per-token LDS terms (decay term of this wave's first state or
+  // delta, the ratio r, u), read into registers one tile ahead of their use.
+  float tt[2][NS_T][3];
+  auto read_terms = [&](auto par_c, int buf) {
+    constexpr int par = decltype(par_c)::value;
+#pragma unroll
+    for (int j = 0; j < NS_T; ++j) {
+      tt[par][j][0] = sm.E[buf][j][STRUCT ? c.w : 0][c.lane];
+      tt[par][j][1] = STRUCT ? sm.E[buf][j][0][c.lane] : 0.0f;
+      tt[par][j][2] = sm.U[buf][j][c.lane];
+    }
+  };
+
+  auto scan_tile = [&](auto slot_c, auto buf_c) {
     constexpr int slot = decltype(slot_c)::value;
+    constexpr int buf = decltype(buf_c)::value;  // term buffer of this tile (tile % NS_EB)
+    constexpr int par = buf & 1;
+    // the next tile's terms (the owners wrote them an iteration ago)
+    read_terms(std::integral_constant<int, par ^ 1>{}, (buf + 1) % NS_EB);
+    __builtin_amdgcn_sched_barrier(0);
     float Blo[NLD], Bhi[NLD], Clo[NLD], Chi[NLD];
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
@@ -484,12 +756,12 @@ __device__ __forceinline__ void scan_loop(Smem& sm, const S* Brow, const S* Crow
         }
         if constexpr (STRUCT && ZOH) Clo[q] *= cslo, Chi[q] *= cshi;
       }
-      const float u = sm.U[buf][j][c.lane];
+      const float u = tt[par][j][2];
       float hv[K];
-      float a = STRUCT ? sm.E[buf][j][c.w][c.lane] : 0.0f;  // ZOH: E of the wave's first state
-      const float r0 = STRUCT ? sm.E[buf][j][0][c.lane] : 0.0f;
-      const float r = (STRUCT && ZOH) ? 1.0f + r0 : r0;    // ZOH: r0 is E_1
-      const float dt = STRUCT ? 0.0f : sm.E[buf][j][0][c.lane];
+      float a = STRUCT ? tt[par][j][0] : 0.0f;           // ZOH: E of the wave's first state
+      const float r0 = STRUCT ? tt[par][j][1] : 0.0f;
+      const float r = (STRUCT && ZOH) ? 1.0f + r0 : r0;  // ZOH: r0 is E_1
+      const float dt = STRUCT ? 0.0f : tt[par][j][0];
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         if constexpr (STRUCT && ZOH) {
@@ -542,7 +814,7 @@ __device__ __forceinline__ void scan_loop(Smem& sm, const S* Brow, const S* Crow
           if constexpr (K >= 12) chunk(std::integral_constant<int, 2>{});
           if constexpr (K >= 16) chunk(std::integral_constant<int, 3>{});
         }
-        sm.P[buf][j][c.w][c.lane] = acc;
+        sm.P[par][j][c.w][c.lane] = acc;
       }
       // keep each pair of tokens' LDS reads, arithmetic and writes together
       // (pairs share paired LDS instructions): reads grouped further ahead of
@@ -565,21 +837,28 @@ __device__ __forceinline__ void scan_loop(Smem& sm, const S* Brow, const S* Crow
   load_tile(I2{}, c.t_begin + 2 * NS_T);
   load_tile(I3{}, c.t_begin + 3 * NS_T);
   __syncthreads();
-  for (int32_t k0 = 0; k0 < c.ntiles; k0 += NS_PF) {
-    if constexpr (WIN) {  // this turn loads tiles k0+4..k0+7
+  read_terms(std::integral_constant<int, 0>{}, 0);
+  int32_t k0 = 0;
+  auto turn_start = [&]() {
+    if constexpr (WIN) {  // this turn loads tiles k0+4..k0+11
       W = opaque_sgpr(c.t_begin + k0 * NS_T);
       set_windows();
     }
-    auto step = [&](auto kc) {
-      constexpr int kk = decltype(kc)::value;
-      scan_tile(kc, kk & 1);
-      load_tile(kc, c.t_begin + (k0 + kk + NS_PF) * NS_T);
-      __syncthreads();
-    };
-    step(I0{});
-    step(I1{});
-    step(I2{});
-    step(I3{});
+  };
+  auto step = [&](auto kc) {
+    constexpr int kk = decltype(kc)::value;
+    using Slot = std::integral_constant<int, kk % NS_PF>;
+    scan_tile(Slot{}, std::integral_constant<int, kk % NS_EB>{});
+    load_tile(Slot{}, c.t_begin + (k0 + kk + NS_PF) * NS_T);
+    __syncthreads();
+  };
+  for (; k0 + NS_TURN <= c.ntiles; k0 += NS_TURN) {
+    turn_start();
+    static_for<NS_TURN>(step);
+  }
+  if (k0 < c.ntiles) {  // a half turn: ntiles is a multiple of NS_TURN / 2
+    turn_start();
+    static_for<NS_TURN / 2>(step);
   }
 }
 
@@ -608,7 +887,7 @@ __global__ __launch_bounds__(512, 1) void scan_nsplit_kernel(
   c.t_begin = s * seg_len;
   c.t_end = (c.t_begin + seg_len < L) ? c.t_begin + seg_len : L;
   const int32_t nt = (c.t_end - c.t_begin + NS_T - 1) / NS_T;
-  c.ntiles = (nt + NS_PF - 1) / NS_PF * NS_PF;
+  c.ntiles = (nt + NS_TURN / 2 - 1) / (NS_TURN / 2) * (NS_TURN / 2);
 
   float A2[K], An[K], iA[K];
 #pragma unroll
@@ -635,14 +914,33 @@ __global__ __launch_bounds__(512, 1) void scan_nsplit_kernel(
   // this batch row of the (B, L, D) and (B, L, N) tensors
   const int64_t rowD = b * static_cast<int64_t>(L) * D, rowN = b * static_cast<int64_t>(L) * N;
 
-  float dsum = 0.0f;
+  float dsum = 0.0f, dsw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float h[K];
   if (c.w >= 4) {
     const S* zrow = z ? z + rowD : x + rowD;  // never read without a gate
-    if (structured)
+    if ((D & 3) == 0) {  // wide layout: 4 channels per lane
+      WideChan ch;
+      const int cg = (c.lane & 15) * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        // channels past D (whole groups) read channel D-1's constants
+        const int64_t dk = c.d0 + cg + k < c.D ? c.d0 + cg + k : c.D - 1;
+        const float ak = A[dk * N];
+        ch.A_0[k] = ak;
+        ch.A2_0[k] = ak * kLog2e;
+        ch.invA_0[k] = ZOH ? 1.0f / ak : 0.0f;
+        ch.bias[k] = bias ? bias[dk] : 0.0f;
+        ch.Dd[k] = Dsk ? Dsk[dk] : 0.0f;
+      }
+      if (structured)
+        owner_loop_wide<S, K, STATE_ONLY, true, GATE, ZOH, WIN>(sm, x + rowD, dl + rowD, zrow, y + rowD, c, ch, dsw);
+      else
+        owner_loop_wide<S, K, STATE_ONLY, false, GATE, ZOH, WIN>(sm, x + rowD, dl + rowD, zrow, y + rowD, c, ch, dsw);
+    } else if (structured) {
       owner_loop<S, K, STATE_ONLY, true, GATE, ZOH, WIN>(sm, x + rowD, dl + rowD, zrow, y + rowD, c, dsum);
-    else
+    } else {
       owner_loop<S, K, STATE_ONLY, false, GATE, ZOH, WIN>(sm, x + rowD, dl + rowD, zrow, y + rowD, c, dsum);
+    }
   } else {
     if constexpr (STATE_ONLY) {
 #pragma unroll
@@ -678,15 +976,31 @@ __global__ __launch_bounds__(512, 1) void scan_nsplit_kernel(
     // per-channel sum of delta: owner partials through LDS (reusing E)
     __syncthreads();
     float* sdv = &sm.E[0][0][0][0];
-    if (c.w >= 4) sdv[(c.w - 4) * 64 + c.lane] = dsum;
+    const bool wide = (D & 3) == 0;
+    if (wide) {  // owner o, token row ti, channel cg + k: 16 partial sums per channel
+      if (c.w >= 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sdv[((c.w - 4) * 4 + (c.lane >> 4)) * 64 + (c.lane & 15) * 4 + k] = dsw[k];
+      }
+    } else if (c.w >= 4) {
+      sdv[(c.w - 4) * 64 + c.lane] = dsum;
+    }
     __syncthreads();
     const int64_t seg = b * splits + s;
     if (c.w < 4 && c.active) {
 #pragma unroll
       for (int k = 0; k < K; ++k) ws_state[(seg * D + d) * N + sw * K + k] = h[k];
     }
-    if (c.w == 0 && c.active)
-      ws_dsum[seg * D + d] = ((sdv[c.lane] + sdv[64 + c.lane]) + sdv[128 + c.lane]) + sdv[192 + c.lane];
+    if (c.w == 0 && c.active) {
+      float tot = 0.0f;
+      if (wide) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tot += sdv[r * 64 + c.lane];
+      } else {
+        tot = ((sdv[c.lane] + sdv[64 + c.lane]) + sdv[128 + c.lane]) + sdv[192 + c.lane];
+      }
+      ws_dsum[seg * D + d] = tot;
+    }
   } else {
     if (hT && c.w < 4 && c.active && s == splits - 1) {
 #pragma unroll

@@ -101,6 +101,20 @@ def test_empty_problems_are_noops():
     assert _fwd(a) == 0
 
 
+def test_empty_problems_plan_and_workspace_queries():
+    # batch or dim zero through the host-only queries: no workspace, one
+    # segment, no crash (the planner's blocks-per-compute-unit division)
+    lib = ssm.lib()
+    for shape in ((0, 64, 128, 16), (2, 64, 0, 16), (0, 8192, 1536, 16), (1, 8192, 0, 16)):
+        a = _args(shape=shape, x=0, y=0)
+        assert lib.ssm_scan_workspace_bytes(ctypes.byref(a)) == 0
+        assert lib.ssm_scan_plan(ctypes.byref(a)) >= 0
+        assert ssm.plan(a)[1] == 1
+        a.workspace, a.workspace_bytes = FAKE + (64 << 32), 1 << 30
+        assert lib.ssm_scan_plan(ctypes.byref(a)) >= 0
+        assert _fwd(a) == 0
+
+
 def test_plan_and_workspace_queries():
     lib = ssm.lib()
     # the benchmark layer: 64 channel blocks x 4 batch rows = 256 blocks, one per compute unit, unsplit
@@ -143,7 +157,7 @@ def test_plan_long_rows_stay_on_the_main_kernel():
     assert ssm.plan(big((1, 270_008, 4104, 16), 0)) == ("nsplit", 1)   # 4.43 GB fp32 row
     assert ssm.plan(big((1, 2**31 - 1025, 64, 16), 1)) == ("nsplit", 1)
     assert ssm.plan(big((1, 2**31 - 1024, 64, 16), 1)) == ("lane", 1)
-    lim = (2**31 - 1) // 144
+    lim = (2**31 - 1) // 288
     assert ssm.plan(big((1, 64, lim // 2, 16), 1)) == ("nsplit", 1)
     assert ssm.plan(big((1, 64, lim // 2 + 1, 16), 1)) == ("lane", 1)
     assert ssm.plan(big((1, 64, lim // 4, 16), 0)) == ("nsplit", 1)
