@@ -110,6 +110,26 @@ int ssm_scan_fwd(const ssm_scan_args *args, void *stream);
  * HIP call.  Returns a negative SSM_ERR_* code for invalid arguments. */
 int64_t ssm_scan_workspace_bytes(const ssm_scan_args *args);
 
+/* ssm_scan_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, plan, kernels and results (bitwise) as ssm_scan_fwd given a
+ * workspace of ssm_scan_workspace_bytes bytes, except that the time-split
+ * segment summaries live in a device array inside the library, 8 MiB per GPU
+ * (held from the library's first such call on that GPU until the process
+ * ends).  args->workspace and args->workspace_bytes are ignored.  The call
+ * allocates nothing.
+ *   - An explicit time_splits > 1 whose summaries need more than 8 MiB
+ *     (batch * time_splits * dim * (dstate + 1) * 4 bytes, each part rounded
+ *     up to 256 bytes) returns SSM_ERR_WORKSPACE; automatic plans need at
+ *     most 4.3 MiB (otherwise they would run unsplit).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (other streams, other threads) race and give wrong
+ *     results.  Calls ordered on one stream are safe.  Nothing in the array
+ *     needs clearing: each call writes every summary it reads.
+ *   - SSM_ERR_LAUNCH if the array's device address cannot be obtained.
+ * The caller still owns and passes every input and output. */
+int ssm_scan_fwd_noalloc(const ssm_scan_args *args, void *stream);
+
 /* The kernel family and number of time segments ssm_scan_fwd would use, as
  * variant * 65536 + time_splits.  Host-only.  Negative on invalid arguments. */
 int64_t ssm_scan_plan(const ssm_scan_args *args);

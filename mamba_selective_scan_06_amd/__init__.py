@@ -32,7 +32,7 @@ FLAG_GENERIC_A = 1
 FLAG_ZOH = 2
 
 # Exported symbols the header declares (checked by the tests).
-EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_scan_bwd",
+EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_noalloc", "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_scan_bwd",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd_plan", "ssm_conv1d_silu_fwd", "ssm_ssd_fwd",
            "ssm_gla_fwd", "ssm_gla_workspace_bytes", "ssm_scan_strerror", "ssm_scan_abi_version")
 
@@ -121,6 +121,8 @@ def lib() -> ctypes.CDLL:
         P = ctypes.POINTER(ScanArgs)
         L.ssm_scan_fwd.argtypes = [P, ctypes.c_void_p]
         L.ssm_scan_fwd.restype = ctypes.c_int
+        L.ssm_scan_fwd_noalloc.argtypes = [P, ctypes.c_void_p]
+        L.ssm_scan_fwd_noalloc.restype = ctypes.c_int
         L.ssm_scan_workspace_bytes.argtypes = [P]
         L.ssm_scan_workspace_bytes.restype = ctypes.c_int64
         L.ssm_scan_plan.argtypes = [P]

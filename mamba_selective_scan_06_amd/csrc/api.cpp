@@ -428,15 +428,11 @@ int64_t ssm_scan_plan(const ssm_scan_args* a) {
   return static_cast<int64_t>(pl.variant) * 65536 + pl.splits;
 }
 
-int ssm_scan_fwd(const ssm_scan_args* a, void* stream) {
-  int64_t bld, bln, bdn;
-  int rc = validate(a, &bld, &bln, &bdn);
-  if (rc != SSM_OK) return rc;
-  if (a->batch == 0 || a->dim == 0) return SSM_OK;
-  Plan pl;
-  rc = make_plan(a, true, &pl);
-  if (rc != SSM_OK) return rc;
+namespace {
 
+// Launch a validated, planned forward call; ws is the segment summaries'
+// memory when the plan splits time.
+int run_fwd(const ssm_scan_args* a, const Plan& pl, void* ws, void* stream) {
   Problem p;
   p.batch = a->batch;
   p.seqlen = a->seqlen;
@@ -458,8 +454,8 @@ int ssm_scan_fwd(const ssm_scan_args* a, void* stream) {
   p.splits = pl.splits;
   p.seg_len = pl.seg_len;
   p.windowed = pl.variant == SSM_VARIANT_NSPLIT && nsplit_windowed(a);
-  p.ws_state = pl.splits > 1 ? static_cast<float*>(a->workspace) : nullptr;
-  p.ws_dsum = pl.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pl.ws_state_bytes) : nullptr;
+  p.ws_state = pl.splits > 1 ? static_cast<float*>(ws) : nullptr;
+  p.ws_dsum = pl.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + pl.ws_state_bytes) : nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -472,6 +468,46 @@ int ssm_scan_fwd(const ssm_scan_args* a, void* stream) {
   else
     e = ssm::launch_lane(p, s);
   return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+int ssm_scan_fwd(const ssm_scan_args* a, void* stream) {
+  int64_t bld, bln, bdn;
+  int rc = validate(a, &bld, &bln, &bdn);
+  if (rc != SSM_OK) return rc;
+  if (a->batch == 0 || a->dim == 0) return SSM_OK;
+  Plan pl;
+  rc = make_plan(a, true, &pl);
+  if (rc != SSM_OK) return rc;
+  return run_fwd(a, pl, a->workspace, stream);
+}
+
+int ssm_scan_fwd_noalloc(const ssm_scan_args* a, void* stream) {
+  int64_t bld, bln, bdn;
+  int rc = validate(a, &bld, &bln, &bdn);
+  if (rc != SSM_OK) return rc;
+  if (a->batch == 0 || a->dim == 0) return SSM_OK;
+  // the plan as if a workspace of any size were given; the caller's own
+  // workspace fields play no part
+  ssm_scan_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  Plan pl;
+  rc = make_plan(&b, false, &pl);
+  if (rc != SSM_OK) return rc;
+  void* ws = nullptr;
+  if (pl.splits > 1) {
+    if (pl.ws_state_bytes + pl.ws_dsum_bytes > ssm::kNoallocScratchBytes) {
+      if (a->time_splits > 1) return SSM_ERR_WORKSPACE;
+      pl.splits = 1;  // automatic splitting falls back to one segment
+      pl.seg_len = a->seqlen;
+      pl.ws_state_bytes = pl.ws_dsum_bytes = 0;
+    } else if (ssm::noalloc_scratch(&ws) != hipSuccess) {
+      return SSM_ERR_LAUNCH;
+    }
+  }
+  return run_fwd(&b, pl, ws, stream);
 }
 
 int64_t ssm_scan_bwd_workspace_bytes(const ssm_scan_bwd_args* a) {

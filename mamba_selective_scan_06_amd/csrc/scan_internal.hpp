@@ -44,6 +44,12 @@ constexpr int kNsplitTurn = 8;
 
 // Each launcher enqueues its kernels on `stream` and returns hipGetLastError().
 hipError_t launch_nsplit(const Problem& p, hipStream_t stream);
+
+// Size of the device array behind ssm_scan_fwd_noalloc (segment summaries of
+// a time-split forward), and its address on the current device (looked up
+// once per device).
+constexpr int64_t kNoallocScratchBytes = int64_t{8} << 20;
+hipError_t noalloc_scratch(void** out);
 hipError_t launch_lane(const Problem& p, hipStream_t stream);
 hipError_t launch_decode(const Problem& p, hipStream_t stream);
 hipError_t launch_state_copy(const Problem& p, hipStream_t stream);  // seqlen == 0: hT <- h0 or 0

@@ -115,6 +115,22 @@ def test_empty_problems_plan_and_workspace_queries():
         assert _fwd(a) == 0
 
 
+def test_noalloc_rejects_oversized_explicit_split_on_host():
+    # 64 x 16384 x 17 x 4 bytes of segment summaries > the 8 MiB device array:
+    # rejected before any HIP call; an automatic plan of the same shape stays
+    # within it (and needs no GPU to be planned)
+    lib = ssm.lib()
+    a = _args(shape=(1, 1 << 20, 16384, 16), time_splits=64)
+    base = FAKE
+    for name in ("x", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0", "hT", "y"):
+        setattr(a, name, base)
+        base += 1 << 40  # disjoint 1 TiB windows
+    assert lib.ssm_scan_fwd_noalloc(ctypes.byref(a), None) == -7
+    assert lib.ssm_scan_fwd_noalloc(None, None) == -1
+    assert lib.ssm_scan_fwd_noalloc(ctypes.byref(_args(shape=(0, 64, 128, 16), x=0, y=0)), None) == 0
+    assert lib.ssm_scan_fwd_noalloc(ctypes.byref(_args(x=FAKE + 2)), None) == -5
+
+
 def test_plan_and_workspace_queries():
     lib = ssm.lib()
     # the benchmark layer: 64 channel blocks x 4 batch rows = 256 blocks, one per compute unit, unsplit
