@@ -93,23 +93,73 @@ def stored_traffic(workload_name: str):
         return None
 
 
-def cpu_baseline(w, inp, max_threads=16, zoh=False):
-    """The fp64 oracle over the whole workload (every batch row, channel and
-    token), threaded over independent channels; only the C call is timed."""
+def cpu_info():
+    """(logical CPUs of the host, CPU model name from /proc/cpuinfo or None)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count() or 1, model
+
+
+def _slice_channels(inp, nd):
+    """The first nd channels of every batch row and token (chains are independent)."""
+    out = dict(inp)
+    for k in ("x", "delta", "z"):
+        if out.get(k) is not None:
+            out[k] = out[k][:, :, :nd].contiguous()
+    out["A"] = out["A"][:nd].contiguous()
+    for k in ("D", "delta_bias"):
+        if out.get(k) is not None:
+            out[k] = out[k][:nd].contiguous()
+    if out.get("h0") is not None:
+        out["h0"] = out["h0"][:, :nd].contiguous()
+    return out
+
+
+def cpu_baseline(w, inp, max_threads=16, zoh=False, what="the whole workload"):
+    """The fp64 oracle timed on the host: over all of `inp` (the whole workload)
+    on all usable cores (at most the 16 of a one-GPU share), and over a channel
+    slice on one thread; only the C calls are timed.  `value` is the all-cores
+    rate."""
     import oracle
-    threads = max(1, min(os.cpu_count() or 1, max_threads))
+    nproc, model = cpu_info()
+    threads = max(1, min(nproc, max_threads))
+    B_, L_, D_ = inp["x"].shape
+    N_ = inp["A"].shape[1]
     timing = {}
     oracle.scan(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["delta_bias"],
                 inp.get("h0"), threads=threads, timing=timing, zoh=zoh)
-    elems = w.elems
+    elems = B_ * L_ * D_ * N_
+    # one thread: the first channels of every row and token, about 1/16 of the work
+    nd = max(1, min(D_, D_ // 16))
+    sub = _slice_channels(inp, nd)
+    t1 = {}
+    oracle.scan(sub["x"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"], sub["delta_bias"],
+                sub.get("h0"), threads=1, timing=t1, zoh=zoh)
+    el1 = B_ * L_ * nd * N_
     return {
         "value": round(elems / timing["seconds"] / 1e9, 4),
         "unit": "GElem/s",
         "cores": timing["threads"],
         "kind": "oracle",
-        "sample": f"the whole workload (B={w.batch} L={w.seqlen} D={w.dim} N={w.dstate}, {elems} elements), "
-                  f"inputs widened to fp64 beforehand; {timing['seconds']:.2f} s on {timing['threads']} threads",
+        "sample": f"{what} (B={B_} L={L_} D={D_} N={N_}, {elems} elements), inputs widened to fp64 "
+                  f"beforehand; {timing['seconds']:.2f} s on {timing['threads']} threads",
+        "single_thread_value": round(el1 / t1["seconds"] / 1e9, 4),
+        "single_thread_sample": f"channels 0..{nd - 1} of every row and token ({el1} elements), "
+                                f"{t1['seconds']:.2f} s on 1 thread",
+        "nproc": nproc,
+        "cpu_model": model,
     }
+
+
+def io_dtype(w) -> str:
+    return "bf16" if "bfloat16" in str(w.dtype) else "f32"
 
 
 def _roofline(alg_bytes, kern_s, kernel):
@@ -174,11 +224,11 @@ def bench_chunked(w, args, ssm, torch):
         probe.workspace, probe.workspace_bytes = ws.data_ptr(), nbytes
     plan = ssm.plan(probe)
     ms_per_step = elapsed * 1e3 / steps
-    return {
+    out = {
         "metric": "scan GElem/s (B*L*D*N) over the chained calls + % HBM roofline per call",
         "value": round(w.elems / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GElem/s", "n_gpus": 1,
         "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": io_dtype(w), "state_dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
                    "io_dtype": str(w.dtype).replace("torch.", ""), "gate": w.gate, "calls": w.chunks,
                    "call_seqlen": Lc, "plan": {"variant": plan[0], "time_splits": plan[1]}},
@@ -186,6 +236,13 @@ def bench_chunked(w, args, ssm, torch):
         "calls_total_kernel_us": round(per_call_s * w.chunks * 1e6, 2),
         "roofline": _roofline(call_bytes, per_call_s, "scan_nsplit_kernel (+ state-only pass)"),
     }
+    out["roofline"]["traffic"] = stored_traffic(w.name)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle over the whole sequence) ...")
+        out["cpu_baseline"] = cpu_baseline(
+            w, inp, what=f"the whole {w.seqlen}-token sequence as one oracle run (bitwise equal to the "
+                         f"{w.chunks} chained oracle calls)")
+    return out
 
 
 def bench_decode(w, args, ssm, torch):
@@ -254,11 +311,11 @@ def bench_decode(w, args, ssm, torch):
     step_bytes = (4 if w.gate else 3) * bd * es + 2 * w.batch * w.dstate * es + w.dim * w.dstate * 4 + \
         2 * w.dim * 4 + 2 * bd * w.dstate * 4
     ms_per_pass = elapsed * 1e3 / passes
-    return {
+    out = {
         "metric": "scan GElem/s (B*D*N per token step) + % HBM roofline per step",
         "value": round(w.elems / (ms_per_pass * 1e-3) / 1e9, 2), "unit": "GElem/s", "n_gpus": 1,
         "steps": passes, "warmup": args.warmup, "ms_per_step": round(ms_per_pass, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": io_dtype(w), "state_dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
                    "io_dtype": str(w.dtype).replace("torch.", ""), "gate": w.gate, "decode_steps": w.steps,
                    "plan": {"variant": "decode", "in_place": True}},
@@ -271,6 +328,22 @@ def bench_decode(w, args, ssm, torch):
                   "note": "one pass of the decode steps captured in a HIP graph and replayed"},
         "roofline": _roofline(step_bytes, graph_step_s, "scan_decode_kernel"),
     }
+    out["roofline"]["traffic"] = stored_traffic(w.name)
+    if not args.no_cpu_baseline:
+        import torch as _t
+        cpu = {k: [] for k in ("x", "delta", "B", "C", "z")}
+        for t in range(w.steps):
+            st = workloads.make_decode_step(w, t)
+            for k in cpu:
+                if st[k] is not None:
+                    cpu[k].append(st[k])
+        stacked = {k: (_t.cat(v, dim=1) if v else None) for k, v in cpu.items()}
+        stacked.update({k: inp[k] for k in ("A", "D", "delta_bias", "h0")})
+        log("cpu baseline (oracle over the stacked decode steps) ...")
+        out["cpu_baseline"] = cpu_baseline(
+            w, stacked, what=f"the {w.steps} decode steps as one L={w.steps} oracle scan from the workload's h0 "
+                             f"(equal to {w.steps} single-token steps)")
+    return out
 
 
 def bench_backward(w, args, ssm, torch):
@@ -328,7 +401,7 @@ def bench_backward(w, args, ssm, torch):
         "metric": "backward scan GElem/s (B*L*D*N) + % HBM roofline",
         "value": round(w.elems / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GElem/s", "n_gpus": 1,
         "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": io_dtype(w), "state_dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "pass": "backward", "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "dstate": w.dstate, "io_dtype": str(w.dtype).replace("torch.", ""), "gate": w.gate,
                    "time_splits": splits, "workspace_bytes": nbytes},
@@ -396,7 +469,7 @@ def bench_conv(w, args, ssm, torch):
         "metric": "conv1d+SiLU prologue GElem/s (B*L*D) + % HBM roofline",
         "value": round(bld / (ms * 1e-3) / 1e9, 2), "unit": "GElem/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": io_dtype(w), "data": "synthetic",
         "config": {"workload": w.name, "pass": "conv1d_silu", "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "width": 4, "io_dtype": str(w.dtype).replace("torch.", "")},
         "roofline": _roofline(alg, kern_s, "conv_silu_kernel"),
@@ -681,7 +754,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": io_dtype(w),
+        "state_dtype": "f32",
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,

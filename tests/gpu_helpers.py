@@ -2,6 +2,8 @@
 binding and the fp64 oracle on the same seeded inputs, and compare."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -25,8 +27,13 @@ def gpu_scan(dinp, **kw):
     return y.float().cpu().double().numpy(), hT.cpu().double().numpy()
 
 
-def oracle_scan(inp):
-    return oracle.scan(*(inp.get(k) for k in TENSORS))
+# oracle threads: the host's share of a one-GPU machine is 16 cores
+ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_scan(inp, **kw):
+    kw.setdefault("threads", ORACLE_THREADS)
+    return oracle.scan(*(inp.get(k) for k in TENSORS), **kw)
 
 
 def select(inp, bidx, didx):

@@ -60,8 +60,12 @@ def test_rows_beyond_32bit_offsets(wi, bsz, L, dim):
     hT = torch.empty((bsz, dim, w.dstate), dtype=torch.float32, device=DEV)
     a = ssm.make_args(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["delta_bias"], None, hT, y)
     assert ssm.plan(a)[0] == "nsplit"
+    # time_splits=1 runs the windowed kernel as one segment over the whole row;
+    # 0 lets the planner split (it takes 3 segments here given a workspace)
+    a.time_splits = 1
+    assert ssm.plan(a) == ("nsplit", 1)
     ci = torch.as_tensor(chans, device=DEV)
-    for splits in (0, 4):
+    for splits in (1, 0, 4):
         y.fill_(float("nan"))
         ssm.scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["delta_bias"],
                      out=y, final_state_out=hT, time_splits=splits)
@@ -78,7 +82,8 @@ def test_rows_beyond_32bit_offsets(wi, bsz, L, dim):
 
 def test_row_beyond_2gib_zoh_generic_decays():
     """The windowed instantiation with the zero-order hold and every decay its
-    own exp (random decay rates, generic path forced), unsplit and in 3 segments."""
+    own exp (random decay rates, generic path forced), as one segment
+    (time_splits=1) and in 3 segments."""
     w = workloads.WORKLOADS[1]
     bsz, L, dim = 1, 262_152, 4104
     inp = workloads.make_large_inputs(w, batch=bsz, seqlen=L, dim=dim, seed_extra=(3,))
@@ -91,7 +96,7 @@ def test_row_beyond_2gib_zoh_generic_decays():
     del inp
     gc.collect()
     ci = torch.as_tensor(chans, device=DEV)
-    for splits in (0, 3):
+    for splits in (1, 3):
         y, hT = ssm.scan_fwd(*(d.get(k) for k in TENS), return_final_state=True, zoh=True, generic_a=True,
                              time_splits=splits)
         torch.cuda.synchronize()
