@@ -195,7 +195,8 @@ def bench_chunked(w, args, ssm, torch):
             if events is not None:
                 events[c][0].record(stream)
             ssm.scan_fwd(ch["x"], ch["delta"], A, ch["B"], ch["C"], D, ch["z"], bias,
-                         h_in if c > 0 else None, out=ys[c], final_state_out=h_out, time_splits=args.time_splits)
+                         h_in if c > 0 else None, out=ys[c], final_state_out=h_out, time_splits=args.time_splits,
+                         carry_scan=args.carry_scan)
             if events is not None:
                 events[c][1].record(stream)
 
@@ -231,7 +232,8 @@ def bench_chunked(w, args, ssm, torch):
         "scaling": "weak", "vs_baseline": None, "dtype": io_dtype(w), "state_dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
                    "io_dtype": str(w.dtype).replace("torch.", ""), "gate": w.gate, "calls": w.chunks,
-                   "call_seqlen": Lc, "plan": {"variant": plan[0], "time_splits": plan[1]}},
+                   "call_seqlen": Lc, "plan": {"variant": plan[0], "time_splits": plan[1],
+                                               "carry": "scan" if args.carry_scan else "serial fold"}},
         "per_call_us": round(per_call_s * 1e6, 2),
         "calls_total_kernel_us": round(per_call_s * w.chunks * 1e6, 2),
         "roofline": _roofline(call_bytes, per_call_s, "scan_nsplit_kernel (+ state-only pass)"),
@@ -630,6 +632,8 @@ def main():
     ap.add_argument("--time-splits", type=int, default=0)
     ap.add_argument("--generic-a", action="store_true", help="never take the structured-decay path")
     ap.add_argument("--zoh", action="store_true", help="zero-order-hold input term instead of the Euler one")
+    ap.add_argument("--carry-scan", action="store_true",
+                    help="time-split calls compose segment summaries with the wave-level scan launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true", help="time ssm_scan_bwd (all gradients) instead")
     ap.add_argument("--prologue", action="store_true", help="time the conv1d + SiLU prologue on x instead")
@@ -717,7 +721,7 @@ def main():
         s = sets[i % 2]
         ssm.scan_fwd(s["x"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], s["delta_bias"], s["h0"],
                      out=y[i % 2], final_state_out=hT[i % 2], workspace=ws, variant=args.variant,
-                     time_splits=args.time_splits, generic_a=args.generic_a, zoh=args.zoh)
+                     time_splits=args.time_splits, generic_a=args.generic_a, zoh=args.zoh, carry_scan=args.carry_scan)
 
     for i in range(args.warmup):
         step(i)

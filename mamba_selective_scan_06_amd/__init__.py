@@ -30,6 +30,7 @@ VARIANTS = {"auto": 0, "nsplit": 1, "lane": 2, "decode": 3}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 FLAG_GENERIC_A = 1
 FLAG_ZOH = 2
+FLAG_CARRY_SCAN = 4
 
 # Exported symbols the header declares (checked by the tests).
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_noalloc", "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_scan_bwd",
@@ -176,7 +177,8 @@ def _check(name, t, shape, dtype, device):
 
 
 def make_args(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, hT=None, y=None,
-              workspace=None, variant="auto", time_splits=0, generic_a=False, zoh=False) -> ScanArgs:
+              workspace=None, variant="auto", time_splits=0, generic_a=False, zoh=False,
+              carry_scan=False) -> ScanArgs:
     """Check shapes/dtypes/devices of torch tensors and fill an ssm_scan_args
     (zoh: zero-order-hold input term instead of the Euler one)."""
     if x.dim() != 3:
@@ -206,7 +208,7 @@ def make_args(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, hT=No
     a = ScanArgs()
     a.batch, a.seqlen, a.dim, a.dstate = bsz, L, dim, N
     a.dtype = DTYPE_F32 if io == torch.float32 else DTYPE_BF16
-    a.flags = (FLAG_GENERIC_A if generic_a else 0) | (FLAG_ZOH if zoh else 0)
+    a.flags = (FLAG_GENERIC_A if generic_a else 0) | (FLAG_ZOH if zoh else 0) | (FLAG_CARRY_SCAN if carry_scan else 0)
     a.x, a.delta, a.A, a.B, a.C = _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C)
     a.D, a.z, a.delta_bias, a.h0, a.hT, a.y = _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(hT), _ptr(y)
     a.workspace = _ptr(workspace)
@@ -233,11 +235,13 @@ def workspace_bytes(args: ScanArgs) -> int:
 
 def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
              return_final_state=False, out=None, final_state_out=None, workspace=None,
-             variant="auto", time_splits=0, generic_a=False, zoh=False):
+             variant="auto", time_splits=0, generic_a=False, zoh=False, carry_scan=False):
     """Selective scan forward on the GPU.  Returns y, or (y, hT) with
     return_final_state=True.  `final_state_out` may be h0 itself (in-place state
     update).  zoh=True discretises the input term with the zero-order hold,
-    (exp(delta A) - 1) / A * B x, instead of delta B x.  Launches on torch's
+    (exp(delta A) - 1) / A * B x, instead of delta B x.  carry_scan=True makes a
+    time-split call compose the segment summaries with the wave-level
+    associative scan launch instead of folding them serially in each block.  Launches on torch's
     current HIP stream and does not synchronise."""
     if not x.is_cuda:
         raise ValueError("scan_fwd runs on the GPU only: move the tensors to a HIP device")
@@ -246,7 +250,8 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
     hT = final_state_out
     if hT is None and return_final_state:
         hT = torch.empty((x.shape[0], x.shape[2], A.shape[1]), dtype=torch.float32, device=x.device)
-    args = make_args(x, delta, A, B, C, D, z, delta_bias, h0, hT, y, None, variant, time_splits, generic_a, zoh)
+    args = make_args(x, delta, A, B, C, D, z, delta_bias, h0, hT, y, None, variant, time_splits, generic_a, zoh,
+                     carry_scan)
     if workspace is None:
         nbytes = L_.ssm_scan_workspace_bytes(ctypes.byref(args))
         if nbytes < 0:

@@ -28,7 +28,7 @@ NSPLIT_INST = [(s, k, w) for s in ("float", "uint16_t") for k in (1, 2, 4, 8, 16
 UNITS = [("api.cpp", [], "api"), ("nsplit_dispatch.cpp", [], "nsplit_dispatch"),
          ("scan_lane.hip", [], "scan_lane"), ("scan_decode.hip", [], "scan_decode"),
          ("scan_bwd.hip", [], "scan_bwd"), ("conv_prologue.hip", [], "conv_prologue"),
-         ("ssd_fwd.hip", [], "ssd_fwd"), ("noalloc_scratch.hip", [], "noalloc_scratch"),
+         ("ssd_fwd.hip", [], "ssd_fwd"), ("noalloc_scratch.hip", [], "noalloc_scratch"), ("carry_scan.hip", [], "carry_scan"),
          ("scan_bwd_inst.hip", ["-DBWD_S=float"], "bwd_f32"), ("scan_bwd_inst.hip", ["-DBWD_S=uint16_t"], "bwd_bf16")] + [
     ("nsplit_inst.hip", [f"-DNSPLIT_S={s}", f"-DNSPLIT_K={k}", f"-DNSPLIT_WIN={w}"],
      f"nsplit_{'f32' if s == 'float' else 'bf16'}_k{k}{'_win' if w else ''}")

@@ -32,6 +32,7 @@ struct Problem {
 
 constexpr int kFlagGenericA = 1;
 constexpr int kFlagZoh = 2;
+constexpr int kFlagCarryScan = 4;  // time split: compose segment summaries with the wave-level scan launch
 
 // Tile length (timesteps) of the NSPLIT family; segment lengths are multiples of it.
 constexpr int kNsplitTile = 16;
@@ -44,6 +45,9 @@ constexpr int kNsplitTurn = 8;
 
 // Each launcher enqueues its kernels on `stream` and returns hipGetLastError().
 hipError_t launch_nsplit(const Problem& p, hipStream_t stream);
+// Time split: turn the segment summaries in p.ws_state into the state
+// entering each segment (wave-level associative scan; carry_scan.hip).
+hipError_t launch_carry_scan(const Problem& p, hipStream_t stream);
 
 // Size of the device array behind ssm_scan_fwd_noalloc (segment summaries of
 // a time-split forward), and its address on the current device (looked up

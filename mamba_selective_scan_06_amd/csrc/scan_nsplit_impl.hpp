@@ -71,11 +71,17 @@
 // Time splitting (for problems with too few channels to fill the GPU): the
 // sequence is cut into segments.  A first launch (STATE_ONLY) runs every
 // segment but the last from a zero state and stores its end state H and the
-// sum of its softplus(delta).  The second launch starts segment s from
-//   h = h0, then h <- exp(A_n sum_j delta) h + H_j for j = 0..s-1
-// (the associative combine (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) of the
-// affine steps, with the product of a segment's decays written as one exp of
-// A_n times its summed step size), and runs the full scan from there.
+// sum of its softplus(delta).  A segment is then the affine map
+// h -> exp(A_n sum delta) h + H, and the maps compose with the associative
+// operator (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2).  Each block of the full
+// pass folds the summaries of the segments before its own, one after the
+// other (at most 63 steps per state, a few percent of a segment's work), and
+// runs its segment from there.  With SSM_FLAG_CARRY_SCAN a small launch
+// between the two (carry_scan.hip) composes all summaries with a wave-level
+// associative scan and leaves the state entering every segment in the
+// workspace instead; measured, the extra launch costs more than the folds it
+// saves (10 segments: 104-106 against 102-104 us per call; 64 segments:
+// equal), so the fold is the default.
 #pragma once
 
 #include <type_traits>
@@ -946,15 +952,22 @@ __global__ __launch_bounds__(512, 1) void scan_nsplit_kernel(
 #pragma unroll
       for (int k = 0; k < K; ++k) h[k] = 0.0f;
     } else {
+      if (s > 0 && (flags & kFlagCarryScan)) {
+        // the state entering this segment, composed by the carry scan
+        const int64_t seg = b * splits + s - 1;
 #pragma unroll
-      for (int k = 0; k < K; ++k) h[k] = h0 ? h0[(b * D + d) * N + sw * K + k] : 0.0f;
-      // Carry in the summaries of the segments before this one.
-      for (int j = 0; j < s; ++j) {
-        const int64_t seg = b * splits + j;
-        const float sdl = ws_dsum[seg * D + d];
+        for (int k = 0; k < K; ++k) h[k] = ws_state[(seg * D + d) * N + sw * K + k];
+      } else {
 #pragma unroll
-        for (int k = 0; k < K; ++k)
-          h[k] = __builtin_fmaf(fast_exp2(A2[k] * sdl), h[k], ws_state[(seg * D + d) * N + sw * K + k]);
+        for (int k = 0; k < K; ++k) h[k] = h0 ? h0[(b * D + d) * N + sw * K + k] : 0.0f;
+        // Carry in the summaries of the segments before this one, in order.
+        for (int j = 0; j < s; ++j) {
+          const int64_t seg = b * splits + j;
+          const float sdl = ws_dsum[seg * D + d];
+#pragma unroll
+          for (int k = 0; k < K; ++k)
+            h[k] = __builtin_fmaf(fast_exp2(A2[k] * sdl), h[k], ws_state[(seg * D + d) * N + sw * K + k]);
+        }
       }
     }
     if (structured) {
@@ -1024,8 +1037,12 @@ template <typename S, int K, bool ZOH, bool WIN>
 hipError_t launch_nsplit_z(const Problem& p, hipStream_t stream) {
   if (p.splits > 1) {
     launch_one<S, K, true, false, ZOH, WIN>(p, stream, static_cast<unsigned>(p.splits - 1));
-    const hipError_t e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (p.flags & kFlagCarryScan) {
+      e = launch_carry_scan(p, stream);
+      if (e != hipSuccess) return e;
+    }
   }
   if (p.z)
     launch_one<S, K, false, true, ZOH, WIN>(p, stream, static_cast<unsigned>(p.splits));

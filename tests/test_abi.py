@@ -60,7 +60,7 @@ def _fwd(a):
     (dict(shape=(2**40, 2**20, 2**20, 16)), -2),
     (dict(x=0), -1), (dict(delta=0), -1), (dict(A=0), -1), (dict(B=0), -1), (dict(C=0), -1), (dict(y=0), -1),
     (dict(x=FAKE + 2), -5), (dict(z=FAKE + 8), -5), (dict(hT=FAKE + 4), -5),
-    (dict(flags=4), -9), (dict(flags=-1), -9), (dict(variant=9), -9), (dict(time_splits=-1), -9),
+    (dict(flags=8), -9), (dict(flags=-1), -9), (dict(variant=9), -9), (dict(time_splits=-1), -9),
     (dict(variant=3), -9),  # decode needs seqlen == 1
     (dict(variant=2, time_splits=4), -9),  # splitting is NSPLIT only
     (dict(shape=(2, 64, 128, 12), variant=1), -9),  # NSPLIT needs N in {4,8,16,32,64}
@@ -183,6 +183,6 @@ def test_plan_long_rows_stay_on_the_main_kernel():
 def test_zoh_flag_accepted():
     """SSM_FLAG_ZOH (alone or with SSM_FLAG_GENERIC_A) passes the host checks;
     with batch 0 nothing is launched."""
-    for f in (2, 3):
+    for f in (2, 3, 4, 7):  # SSM_FLAG_CARRY_SCAN (4) as well
         assert _fwd(_args(shape=(0, 8, 8, 16), flags=f)) == 0
         assert ssm.lib().ssm_scan_plan(ctypes.byref(_args(flags=f))) >= 0

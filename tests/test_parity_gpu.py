@@ -97,6 +97,28 @@ def test_time_splits_fp32(splits):
     check("hT", hT, hr, w.dtype)
 
 
+# Carry combine of time splits: the wave-level associative scan in rows of 16,
+# 32 and 64 lanes (up to 16, 32 and 63 summaries) against the serial fold and
+# the oracle, with an initial state, structured and generic decays.
+@pytest.mark.parametrize("splits", [2, 13, 17, 18, 33, 34, 64])
+@pytest.mark.parametrize("generic_a", [False, True])
+def test_carry_scan_against_serial_fold(splits, generic_a):
+    w = W[0]
+    # segments of 16 tokens and a last one of 5: exactly `splits` segments
+    inp = _case(w, batch=2, seqlen=16 * (splits - 1) + 5, dim=72)
+    g = np.random.default_rng(splits)
+    inp["h0"] = torch.from_numpy(g.normal(0, 1.0, size=(2, 72, 16)).astype(np.float32))
+    d = to_dev(inp)
+    y, hT = gpu_scan(d, time_splits=splits, generic_a=generic_a, carry_scan=True)
+    ys, hs = gpu_scan(d, time_splits=splits, generic_a=generic_a)
+    yr, hr = oracle_scan(inp)
+    check("y scan", y, yr, w.dtype)
+    check("hT scan", hT, hr, w.dtype)
+    check("y serial", ys, yr, w.dtype)
+    check("hT serial", hs, hr, w.dtype)
+    assert workloads.rel_err(hT, hs) <= 1e-5
+
+
 def test_edge_lengths_and_shapes():
     w = W[0]
     for (b, L, dim) in [(1, 1, 1), (1, 2, 1), (3, 1, 65), (1, 17, 64), (2, 15, 3), (1, 16, 128), (1, 33, 200)]:
