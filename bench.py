@@ -746,7 +746,7 @@ def main():
     kern_avg_s = float(np.mean(kern_ms)) * 1e-3
     alg = algorithmic_bytes(w)
     achieved = alg / kern_avg_s / 1e9
-    traffic = None if args.zoh else stored_traffic(w.name)  # counters were taken on the Euler kernel
+    traffic = stored_traffic(w.name + ("_zoh" if args.zoh else ""))  # counters of the kernel this line runs
     out = {
         "metric": "scan GElem/s (B*L*D*N) + % HBM roofline, B4 L8192 D4096 N16 bf16",
         "value": round(value, 2),
