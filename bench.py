@@ -524,11 +524,15 @@ def bench_ssd(args, ssm, torch):
     alg = (2 * toks * w.headdim * 2 + toks * 2 + 2 * w.batch * w.seqlen * w.ngroups * w.dstate * 2
            + w.batch * w.nheads * w.headdim * w.dstate * 4 + 3 * w.nheads * 4)  # x, y, dt, B, C, hT, A/D/bias
     Q, N, P = 64, w.dstate, w.headdim
-    flops = toks * 2 * (Q * N + Q * P + 2 * N * P)  # C B^T, M X, C H^T, the state update: per token and head
+    # the method's own work: per token and head, the state update (N P multiply-adds) and the readout
+    # (N P multiply-adds), 4 N P flops; the chunked form does 2 (Q N + Q P + 2 N P) on the matrix cores
+    method_flops = toks * 4 * N * P
+    chunked_flops = toks * 2 * (Q * N + Q * P + 2 * N * P)
     ms = elapsed * 1e3 / steps
     roof = _roofline(alg, kern_s, "ssd_fwd_kernel")
-    roof["mfma_tflops"] = round(flops / kern_s / 1e12, 2)
-    roof["mfma_frac_bf16_dense"] = round(flops / kern_s / 2.5e15, 4)
+    roof["method_tflops"] = round(method_flops / kern_s / 1e12, 2)
+    roof["method_frac_bf16_dense"] = round(method_flops / kern_s / 2.5e15, 4)
+    roof["chunked_form_tflops"] = round(chunked_flops / kern_s / 1e12, 2)
     out = {
         "metric": "SSD layer GElem/s (B*L*H*P*N) + % HBM roofline",
         "value": round(w.elems / (ms * 1e-3) / 1e9, 2), "unit": "GElem/s", "n_gpus": 1, "steps": steps,
@@ -591,11 +595,15 @@ def bench_gla(args, ssm, torch):
     alg = (2 * toks * w.headdim * 2 + 2 * w.batch * w.seqlen * w.ngroups * w.dstate * 2
            + (2 * toks * 4 if w.gated else 0) + w.batch * w.nheads * w.headdim * w.dstate * 4)  # v, y, q, k, gates, hT
     Q, N, P = 64, w.dstate, w.headdim
-    flops = toks * 2 * (Q * N + Q * P + 2 * N * P)  # Q K^T, M V, Q S^T, the state update: per token and head
+    # the recurrence's own work per token and head: state update and readout, 4 N P flops; the chunked form
+    # does 2 (Q N + Q P + 2 N P) on the matrix cores (Q K^T, M V, Q S^T, the state update)
+    method_flops = toks * 4 * N * P
+    chunked_flops = toks * 2 * (Q * N + Q * P + 2 * N * P)
     ms = elapsed * 1e3 / steps
     roof = _roofline(alg, kern_s, "ssd_fwd_kernel")
-    roof["mfma_tflops"] = round(flops / kern_s / 1e12, 2)
-    roof["mfma_frac_bf16_dense"] = round(flops / kern_s / 2.5e15, 4)
+    roof["method_tflops"] = round(method_flops / kern_s / 1e12, 2)
+    roof["method_frac_bf16_dense"] = round(method_flops / kern_s / 2.5e15, 4)
+    roof["chunked_form_tflops"] = round(chunked_flops / kern_s / 1e12, 2)
     out = {
         "metric": "gated linear attention GElem/s (B*L*H*P*N) + % HBM roofline",
         "value": round(w.elems / (ms * 1e-3) / 1e9, 2), "unit": "GElem/s", "n_gpus": 1, "steps": steps,
