@@ -490,8 +490,9 @@ def bench_conv(w, args, ssm, torch):
 
 
 def bench_ssd(args, ssm, torch):
-    """One step = one ssm_ssd_fwd over the Mamba-2-shaped layer (B4 L8192 H64 P64
-    G1 N128, bf16, hT returned)."""
+    """One step = one ssm_ssd_fwd over a Mamba-2-shaped layer (default B4 L8192
+    H64 P64 G1 N128, bf16, hT returned).  With few (b, h) pairs the library cuts
+    time into segments: a step is then both launches (state-only pass, full pass)."""
     import workloads
     w = workloads.SSD_BY_NAME[args.ssd]
     dev = torch.device("cuda:0")
@@ -503,9 +504,17 @@ def bench_ssd(args, ssm, torch):
     ys = [torch.empty_like(xs[0]) for _ in xs]
     hT = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    # segment summaries (time-split calls): allocated here, outside the timed region
+    a0 = ssm.make_ssd_args(xs[0], *(d[k] for k in names), None, hT, ys[0], time_splits=args.time_splits)
+    nws = ssm.ssd_workspace_bytes(a0)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    a0.workspace, a0.workspace_bytes = (ws.data_ptr() if nws else None), nws
+    splits = ssm.ssd_plan(a0)
+    log(f"time segments {splits}, workspace {nws} B")
 
     def step(i):
-        ssm.ssd_fwd(xs[i % 2], *(d[k] for k in names), None, out=ys[i % 2], final_state_out=hT)
+        ssm.ssd_fwd(xs[i % 2], *(d[k] for k in names), None, out=ys[i % 2], final_state_out=hT,
+                    time_splits=args.time_splits, workspace=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -529,7 +538,7 @@ def bench_ssd(args, ssm, torch):
     method_flops = toks * 4 * N * P
     chunked_flops = toks * 2 * (Q * N + Q * P + 2 * N * P)
     ms = elapsed * 1e3 / steps
-    roof = _roofline(alg, kern_s, "ssd_fwd_kernel")
+    roof = _roofline(alg, kern_s, "ssd_fwd_kernel" if splits == 1 else "ssd_fwd_kernel, state-only + full pass")
     roof["method_tflops"] = round(method_flops / kern_s / 1e12, 2)
     roof["method_frac_bf16_dense"] = round(method_flops / kern_s / 2.5e15, 4)
     roof["chunked_form_tflops"] = round(chunked_flops / kern_s / 1e12, 2)
@@ -539,7 +548,8 @@ def bench_ssd(args, ssm, torch):
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
-                   "headdim": w.headdim, "ngroups": w.ngroups, "dstate": w.dstate, "chunk": Q},
+                   "headdim": w.headdim, "ngroups": w.ngroups, "dstate": w.dstate, "chunk": Q,
+                   "time_splits": splits},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
@@ -570,13 +580,18 @@ def bench_gla(args, ssm, torch):
     hT = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     # the feature map's once-per-call pass needs a workspace; allocated here, outside the timed region
-    nws = ssm.gla_workspace_bytes(ssm.make_gla_args(d["q"], d["k"], vs[0], d["log_f"], d["in_gate"], None, hT,
-                                                    ys[0], w.feature_map))
+    # (and the time-segment summaries)
+    a0 = ssm.make_gla_args(d["q"], d["k"], vs[0], d["log_f"], d["in_gate"], None, hT, ys[0], w.feature_map,
+                           args.time_splits)
+    nws = ssm.gla_workspace_bytes(a0)
     ws = torch.empty(max(nws, 0), dtype=torch.uint8, device=dev)
+    a0.workspace, a0.workspace_bytes = (ws.data_ptr() if nws else None), nws
+    splits = ssm.gla_plan(a0)
+    log(f"time segments {splits}, workspace {nws} B")
 
     def step(i):
         ssm.gla_fwd(d["q"], d["k"], vs[i % 2], d["log_f"], d["in_gate"], None, feature_map=w.feature_map,
-                    out=ys[i % 2], final_state_out=hT, workspace=ws)
+                    out=ys[i % 2], final_state_out=hT, workspace=ws, time_splits=args.time_splits)
 
     for i in range(args.warmup):
         step(i)
@@ -600,7 +615,7 @@ def bench_gla(args, ssm, torch):
     method_flops = toks * 4 * N * P
     chunked_flops = toks * 2 * (Q * N + Q * P + 2 * N * P)
     ms = elapsed * 1e3 / steps
-    roof = _roofline(alg, kern_s, "ssd_fwd_kernel")
+    roof = _roofline(alg, kern_s, "ssd_fwd_kernel" if splits == 1 else "ssd_fwd_kernel, state-only + full pass")
     roof["method_tflops"] = round(method_flops / kern_s / 1e12, 2)
     roof["method_frac_bf16_dense"] = round(method_flops / kern_s / 2.5e15, 4)
     roof["chunked_form_tflops"] = round(chunked_flops / kern_s / 1e12, 2)
@@ -611,7 +626,7 @@ def bench_gla(args, ssm, torch):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
                    "headdim": w.headdim, "ngroups": w.ngroups, "dstate": w.dstate, "gated": w.gated,
-                   "feature_map": "elu+1" if w.feature_map else None, "chunk": Q,
+                   "feature_map": "elu+1" if w.feature_map else None, "chunk": Q, "time_splits": splits,
                    **({"feature_map_pass": "once per call, into the workspace"} if w.feature_map else {})},
         "roofline": roof,
     }

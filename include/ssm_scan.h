@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 2
+#define SSM_SCAN_ABI_VERSION 3
 
 /* Element type of x, delta, B, C, z and y.  A, D, delta_bias, h0, hT are
  * always fp32, and all arithmetic (state, accumulation) is fp32. */
@@ -255,6 +255,21 @@ int ssm_conv1d_silu_fwd(const ssm_conv_args *args, void *stream);
  * evaluated in the chunked matrix (dual) form on the matrix cores.
  * Layouts: x, y (B, L, H, P); dt (B, L, H); B, C (B, L, G, N) in bf16;
  * A, D, dt_bias (H) and the state S0 / ST (B, H, P, N) fp32.
+ * One workgroup walks the chunks of one (b, h) in order, so with B*H well
+ * under the device's 256 compute units most of them sit idle.  Time
+ * splitting cuts the sequence into S segments of whole 64-token chunks: a
+ * state-only pass gives each of the first S-1 segments its end state from
+ * zero and its total log decay (the same recurrence restricted to the
+ * segment, section 4.1's h_t = A_t h_{t-1} + B_t x_t composed over it), and
+ * the full pass starts segment s from h0 advanced through segments 0..s-1
+ * with those summaries (S_in = exp(sum of log decays) S_prev + S_seg).
+ * Results agree with the unsplit call to fp32 rounding.  time_splits: 0
+ * picks S from the shape, the most segments for which B*H*S workgroups fit
+ * the 256 compute units with segments of at least 4 chunks, at most 64 (so
+ * S = 1 once B*H > 128), and S = 1 when workspace is NULL or smaller than
+ * ssm_ssd_workspace_bytes reports; 1 never splits; S > 1 asks for S segments
+ * (fewer when L has fewer chunks; SSM_ERR_WORKSPACE without a large enough
+ * workspace).
  * Limits of this version: dtype SSM_DTYPE_BF16, headdim P = 64,
  * dstate N in {64, 128, 256} (SSM_ERR_VARIANT otherwise). */
 typedef struct ssm_ssd_args {
@@ -262,7 +277,7 @@ typedef struct ssm_ssd_args {
   int64_t nheads, headdim;    /* H >= 1, P = 64                                       */
   int64_t ngroups, dstate;    /* G divides H; N in {64, 128, 256}                     */
   int32_t dtype;              /* SSM_DTYPE_BF16                                       */
-  int32_t reserved;           /* must be 0                                            */
+  int32_t time_splits;        /* 0 automatic, 1 none, S > 1 segments (see above)       */
   const void *x;              /* (B, L, H, P)                                required */
   const void *dt;             /* (B, L, H) raw step, before bias and softplus required */
   const float *A;             /* (H) decay rate per head (normally < 0)      required */
@@ -273,11 +288,28 @@ typedef struct ssm_ssd_args {
   const float *h0;            /* (B, H, P, N) initial state or NULL (zeros)            */
   float *hT;                  /* (B, H, P, N) final state out or NULL                  */
   void *y;                    /* (B, L, H, P) out                            required */
+  void *workspace;            /* device scratch for the segment summaries, or NULL;
+                                 16-byte aligned, overwritten, must not overlap any
+                                 tensor                                              */
+  int64_t workspace_bytes;    /* its size in bytes                                     */
 } ssm_ssd_args;
 
 /* Errors as for ssm_scan_fwd; y and hT must not overlap any input or each
- * other (hT may not alias h0).  With L == 0, hT receives h0 (or zeros). */
+ * other (hT may not alias h0); SSM_ERR_VARIANT for time_splits < 0.  With
+ * L == 0, hT receives h0 (or zeros). */
 int ssm_ssd_fwd(const ssm_ssd_args *args, void *stream);
+
+/* Bytes of workspace ssm_ssd_fwd uses for the segment summaries with these
+ * arguments' time_splits (0 when the call would not split): (B, S-1, H, P, N)
+ * fp32 end states, then (B, S-1, H) fp32 total log decays, each part starting
+ * at a 256-byte boundary.  Host-only; negative SSM_ERR_* for invalid
+ * arguments (the workspace fields are not checked here). */
+int64_t ssm_ssd_workspace_bytes(const ssm_ssd_args *args);
+
+/* Segments ssm_ssd_fwd would use with these arguments and a workspace of
+ * workspace_bytes (1: no split).  Host-only; negative SSM_ERR_* as the call
+ * would return them, SSM_ERR_WORKSPACE included. */
+int ssm_ssd_plan(const ssm_ssd_args *args);
 
 /* ---- Gated linear attention / mLSTM matrix-state recurrence ----------------
  * Linear attention as a recurrence (HedgeMamba review, stage 2:
@@ -300,6 +332,8 @@ int ssm_ssd_fwd(const ssm_ssd_args *args, void *stream);
  * an elementwise pass that writes phi(k) and phi(q) to the workspace; without
  * one (NULL or too small) every head's workgroup applies it to its group's
  * keys and queries again.  Both give bitwise the same results.
+ * time_splits as for ssm_ssd_fwd: the workspace then also holds the segment
+ * summaries, after phi(k) and phi(q) when the feature map is applied once.
  * Limits of this version: dtype SSM_DTYPE_BF16, headdim P = 64,
  * dstate N in {64, 128, 256} (SSM_ERR_VARIANT otherwise). */
 typedef struct ssm_gla_args {
@@ -316,20 +350,29 @@ typedef struct ssm_gla_args {
   const float *h0;            /* (B, H, P, N) initial state or NULL (zeros)            */
   float *hT;                  /* (B, H, P, N) final state out or NULL                  */
   void *y;                    /* (B, L, H, P) out                            required */
-  void *workspace;            /* device scratch for phi(k), phi(q), or NULL; 16-byte
-                                 aligned, overwritten, must not overlap any tensor  */
+  void *workspace;            /* device scratch for phi(k), phi(q) and the segment
+                                 summaries, or NULL; 16-byte aligned, overwritten,
+                                 must not overlap any tensor                          */
   int64_t workspace_bytes;    /* its size in bytes                                     */
+  int32_t time_splits;        /* 0 automatic, 1 none, S > 1 segments (ssm_ssd_args)    */
+  int32_t reserved;           /* must be 0                                            */
 } ssm_gla_args;
 
 /* Errors as for ssm_ssd_fwd (SSM_ERR_VARIANT also for feature_map outside
- * {0, 1}); y and hT must not overlap any input or each other.  With L == 0,
- * hT receives h0 (or zeros). */
+ * {0, 1} or reserved != 0); y and hT must not overlap any input or each
+ * other.  With L == 0, hT receives h0 (or zeros). */
 int ssm_gla_fwd(const ssm_gla_args *args, void *stream);
 
-/* Bytes of workspace ssm_gla_fwd uses to apply the feature map once per call
- * (0 without a feature map).  Host-only; negative SSM_ERR_* for invalid
- * arguments (the workspace fields are not checked here). */
+/* Bytes of workspace ssm_gla_fwd uses: phi(k) and phi(q), each (B, L, G, N)
+ * bf16, with the feature map, then the segment summaries laid out as for
+ * ssm_ssd_workspace_bytes when the call would split; every part starts at a
+ * 256-byte boundary.  With a smaller workspace, an automatic split is dropped
+ * first, then the feature-map pass.  Host-only; negative SSM_ERR_* for
+ * invalid arguments (the workspace fields are not checked here). */
 int64_t ssm_gla_workspace_bytes(const ssm_gla_args *args);
+
+/* Segments ssm_gla_fwd would use (as ssm_ssd_plan). */
+int ssm_gla_plan(const ssm_gla_args *args);
 
 /* Static, human-readable text for a status code. */
 const char *ssm_scan_strerror(int code);

@@ -31,11 +31,13 @@ VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 FLAG_GENERIC_A = 1
 FLAG_ZOH = 2
 FLAG_CARRY_SCAN = 4
+ABI_VERSION = 3  # SSM_SCAN_ABI_VERSION of include/ssm_scan.h
 
 # Exported symbols the header declares (checked by the tests).
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_noalloc", "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_scan_bwd",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd_plan", "ssm_conv1d_silu_fwd", "ssm_ssd_fwd",
-           "ssm_gla_fwd", "ssm_gla_workspace_bytes", "ssm_scan_strerror", "ssm_scan_abi_version")
+           "ssm_ssd_workspace_bytes", "ssm_ssd_plan", "ssm_gla_fwd", "ssm_gla_workspace_bytes", "ssm_gla_plan",
+           "ssm_scan_strerror", "ssm_scan_abi_version")
 
 
 class ScanArgs(ctypes.Structure):
@@ -84,10 +86,11 @@ class SsdArgs(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
         ("headdim", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dstate", ctypes.c_int64),
-        ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("time_splits", ctypes.c_int32),
         ("x", ctypes.c_void_p), ("dt", ctypes.c_void_p), ("A", ctypes.c_void_p),
         ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p),
         ("dt_bias", ctypes.c_void_p), ("h0", ctypes.c_void_p), ("hT", ctypes.c_void_p), ("y", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -101,6 +104,7 @@ class GlaArgs(ctypes.Structure):
         ("log_f", ctypes.c_void_p), ("in_gate", ctypes.c_void_p),
         ("h0", ctypes.c_void_p), ("hT", ctypes.c_void_p), ("y", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
+        ("time_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -139,15 +143,21 @@ def lib() -> ctypes.CDLL:
         L.ssm_ssd_fwd.restype = ctypes.c_int
         L.ssm_gla_fwd.argtypes = [ctypes.POINTER(GlaArgs), ctypes.c_void_p]
         L.ssm_gla_fwd.restype = ctypes.c_int
+        L.ssm_ssd_workspace_bytes.argtypes = [ctypes.POINTER(SsdArgs)]
+        L.ssm_ssd_workspace_bytes.restype = ctypes.c_int64
+        L.ssm_ssd_plan.argtypes = [ctypes.POINTER(SsdArgs)]
+        L.ssm_ssd_plan.restype = ctypes.c_int
         L.ssm_gla_workspace_bytes.argtypes = [ctypes.POINTER(GlaArgs)]
         L.ssm_gla_workspace_bytes.restype = ctypes.c_int64
+        L.ssm_gla_plan.argtypes = [ctypes.POINTER(GlaArgs)]
+        L.ssm_gla_plan.restype = ctypes.c_int
         L.ssm_conv1d_silu_fwd.argtypes = [ctypes.POINTER(ConvArgs), ctypes.c_void_p]
         L.ssm_conv1d_silu_fwd.restype = ctypes.c_int
         L.ssm_scan_strerror.argtypes = [ctypes.c_int]
         L.ssm_scan_strerror.restype = ctypes.c_char_p
         L.ssm_scan_abi_version.argtypes = []
         L.ssm_scan_abi_version.restype = ctypes.c_int
-        if L.ssm_scan_abi_version() != 2:
+        if L.ssm_scan_abi_version() != ABI_VERSION:
             raise RuntimeError("libssm_scan ABI version mismatch")
         _lib = L
     return _lib
@@ -399,7 +409,7 @@ def conv1d_silu(x, weight, bias=None, state=None, *, return_state=False, out=Non
     return u
 
 
-def make_ssd_args(x, dt, A, B, C, D=None, dt_bias=None, h0=None, hT=None, y=None) -> SsdArgs:
+def make_ssd_args(x, dt, A, B, C, D=None, dt_bias=None, h0=None, hT=None, y=None, time_splits=0) -> SsdArgs:
     """Check shapes/dtypes/devices and fill an ssm_ssd_args."""
     if x.dim() != 4 or B.dim() != 4:
         raise ValueError("x must be (B, L, H, P) and B, C (B, L, G, N)")
@@ -418,17 +428,50 @@ def make_ssd_args(x, dt, A, B, C, D=None, dt_bias=None, h0=None, hT=None, y=None
     _check("y", y, (bsz, L, H, P), bf, dev)
     a = SsdArgs()
     a.batch, a.seqlen, a.nheads, a.headdim, a.ngroups, a.dstate = bsz, L, H, P, G, N
-    a.dtype, a.reserved = DTYPE_BF16, 0
+    a.dtype, a.time_splits = DTYPE_BF16, int(time_splits)
     a.x, a.dt, a.A, a.B, a.C = _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C)
     a.D, a.dt_bias, a.h0, a.hT, a.y = _ptr(D), _ptr(dt_bias), _ptr(h0), _ptr(hT), _ptr(y)
     return a
 
 
+def _attach_workspace(args, query, workspace, device, name):
+    """Size (query) and allocate a workspace when none is given; an empty tensor declines it."""
+    if workspace is None:
+        nbytes = query(ctypes.byref(args))
+        if nbytes < 0:
+            raise RuntimeError(f"{name}: {strerror(int(nbytes))}")
+        if nbytes > 0:
+            workspace = torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+    if workspace is not None and workspace.numel() > 0:
+        args.workspace = _ptr(workspace)
+        args.workspace_bytes = workspace.numel() * workspace.element_size()
+    return workspace
+
+
+def ssd_workspace_bytes(args: SsdArgs) -> int:
+    """Bytes of workspace ssm_ssd_fwd uses for time-segment summaries (0: no split)."""
+    r = lib().ssm_ssd_workspace_bytes(ctypes.byref(args))
+    if r < 0:
+        raise RuntimeError(f"ssm_ssd_workspace_bytes: {strerror(int(r))}")
+    return int(r)
+
+
+def ssd_plan(args: SsdArgs) -> int:
+    """Time segments ssm_ssd_fwd would run with these arguments (1: no split)."""
+    r = lib().ssm_ssd_plan(ctypes.byref(args))
+    if r < 0:
+        raise RuntimeError(f"ssm_ssd_plan: {strerror(int(r))}")
+    return int(r)
+
+
 def ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, h0=None, *, return_final_state=False, out=None,
-            final_state_out=None):
+            final_state_out=None, time_splits=0, workspace=None):
     """Mamba-2 SSD layer forward on the GPU (chunked matrix form on the matrix
-    cores).  Returns y, or (y, hT) with return_final_state=True.  Launches on
-    torch's current HIP stream and does not synchronise."""
+    cores).  Returns y, or (y, hT) with return_final_state=True.  time_splits:
+    0 lets the library cut the sequence into time segments when batch x heads
+    leaves compute units idle, 1 never, S > 1 asks for S; the segment summaries
+    go to `workspace` (allocated here when None; an empty tensor declines it).
+    Launches on torch's current HIP stream and does not synchronise."""
     if not x.is_cuda:
         raise ValueError("ssd_fwd runs on the GPU only: move the tensors to a HIP device")
     L_ = lib()
@@ -436,7 +479,8 @@ def ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, h0=None, *, return_final_state
     hT = final_state_out
     if hT is None and return_final_state:
         hT = torch.empty((x.shape[0], x.shape[2], x.shape[3], B.shape[3]), dtype=torch.float32, device=x.device)
-    args = make_ssd_args(x, dt, A, B, C, D, dt_bias, h0, hT, y)
+    args = make_ssd_args(x, dt, A, B, C, D, dt_bias, h0, hT, y, time_splits)
+    _attach_workspace(args, L_.ssm_ssd_workspace_bytes, workspace, x.device, "ssm_ssd_fwd")
     stream = torch.cuda.current_stream(x.device).cuda_stream
     rc = L_.ssm_ssd_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
     if rc != 0:
@@ -446,7 +490,8 @@ def ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, h0=None, *, return_final_state
     return y
 
 
-def make_gla_args(q, k, v, log_f=None, in_gate=None, h0=None, hT=None, y=None, feature_map=False) -> GlaArgs:
+def make_gla_args(q, k, v, log_f=None, in_gate=None, h0=None, hT=None, y=None, feature_map=False,
+                  time_splits=0) -> GlaArgs:
     """Check shapes/dtypes/devices and fill an ssm_gla_args."""
     if v.dim() != 4 or k.dim() != 4:
         raise ValueError("v must be (B, L, H, P) and q, k (B, L, G, N)")
@@ -464,27 +509,38 @@ def make_gla_args(q, k, v, log_f=None, in_gate=None, h0=None, hT=None, y=None, f
     a = GlaArgs()
     a.batch, a.seqlen, a.nheads, a.headdim, a.ngroups, a.dstate = bsz, L, H, P, G, N
     a.dtype, a.feature_map = DTYPE_BF16, int(bool(feature_map))
+    a.time_splits, a.reserved = int(time_splits), 0
     a.q, a.k, a.v, a.log_f, a.in_gate = _ptr(q), _ptr(k), _ptr(v), _ptr(log_f), _ptr(in_gate)
     a.h0, a.hT, a.y = _ptr(h0), _ptr(hT), _ptr(y)
     return a
 
 
 def gla_workspace_bytes(args: GlaArgs) -> int:
-    """Bytes of workspace ssm_gla_fwd uses to apply the feature map once per call."""
+    """Bytes of workspace ssm_gla_fwd uses: the feature map applied once per
+    call, then the time-segment summaries."""
     r = lib().ssm_gla_workspace_bytes(ctypes.byref(args))
     if r < 0:
         raise RuntimeError(f"ssm_gla_workspace_bytes: {strerror(int(r))}")
     return int(r)
 
 
+def gla_plan(args: GlaArgs) -> int:
+    """Time segments ssm_gla_fwd would run with these arguments (1: no split)."""
+    r = lib().ssm_gla_plan(ctypes.byref(args))
+    if r < 0:
+        raise RuntimeError(f"ssm_gla_plan: {strerror(int(r))}")
+    return int(r)
+
+
 def gla_fwd(q, k, v, log_f=None, in_gate=None, h0=None, *, feature_map=False, return_final_state=False, out=None,
-            final_state_out=None, workspace=None):
+            final_state_out=None, workspace=None, time_splits=0):
     """Gated linear attention / mLSTM matrix-state recurrence on the GPU:
     S_t = exp(log_f) S_{t-1} + in_gate v_t phi(k_t)^T, y_t = S_t phi(q_t), phi the
     identity or elu + 1 (feature_map=True).  Returns y, or (y, hT) with
-    return_final_state=True.  With the feature map, a workspace (allocated here
-    when None; an empty tensor declines it) lets the library apply phi once per
-    call.  Launches on torch's current HIP stream and does not synchronise."""
+    return_final_state=True.  A workspace (allocated here when None; an empty
+    tensor declines it) lets the library apply phi once per call and hold the
+    time-segment summaries (time_splits as for ssd_fwd).  Launches on torch's
+    current HIP stream and does not synchronise."""
     if not v.is_cuda:
         raise ValueError("gla_fwd runs on the GPU only: move the tensors to a HIP device")
     L_ = lib()
@@ -492,16 +548,8 @@ def gla_fwd(q, k, v, log_f=None, in_gate=None, h0=None, *, feature_map=False, re
     hT = final_state_out
     if hT is None and return_final_state:
         hT = torch.empty((v.shape[0], v.shape[2], v.shape[3], k.shape[3]), dtype=torch.float32, device=v.device)
-    args = make_gla_args(q, k, v, log_f, in_gate, h0, hT, y, feature_map)
-    if workspace is None:
-        nbytes = L_.ssm_gla_workspace_bytes(ctypes.byref(args))
-        if nbytes < 0:
-            raise RuntimeError(f"ssm_gla_fwd: {strerror(int(nbytes))}")
-        if nbytes > 0:
-            workspace = torch.empty(int(nbytes), dtype=torch.uint8, device=v.device)
-    if workspace is not None and workspace.numel() > 0:
-        args.workspace = _ptr(workspace)
-        args.workspace_bytes = workspace.numel() * workspace.element_size()
+    args = make_gla_args(q, k, v, log_f, in_gate, h0, hT, y, feature_map, time_splits)
+    _attach_workspace(args, L_.ssm_gla_workspace_bytes, workspace, v.device, "ssm_gla_fwd")
     stream = torch.cuda.current_stream(v.device).cuda_stream
     rc = L_.ssm_gla_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
     if rc != 0:
@@ -511,5 +559,5 @@ def gla_fwd(q, k, v, log_f=None, in_gate=None, h0=None, *, feature_map=False, re
     return y
 
 
-__all__ = ["scan_fwd", "scan_bwd", "conv1d_silu", "ssd_fwd", "gla_fwd", "make_gla_args", "GlaArgs", "gla_workspace_bytes", "make_ssd_args", "SsdArgs", "make_conv_args", "ConvArgs", "make_args", "make_bwd_args", "plan", "bwd_plan", "workspace_bytes",
+__all__ = ["scan_fwd", "scan_bwd", "conv1d_silu", "ssd_fwd", "gla_fwd", "make_gla_args", "GlaArgs", "gla_workspace_bytes", "gla_plan", "make_ssd_args", "SsdArgs", "ssd_workspace_bytes", "ssd_plan", "make_conv_args", "ConvArgs", "make_args", "make_bwd_args", "plan", "bwd_plan", "workspace_bytes",
            "bwd_workspace_bytes", "lib", "strerror", "ScanArgs", "ScanBwdArgs", "EXPORTS"]

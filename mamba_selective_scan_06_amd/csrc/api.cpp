@@ -287,12 +287,16 @@ bool bwd_has_work(const ssm_scan_bwd_args* a) { return a->batch > 0 && a->seqlen
 
 // ---- Mamba-2 SSD ------------------------------------------------------------------------------
 
-int validate_ssd(const ssm_ssd_args* a) {
+// Segments beyond what one grid dimension holds are not asked for.
+constexpr int32_t kSsdMaxSplits = 65535;
+
+int validate_ssd(const ssm_ssd_args* a, bool check_workspace = true) {
   if (!a) return SSM_ERR_NULL;
   if (a->batch < 0 || a->seqlen < 0 || a->nheads < 1 || a->headdim < 1 || a->ngroups < 1 || a->dstate < 1)
     return SSM_ERR_SHAPE;
   if (a->dtype != SSM_DTYPE_BF16) return a->dtype == SSM_DTYPE_F32 ? SSM_ERR_VARIANT : SSM_ERR_DTYPE;
-  if (a->reserved != 0 || a->headdim != 64 || a->nheads % a->ngroups != 0) return SSM_ERR_VARIANT;
+  if (a->time_splits < 0 || a->time_splits > kSsdMaxSplits || a->headdim != 64 || a->nheads % a->ngroups != 0)
+    return SSM_ERR_VARIANT;
   if (a->dstate != 64 && a->dstate != 128 && a->dstate != 256) return SSM_ERR_VARIANT;
   if (a->batch > 65535 || a->nheads > 65535) return SSM_ERR_SHAPE;
   int64_t bl, blh, xe, bn, st, tmp;
@@ -313,6 +317,72 @@ int validate_ssd(const ssm_ssd_args* a) {
     if (overlaps(a->hT, st * 4, ins[i], insz[i])) return SSM_ERR_ALIAS;
   }
   if (overlaps(a->hT, st * 4, a->y, xe * 2)) return SSM_ERR_ALIAS;
+  if (check_workspace && a->workspace) {
+    if (!aligned16(a->workspace) || a->workspace_bytes < 0) return SSM_ERR_ALIGN;
+    const int64_t wb = a->workspace_bytes;
+    for (int i = 0; i < 8; ++i)
+      if (overlaps(a->workspace, wb, ins[i], insz[i])) return SSM_ERR_ALIAS;
+    if (overlaps(a->workspace, wb, a->y, xe * 2) || overlaps(a->workspace, wb, a->hT, st * 4)) return SSM_ERR_ALIAS;
+  }
+  return SSM_OK;
+}
+
+// Time segments of the chunked SSD / gated-attention kernel: how many, and
+// the summary bytes they need.
+struct SsdPlan {
+  int splits = 1;
+  int64_t seg_chunks = 0;
+  int64_t ws_state = 0;  // (B, S-1, H, P, N) fp32, rounded up to 256 bytes
+  int64_t ws_la = 0;     // (B, S-1, H) fp32, rounded up to 256 bytes
+  int64_t bytes() const { return ws_state + ws_la; }
+};
+
+// One workgroup runs per compute unit (its LDS use is over half of the 160 KiB),
+// and one walks the chunks of one (b, h) in order.  Splitting costs a state-only
+// pass over all but the last segment; it pays while every segment's workgroup
+// still finds a compute unit of its own, so the automatic choice takes the most
+// segments for which B H S fits the 256 compute units, with at least 4 chunks
+// per segment and at most 64 segments.
+int ssd_plan(int64_t B, int64_t L, int64_t H, int64_t N, int32_t time_splits, SsdPlan* pl) {
+  constexpr int64_t kComputeUnits = 256;
+  const int64_t nch = (L + 63) / 64;
+  int64_t S = 1;
+  if (B > 0 && nch > 0) {
+    if (time_splits > 1) {
+      S = time_splits;
+    } else if (time_splits == 0) {
+      int64_t fit = kComputeUnits / (B * H);
+      if (fit > nch / 4) fit = nch / 4;
+      if (fit > 64) fit = 64;
+      if (fit > 1) S = fit;
+    }
+  }
+  if (S > nch) S = nch;
+  *pl = SsdPlan{};
+  if (S < 2) return SSM_OK;
+  const int64_t segc = (nch + S - 1) / S;
+  S = (nch + segc - 1) / segc;  // no empty segment
+  if (S < 2) return SSM_OK;
+  int64_t bs, st, tmp;
+  if (!mul_ok(B, S - 1, &bs) || !mul_ok(bs, H, &tmp) || !mul_ok(tmp, 64 * N * 4, &st)) return SSM_ERR_SHAPE;
+  pl->splits = static_cast<int>(S);
+  pl->seg_chunks = segc;
+  pl->ws_state = round_up(st, 256);
+  pl->ws_la = round_up(tmp * 4, 256);
+  return SSM_OK;
+}
+
+// The plan with the caller's workspace: an automatic split that does not fit
+// (summaries at byte `offset` of the workspace) falls back to one segment, an
+// explicit one is an error.
+int ssd_plan_fit(int64_t B, int64_t L, int64_t H, int64_t N, int32_t time_splits, const void* ws, int64_t ws_bytes,
+                 int64_t offset, SsdPlan* pl) {
+  const int rc = ssd_plan(B, L, H, N, time_splits, pl);
+  if (rc != SSM_OK) return rc;
+  if (pl->splits > 1 && (!ws || ws_bytes < offset + pl->bytes())) {
+    if (time_splits > 1) return SSM_ERR_WORKSPACE;
+    *pl = SsdPlan{};
+  }
   return SSM_OK;
 }
 
@@ -327,7 +397,8 @@ int validate_gla(const ssm_gla_args* a, bool check_workspace = true) {
   if (a->batch < 0 || a->seqlen < 0 || a->nheads < 1 || a->headdim < 1 || a->ngroups < 1 || a->dstate < 1)
     return SSM_ERR_SHAPE;
   if (a->dtype != SSM_DTYPE_BF16) return a->dtype == SSM_DTYPE_F32 ? SSM_ERR_VARIANT : SSM_ERR_DTYPE;
-  if (a->feature_map < 0 || a->feature_map > 1 || a->headdim != 64 || a->nheads % a->ngroups != 0)
+  if (a->feature_map < 0 || a->feature_map > 1 || a->headdim != 64 || a->nheads % a->ngroups != 0 ||
+      a->reserved != 0 || a->time_splits < 0 || a->time_splits > kSsdMaxSplits)
     return SSM_ERR_VARIANT;
   if (a->dstate != 64 && a->dstate != 128 && a->dstate != 256) return SSM_ERR_VARIANT;
   if (a->batch > 65535 || a->nheads > 65535) return SSM_ERR_SHAPE;
@@ -608,6 +679,20 @@ int ssm_conv1d_silu_fwd(const ssm_conv_args* a, void* stream) {
   return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
 
+namespace {
+
+// Segment fields of a kernel problem from a plan; summaries at `ws`.
+void set_segments(ssm::SsdProblem* p, const SsdPlan& pl, void* ws) {
+  p->splits = pl.splits;
+  p->seg_chunks = pl.seg_chunks;
+  if (pl.splits > 1) {
+    p->ws_state = static_cast<float*>(ws);
+    p->ws_la = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.ws_state);
+  }
+}
+
+}  // namespace
+
 int ssm_ssd_fwd(const ssm_ssd_args* a, void* stream) {
   const int rc = validate_ssd(a);
   if (rc != SSM_OK) return rc;
@@ -629,18 +714,55 @@ int ssm_ssd_fwd(const ssm_ssd_args* a, void* stream) {
   p.h0 = a->h0;
   p.hT = a->hT;
   p.y = a->y;
+  SsdPlan pl;
+  const int prc = ssd_plan_fit(a->batch, a->seqlen, a->nheads, a->dstate, a->time_splits, a->workspace,
+                               a->workspace_bytes, 0, &pl);
+  if (prc != SSM_OK) return prc;
+  set_segments(&p, pl, a->workspace);
   const hipError_t e = ssm::launch_ssd(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
+
+int64_t ssm_ssd_workspace_bytes(const ssm_ssd_args* a) {
+  const int rc = validate_ssd(a, false);
+  if (rc != SSM_OK) return rc;
+  SsdPlan pl;
+  const int prc = ssd_plan(a->batch, a->seqlen, a->nheads, a->dstate, a->time_splits, &pl);
+  return prc != SSM_OK ? prc : pl.bytes();
+}
+
+int ssm_ssd_plan(const ssm_ssd_args* a) {
+  const int rc = validate_ssd(a);
+  if (rc != SSM_OK) return rc;
+  SsdPlan pl;
+  const int prc = ssd_plan_fit(a->batch, a->seqlen, a->nheads, a->dstate, a->time_splits, a->workspace,
+                               a->workspace_bytes, 0, &pl);
+  return prc != SSM_OK ? prc : pl.splits;
+}
+
+namespace {
+
+// Bytes in front of the segment summaries in a gated-attention workspace:
+// phi(k) and phi(q) with the feature map.
+int64_t gla_phi_bytes(const ssm_gla_args* a) {
+  return a->feature_map == 1 && a->batch > 0 && a->seqlen > 0 ? 2 * gla_ws_part(a) : 0;
+}
+
+}  // namespace
 
 int ssm_gla_fwd(const ssm_gla_args* a, void* stream) {
   const int rc = validate_gla(a);
   if (rc != SSM_OK) return rc;
   if (a->batch == 0) return SSM_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  SsdPlan pl;
+  const int64_t phi = gla_phi_bytes(a);
+  const int prc = ssd_plan_fit(a->batch, a->seqlen, a->nheads, a->dstate, a->time_splits, a->workspace,
+                               a->workspace_bytes, phi, &pl);
+  if (prc != SSM_OK) return prc;
   // feature map applied once per call into the workspace when one is given
   const int64_t part = gla_ws_part(a);
-  const bool prepass = a->feature_map == 1 && a->seqlen > 0 && a->workspace && a->workspace_bytes >= 2 * part;
+  const bool prepass = phi > 0 && a->workspace && a->workspace_bytes >= phi;
   const void* keys = a->k;
   const void* queries = a->q;
   if (prepass) {
@@ -672,6 +794,7 @@ int ssm_gla_fwd(const ssm_gla_args* a, void* stream) {
   p.h0 = a->h0;
   p.hT = a->hT;
   p.y = a->y;
+  set_segments(&p, pl, pl.splits > 1 ? static_cast<char*>(a->workspace) + phi : nullptr);
   const hipError_t e = ssm::launch_ssd(p, s);
   return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
@@ -679,7 +802,18 @@ int ssm_gla_fwd(const ssm_gla_args* a, void* stream) {
 int64_t ssm_gla_workspace_bytes(const ssm_gla_args* a) {
   const int rc = validate_gla(a, false);
   if (rc != SSM_OK) return rc;
-  return a->feature_map == 1 && a->batch > 0 && a->seqlen > 0 ? 2 * gla_ws_part(a) : 0;
+  SsdPlan pl;
+  const int prc = ssd_plan(a->batch, a->seqlen, a->nheads, a->dstate, a->time_splits, &pl);
+  return prc != SSM_OK ? prc : gla_phi_bytes(a) + pl.bytes();
+}
+
+int ssm_gla_plan(const ssm_gla_args* a) {
+  const int rc = validate_gla(a);
+  if (rc != SSM_OK) return rc;
+  SsdPlan pl;
+  const int prc = ssd_plan_fit(a->batch, a->seqlen, a->nheads, a->dstate, a->time_splits, a->workspace,
+                               a->workspace_bytes, gla_phi_bytes(a), &pl);
+  return prc != SSM_OK ? prc : pl.splits;
 }
 
 }  // extern "C"

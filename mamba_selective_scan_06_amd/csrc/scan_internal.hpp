@@ -163,6 +163,13 @@ struct SsdProblem {
   const float* h0;
   float* hT;
   void* y;
+  // time segments: splits > 1 runs a state-only pass over the first splits - 1
+  // segments of seg_chunks 64-token chunks into ws_state (B, splits-1, H, P, N)
+  // and ws_la (B, splits-1, H), then the full pass
+  int splits = 1;
+  int64_t seg_chunks = 0;
+  float* ws_state = nullptr;
+  float* ws_la = nullptr;
 };
 
 hipError_t launch_ssd(const SsdProblem& p, hipStream_t stream);

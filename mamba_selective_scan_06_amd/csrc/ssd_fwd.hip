@@ -42,6 +42,15 @@
 //   C. y^T for the wave's tiles (M X from LDS), store; state update.
 // Tokens past L are padded with i = 0, a = 0 and x = B = C = 0, which leaves
 // the state unchanged.
+//
+// Time segments (when B H workgroups leave most compute units idle): segment s
+// owns the chunks [s SC, (s + 1) SC).  The state recurrence over a segment is
+// affine in the state entering it, S_out = exp(la) S_in + S_seg, with la the
+// sum of the segment's log decays and S_seg its end state from zero.  A
+// state-only launch (no M, no C H^T, no y: per chunk only the scalars, B^T,
+// x o w and the state update) writes S_seg and la for every segment but the
+// last; the full launch starts segment s from h0 and folds the summaries of
+// segments 0 .. s-1 into it in order, then runs the chunks as above.
 #include <type_traits>
 
 #include "buffer_io.hpp"
@@ -145,11 +154,15 @@ struct KArgs {
   const float* h0;
   float* hT;
   uint16_t* y;
+  float* ws_state;   // (B, S-1, H, P, N) end state of each segment but the last, from zero
+  float* ws_la;      // (B, S-1, H) sum of the log decays over each of those segments
   int64_t L;
-  int H, G;
+  int64_t seg_chunks;  // chunks per segment (all of them when S = 1)
+  int H, G, S;
 };
 
-template <int N, int MODE, int NW>
+// ST: the state-only pass of a time-split call (see the top of the file).
+template <int N, int MODE, int NW, bool ST>
 __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
   constexpr int NK = NW / 4;          // parts of the n range, one per wave of a channel slice
   constexpr int XT = kQ / NW;         // x tokens per staging lane (one channel each)
@@ -163,14 +176,14 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
   const int w = wi & 3, k = wi >> 2;  // channel slice, n part
   const int lr = lane & 15, lg = lane >> 4;
   // XCD-aware order: the hardware deals workgroups to the 8 XCDs round-robin, so
-  // every 8th workgroup takes the next head.  The heads of a batch row then run
-  // on one XCD and share its L2 for B, C and the cache lines of their per-token
-  // inputs (one line holds the values of many heads).
-  const int nwg = gridDim.x * gridDim.y;
-  int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  // every 8th workgroup takes the next head.  The heads of a batch row (and time
+  // segment) then run on one XCD and share its L2 for B, C and the cache lines of
+  // their per-token inputs (one line holds the values of many heads).
+  const int64_t nwg = static_cast<int64_t>(gridDim.x) * gridDim.y * gridDim.z;
+  int64_t lin = blockIdx.x + gridDim.x * (blockIdx.y + static_cast<int64_t>(gridDim.y) * blockIdx.z);
   if (nwg % 8 == 0) lin = (lin % 8) * (nwg / 8) + lin / 8;
-  const int64_t b = lin / a.H, L = a.L;
-  const int h = lin % a.H;
+  const int h = static_cast<int>(lin % a.H);
+  const int64_t b = (lin / a.H) % gridDim.y, seg = lin / a.H / gridDim.y, L = a.L;
   const int g = h / (a.H / a.G);
   const int64_t xrow = static_cast<int64_t>(a.H) * kP;  // elements between tokens in x / y
   const int64_t brow = static_cast<int64_t>(a.G) * N;   // elements between tokens in B / C
@@ -197,13 +210,29 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
 
   // the wave's state part: Hs[j][r] = S[p = 16 w + lr][n = 16 (k NJK + j) + 4 lg + r]
   float Hs[NJK][4];
-  const int64_t sbase = ((b * a.H + h) * kP + 16 * w + lr) * N + 16 * k * NJK + 4 * lg;
+  const int64_t spart = (16 * w + lr) * N + 16 * k * NJK + 4 * lg;  // offset inside one (P, N) state
+  const int64_t sbase = (b * a.H + h) * kP * N + spart;
+  // summary j of this (b, h): state at ((b (S-1) + j) H + h) P N, log decay at (b (S-1) + j) H + h
+  auto summary = [&](int64_t j) { return (b * (a.S - 1) + j) * a.H + h; };
 #pragma unroll
   for (int j = 0; j < NJK; ++j) {
     float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (a.h0) v = *reinterpret_cast<const float4*>(a.h0 + sbase + 16 * j);
+    if (!ST && a.h0) v = *reinterpret_cast<const float4*>(a.h0 + sbase + 16 * j);
     Hs[j][0] = v.x, Hs[j][1] = v.y, Hs[j][2] = v.z, Hs[j][3] = v.w;
   }
+  if constexpr (!ST) {  // the state entering this segment: earlier segments' summaries, in order
+    for (int64_t sj = 0; sj < seg; ++sj) {
+      const float dec = fast_exp2(a.ws_la[summary(sj)] * kLog2e);
+      const float* src = a.ws_state + summary(sj) * kP * N + spart;
+#pragma unroll
+      for (int j = 0; j < NJK; ++j) {
+        const float4 v = *reinterpret_cast<const float4*>(src + 16 * j);
+        Hs[j][0] = __builtin_fmaf(dec, Hs[j][0], v.x), Hs[j][1] = __builtin_fmaf(dec, Hs[j][1], v.y);
+        Hs[j][2] = __builtin_fmaf(dec, Hs[j][2], v.z), Hs[j][3] = __builtin_fmaf(dec, Hs[j][3], v.w);
+      }
+    }
+  }
+  float la_total = 0.0f;  // state-only pass: the segment's summed log decay
 
   // raw data of the next chunk, loaded one chunk ahead
   uint32_t xr[XT], br[TPT][4], cr[TPT][4];
@@ -221,9 +250,11 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
     for (int j = 0; j < TPT; ++j) {
       const uint32_t off = static_cast<uint32_t>((TPT * btq + j) * brow * 2 + 16 * bng);
       const u32x4 vb = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-      const u32x4 vc = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
       br[j][0] = vb.x, br[j][1] = vb.y, br[j][2] = vb.z, br[j][3] = vb.w;
-      cr[j][0] = vc.x, cr[j][1] = vc.y, cr[j][2] = vc.z, cr[j][3] = vc.w;
+      if constexpr (!ST) {  // the state-only pass reads no C
+        const u32x4 vc = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
+        cr[j][0] = vc.x, cr[j][1] = vc.y, cr[j][2] = vc.z, cr[j][3] = vc.w;
+      }
     }
   };
   auto load_tok = [&](int64_t t0) {  // wave 0 only: it turns them into delta and the prefix sums
@@ -239,14 +270,16 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
   };
 
   const int64_t nchunks = (L + kQ - 1) / kQ;
-  load_bc(0);
-  load_tok(0);
-  load_x(0);
+  const int64_t c_begin = seg * a.seg_chunks;
+  const int64_t c_end = c_begin + a.seg_chunks < nchunks ? c_begin + a.seg_chunks : nchunks;
+  load_bc(c_begin * kQ);
+  load_tok(c_begin * kQ);
+  load_x(c_begin * kQ);
   // wait for the first chunk here, so that the wait at the top of the loop is set
   // by the loop alone: only the y stores issued after the prefetch are still in
   // flight there, and the wait lets them run (vmcnt counts stores too)
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  for (int64_t c = 0; c < nchunks; ++c) {
+  for (int64_t c = c_begin; c < c_end; ++c) {
     const int64_t t0 = c * kQ;
     const int cb = kSsdStageBufs<N> == 2 ? static_cast<int>(c & 1) : 0;  // staging buffer of this chunk
     // ---- A. per-token scalars (wave 0, one token per lane); x^T, B^T, B, C into LDS
@@ -271,14 +304,19 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
       const float s_end = __shfl(s, kQ - 1, 64);
       sm.ww[cb][lane] = fast_exp2((s_end - s) * kLog2e) * d;
     }
+    if constexpr (!ST) {
 #pragma unroll
-    for (int q = 0; q < XT / 8; ++q)
-      *reinterpret_cast<uint4*>(&sm.xt[cb][XT / 8 * wi + q][lane][0]) =
-          make_uint4(xr[8 * q] | (xr[8 * q + 1] << 16), xr[8 * q + 2] | (xr[8 * q + 3] << 16),
-                     xr[8 * q + 4] | (xr[8 * q + 5] << 16), xr[8 * q + 6] | (xr[8 * q + 7] << 16));
+      for (int q = 0; q < XT / 8; ++q)
+        *reinterpret_cast<uint4*>(&sm.xt[cb][XT / 8 * wi + q][lane][0]) =
+            make_uint4(xr[8 * q] | (xr[8 * q + 1] << 16), xr[8 * q + 2] | (xr[8 * q + 3] << 16),
+                       xr[8 * q + 4] | (xr[8 * q + 5] << 16), xr[8 * q + 6] | (xr[8 * q + 7] << 16));
+    }
     if constexpr (MODE == 2) {
 #pragma unroll
-      for (int j = 0; j < TPT; ++j) feature_map(br[j]), feature_map(cr[j]);
+      for (int j = 0; j < TPT; ++j) {
+        feature_map(br[j]);
+        if constexpr (!ST) feature_map(cr[j]);
+      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -294,10 +332,12 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
         if constexpr (TPT == 8) *reinterpret_cast<uint4*>(dst) = make_uint4(q[0], q[1], q[2], q[3]);
       }
     }
+    if constexpr (!ST) {
 #pragma unroll
-    for (int j = 0; j < TPT; ++j) {
-      write_perm(sm.bn[TPT * btq + j], 8 * bng, br[j]);
-      write_perm(sm.cn[TPT * btq + j], 8 * bng, cr[j]);
+      for (int j = 0; j < TPT; ++j) {
+        write_perm(sm.bn[TPT * btq + j], 8 * bng, br[j]);
+        write_perm(sm.cn[TPT * btq + j], 8 * bng, cr[j]);
+      }
     }
     load_bc(t0 + kQ);  // past the last chunk these read nothing
     load_tok(t0 + kQ);
@@ -319,124 +359,129 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
       *reinterpret_cast<uint4*>(&sm.xw[1][c8][lane][0]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
     load_x(t0 + kQ);
+    f32x4 yo[4] = {};  // this wave's part of C H^T, tile by tile
+    if constexpr (!ST) {
 #pragma unroll
-    for (int tk = wi; tk < 12; tk += NW) {
-      // the 12 16x16 tiles of M that y reads: tk < 10 enumerates (t tile, s tile)
-      // on or below the diagonal row by row; 10 and 11 are the two above it that
-      // a 32-token k step of y also covers, (0, 1) and (2, 3), all zero
-      int ti, si;
-      if (tk < 10) {
-        ti = (tk >= 1) + (tk >= 3) + (tk >= 6);
-        si = tk - ti * (ti + 1) / 2;
-      } else {
-        ti = tk == 10 ? 0 : 2;
-        si = ti + 1;
-      }
-      const int t = 16 * ti + lr, s0 = 16 * si + 4 * lg;
-      uint2 hw = make_uint2(0, 0), lw = make_uint2(0, 0);
-      if (tk < 10) {
-        f32x4 acc = {};
-#pragma unroll
-        for (int m = 0; m < N / 32; ++m)
-          acc = mfma(lds8(&sm.bn[16 * si + lr][32 * m + 8 * lg]), lds8(&sm.cn[t][32 * m + 8 * lg]), acc);
-        const float cst = sm.cs[cb][t];
-        const float4 css = *reinterpret_cast<const float4*>(&sm.cs[cb][s0]);
-        const float4 dls = *reinterpret_cast<const float4*>(&sm.dl[cb][s0]);
-        const float csv[4] = {css.x, css.y, css.z, css.w}, dlv[4] = {dls.x, dls.y, dls.z, dls.w};
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int s = s0 + r;
-          v[r] = acc[r] * fast_exp2((cst - csv[r]) * kLog2e) * dlv[r];
-          v[r] = s <= t ? v[r] : 0.0f;
-          if constexpr (MODE == 0) v[r] += s == t ? Dh : 0.0f;
+      for (int tk = wi; tk < 12; tk += NW) {
+        // the 12 16x16 tiles of M that y reads: tk < 10 enumerates (t tile, s tile)
+        // on or below the diagonal row by row; 10 and 11 are the two above it that
+        // a 32-token k step of y also covers, (0, 1) and (2, 3), all zero
+        int ti, si;
+        if (tk < 10) {
+          ti = (tk >= 1) + (tk >= 3) + (tk >= 6);
+          si = tk - ti * (ti + 1) / 2;
+        } else {
+          ti = tk == 10 ? 0 : 2;
+          si = ti + 1;
         }
-        split2(v[0], v[1], hw.x, lw.x);
-        split2(v[2], v[3], hw.y, lw.y);
+        const int t = 16 * ti + lr, s0 = 16 * si + 4 * lg;
+        uint2 hw = make_uint2(0, 0), lw = make_uint2(0, 0);
+        if (tk < 10) {
+          f32x4 acc = {};
+#pragma unroll
+          for (int m = 0; m < N / 32; ++m)
+            acc = mfma(lds8(&sm.bn[16 * si + lr][32 * m + 8 * lg]), lds8(&sm.cn[t][32 * m + 8 * lg]), acc);
+          const float cst = sm.cs[cb][t];
+          const float4 css = *reinterpret_cast<const float4*>(&sm.cs[cb][s0]);
+          const float4 dls = *reinterpret_cast<const float4*>(&sm.dl[cb][s0]);
+          const float csv[4] = {css.x, css.y, css.z, css.w}, dlv[4] = {dls.x, dls.y, dls.z, dls.w};
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int s = s0 + r;
+            v[r] = acc[r] * fast_exp2((cst - csv[r]) * kLog2e) * dlv[r];
+            v[r] = s <= t ? v[r] : 0.0f;
+            if constexpr (MODE == 0) v[r] += s == t ? Dh : 0.0f;
+          }
+          split2(v[0], v[1], hw.x, lw.x);
+          split2(v[2], v[3], hw.y, lw.y);
+        }
+        *reinterpret_cast<uint2*>(&sm.M[0][s0 / 8][t][s0 % 8]) = hw;
+        *reinterpret_cast<uint2*>(&sm.M[1][s0 / 8][t][s0 % 8]) = lw;
       }
-      *reinterpret_cast<uint2*>(&sm.M[0][s0 / 8][t][s0 % 8]) = hw;
-      *reinterpret_cast<uint2*>(&sm.M[1][s0 / 8][t][s0 % 8]) = lw;
-    }
-    f32x4 yo[4] = {};
 #pragma unroll
-    for (int mm = 0; mm < NMK; ++mm) {
-      const int m = k * NMK + mm;
-      uint32_t hv[4], lv[4];
-      split2(Hs[2 * mm][0], Hs[2 * mm][1], hv[0], lv[0]);
-      split2(Hs[2 * mm][2], Hs[2 * mm][3], hv[1], lv[1]);
-      split2(Hs[2 * mm + 1][0], Hs[2 * mm + 1][1], hv[2], lv[2]);
-      split2(Hs[2 * mm + 1][2], Hs[2 * mm + 1][3], hv[3], lv[3]);
-      const bf16x8 hh = __builtin_bit_cast(bf16x8, make_uint4(hv[0], hv[1], hv[2], hv[3]));
-      const bf16x8 hl = __builtin_bit_cast(bf16x8, make_uint4(lv[0], lv[1], lv[2], lv[3]));
+      for (int mm = 0; mm < NMK; ++mm) {
+        const int m = k * NMK + mm;
+        uint32_t hv[4], lv[4];
+        split2(Hs[2 * mm][0], Hs[2 * mm][1], hv[0], lv[0]);
+        split2(Hs[2 * mm][2], Hs[2 * mm][3], hv[1], lv[1]);
+        split2(Hs[2 * mm + 1][0], Hs[2 * mm + 1][1], hv[2], lv[2]);
+        split2(Hs[2 * mm + 1][2], Hs[2 * mm + 1][3], hv[3], lv[3]);
+        const bf16x8 hh = __builtin_bit_cast(bf16x8, make_uint4(hv[0], hv[1], hv[2], hv[3]));
+        const bf16x8 hl = __builtin_bit_cast(bf16x8, make_uint4(lv[0], lv[1], lv[2], lv[3]));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x8 cb = lds8(&sm.cn[16 * i + lr][32 * m + 8 * lg]);
-        yo[i] = mfma(hh, cb, yo[i]);
-        yo[i] = mfma(hl, cb, yo[i]);
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8 cb = lds8(&sm.cn[16 * i + lr][32 * m + 8 * lg]);
+          yo[i] = mfma(hh, cb, yo[i]);
+          yo[i] = mfma(hl, cb, yo[i]);
+        }
       }
-    }
-    if constexpr (NK == 2) {  // hand the other wave of the slice its two tiles
+      if constexpr (NK == 2) {  // hand the other wave of the slice its two tiles
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const f32x4 v = k ? yo[u] : yo[2 + u];
-        sm.xch[w + 4 * (1 - k)][u][lane] = make_float4(v[0], v[1], v[2], v[3]);
+        for (int u = 0; u < 2; ++u) {
+          const f32x4 v = k ? yo[u] : yo[2 + u];
+          sm.xch[w + 4 * (1 - k)][u][lane] = make_float4(v[0], v[1], v[2], v[3]);
+        }
       }
     }
     __syncthreads();  // M, x o w and the exchanged halves complete
 
     // ---- C. y^T for the wave's tiles; the state update
-    const auto ybuf = rows_buf(yb + t0 * xrow, t0, xrow * 2, kP * 2);
-    // y tile i (16 tokens) of the slice; KS 32-token k steps cover s <= t
-    auto y_tile = [&](const int i, const f32x4& yt, auto ks, u32x2& out) {
-      constexpr int KS = decltype(ks)::value;
-      f32x4 acc = {};
+    if constexpr (!ST) {
+      const auto ybuf = rows_buf(yb + t0 * xrow, t0, xrow * 2, kP * 2);
+      // y tile i (16 tokens) of the slice; KS 32-token k steps cover s <= t
+      auto y_tile = [&](const int i, const f32x4& yt, auto ks, u32x2& out) {
+        constexpr int KS = decltype(ks)::value;
+        f32x4 acc = {};
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const bf16x8 xa = lds8(&sm.xt[cb][4 * kk + lg][16 * w + lr][0]);
-        acc = mfma(xa, lds8(&sm.M[0][4 * kk + lg][16 * i + lr][0]), acc);
-        acc = mfma(xa, lds8(&sm.M[1][4 * kk + lg][16 * i + lr][0]), acc);
-      }
-      const int t = 16 * i + lr;
-      const float e = fast_exp2(sm.cs[cb][t] * kLog2e);
-      out = (u32x2){pack_bf16(__builtin_fmaf(e, yt[0], acc[0]), __builtin_fmaf(e, yt[1], acc[1])),
-                    pack_bf16(__builtin_fmaf(e, yt[2], acc[2]), __builtin_fmaf(e, yt[3], acc[3]))};
-    };
-    // the stores stay outside the branches so the wait on the prefetch at the top
-    // of the loop counts them exactly
-    auto y_store = [&](const int i, const u32x2& out) {
-      __builtin_amdgcn_raw_buffer_store_b64(out, ybuf, static_cast<uint32_t>((16 * i + lr) * xrow * 2 + (16 * w + 4 * lg) * 2),
-                                            0, 0);
-    };
-    using One = std::integral_constant<int, 1>;
-    using Two = std::integral_constant<int, 2>;
-    if constexpr (NK == 2) {  // tiles 2k and 2k + 1
-      f32x4 yt[2];
+        for (int kk = 0; kk < KS; ++kk) {
+          const bf16x8 xa = lds8(&sm.xt[cb][4 * kk + lg][16 * w + lr][0]);
+          acc = mfma(xa, lds8(&sm.M[0][4 * kk + lg][16 * i + lr][0]), acc);
+          acc = mfma(xa, lds8(&sm.M[1][4 * kk + lg][16 * i + lr][0]), acc);
+        }
+        const int t = 16 * i + lr;
+        const float e = fast_exp2(sm.cs[cb][t] * kLog2e);
+        out = (u32x2){pack_bf16(__builtin_fmaf(e, yt[0], acc[0]), __builtin_fmaf(e, yt[1], acc[1])),
+                      pack_bf16(__builtin_fmaf(e, yt[2], acc[2]), __builtin_fmaf(e, yt[3], acc[3]))};
+      };
+      // the stores stay outside the branches so the wait on the prefetch at the top
+      // of the loop counts them exactly
+      auto y_store = [&](const int i, const u32x2& out) {
+        __builtin_amdgcn_raw_buffer_store_b64(out, ybuf, static_cast<uint32_t>((16 * i + lr) * xrow * 2 + (16 * w + 4 * lg) * 2),
+                                              0, 0);
+      };
+      using One = std::integral_constant<int, 1>;
+      using Two = std::integral_constant<int, 2>;
+      if constexpr (NK == 2) {  // tiles 2k and 2k + 1
+        f32x4 yt[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float4 o = sm.xch[wi][u][lane];
-        yt[u] = k ? yo[2 + u] : yo[u];
-        yt[u][0] += o.x, yt[u][1] += o.y, yt[u][2] += o.z, yt[u][3] += o.w;
-      }
-      u32x2 out[2];
-      if (k == 0) {
-        y_tile(0, yt[0], One{}, out[0]);
-        y_tile(1, yt[1], One{}, out[1]);
+        for (int u = 0; u < 2; ++u) {
+          const float4 o = sm.xch[wi][u][lane];
+          yt[u] = k ? yo[2 + u] : yo[u];
+          yt[u][0] += o.x, yt[u][1] += o.y, yt[u][2] += o.z, yt[u][3] += o.w;
+        }
+        u32x2 out[2];
+        if (k == 0) {
+          y_tile(0, yt[0], One{}, out[0]);
+          y_tile(1, yt[1], One{}, out[1]);
+        } else {
+          y_tile(2, yt[0], Two{}, out[0]);
+          y_tile(3, yt[1], Two{}, out[1]);
+        }
+        y_store(2 * k, out[0]);
+        y_store(2 * k + 1, out[1]);
       } else {
-        y_tile(2, yt[0], Two{}, out[0]);
-        y_tile(3, yt[1], Two{}, out[1]);
-      }
-      y_store(2 * k, out[0]);
-      y_store(2 * k + 1, out[1]);
-    } else {
-      u32x2 out[4];
-      y_tile(0, yo[0], One{}, out[0]);
-      y_tile(1, yo[1], One{}, out[1]);
-      y_tile(2, yo[2], Two{}, out[2]);
-      y_tile(3, yo[3], Two{}, out[3]);
+        u32x2 out[4];
+        y_tile(0, yo[0], One{}, out[0]);
+        y_tile(1, yo[1], One{}, out[1]);
+        y_tile(2, yo[2], Two{}, out[2]);
+        y_tile(3, yo[3], Two{}, out[3]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) y_store(i, out[i]);
+        for (int i = 0; i < 4; ++i) y_store(i, out[i]);
+      }
     }
     {
+      if constexpr (ST) la_total += cs_end;
       const float dec = fast_exp2(cs_end * kLog2e);
       bf16x8 xh[2], xl[2];
 #pragma unroll
@@ -463,7 +508,13 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
     // wave reaches after finishing this chunk.
     if constexpr (kSsdStageBufs<N> == 1) __syncthreads();
   }
-  if (a.hT) {
+  if constexpr (ST) {
+    float* dst = a.ws_state + summary(seg) * kP * N + spart;
+#pragma unroll
+    for (int j = 0; j < NJK; ++j)
+      *reinterpret_cast<float4*>(dst + 16 * j) = make_float4(Hs[j][0], Hs[j][1], Hs[j][2], Hs[j][3]);
+    if (tid == 0) a.ws_la[summary(seg)] = la_total;
+  } else if (a.hT && seg == a.S - 1) {
 #pragma unroll
     for (int j = 0; j < NJK; ++j)
       *reinterpret_cast<float4*>(a.hT + sbase + 16 * j) = make_float4(Hs[j][0], Hs[j][1], Hs[j][2], Hs[j][3]);
@@ -486,11 +537,22 @@ hipError_t launch_ssd_n(const SsdProblem& p, hipStream_t stream) {
   k.h0 = p.h0;
   k.hT = p.hT;
   k.y = static_cast<uint16_t*>(p.y);
+  k.ws_state = p.ws_state;
+  k.ws_la = p.ws_la;
   k.L = p.seqlen;
+  k.seg_chunks = p.splits > 1 ? p.seg_chunks : (p.seqlen + kQ - 1) / kQ;
   k.H = static_cast<int>(p.nheads);
   k.G = static_cast<int>(p.ngroups);
-  hipLaunchKernelGGL((ssd_fwd_kernel<N, MODE, NW>), dim3(static_cast<unsigned>(p.nheads), static_cast<unsigned>(p.batch)),
-                     dim3(64 * NW), 0, stream, k);
+  k.S = p.splits > 1 ? p.splits : 1;
+  const unsigned gh = static_cast<unsigned>(p.nheads), gb = static_cast<unsigned>(p.batch);
+  if (k.S > 1) {  // summaries of every segment but the last, then the full pass
+    hipLaunchKernelGGL((ssd_fwd_kernel<N, MODE, NW, true>), dim3(gh, gb, static_cast<unsigned>(k.S - 1)), dim3(64 * NW),
+                       0, stream, k);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((ssd_fwd_kernel<N, MODE, NW, false>), dim3(gh, gb, static_cast<unsigned>(k.S)), dim3(64 * NW), 0,
+                     stream, k);
   return hipGetLastError();
 }
 

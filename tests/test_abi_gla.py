@@ -40,6 +40,7 @@ def _gla(a):
     (dict(shape=(2, 64, 8, 128, 2, 128)), -9),  # headdim 128
     (dict(shape=(2, 64, 8, 64, 3, 128)), -9),   # groups must divide heads
     (dict(shape=(2, 64, 8, 64, 2, 32)), -9),    # dstate 32
+    (dict(reserved=1), -9), (dict(time_splits=-1), -9), (dict(time_splits=65536), -9),
     (dict(q=0), -1), (dict(k=0), -1), (dict(v=0), -1), (dict(y=0), -1),
     (dict(v=FAKE + 2), -5), (dict(log_f=FAKE + 4), -5), (dict(hT=FAKE + 8), -5),
 ])
@@ -87,3 +88,22 @@ def test_workspace_checked_on_host():
     assert _gla(_args(feature_map=1, workspace=FAKE + (2 << 32), workspace_bytes=big)) == -6   # v
     assert _gla(_args(feature_map=1, workspace=FAKE + (7 << 32), workspace_bytes=big)) == -6   # y
     assert _gla(_args(feature_map=1, workspace=FAKE - 256, workspace_bytes=big)) == -6         # q
+
+
+def test_workspace_with_time_segments():
+    """The segment summaries follow phi(k) and phi(q) in the workspace; a
+    workspace too small for both drops an automatic split first."""
+    up = lambda n: (n + 255) // 256 * 256
+    shape = (1, 4096, 16, 64, 1, 64)  # 64 chunks, B*H = 16 -> 16 segments of 4 chunks
+    phi = 2 * up(4096 * 64 * 2)
+    summ = up(15 * 16 * 64 * 64 * 4) + up(15 * 16 * 4)
+    assert _ws_bytes(_args(shape=shape)) == summ
+    assert _ws_bytes(_args(shape=shape, feature_map=1)) == phi + summ
+    assert _ws_bytes(_args(shape=shape, feature_map=1, time_splits=1)) == phi
+    far = FAKE + (40 << 32)
+    plan = lambda a: ssm.lib().ssm_gla_plan(ctypes.byref(a))
+    assert plan(_args(shape=shape, feature_map=1, workspace=far, workspace_bytes=phi + summ)) == 16
+    assert plan(_args(shape=shape, feature_map=1, workspace=far, workspace_bytes=phi + summ - 1)) == 1
+    assert plan(_args(shape=shape, workspace=far, workspace_bytes=summ)) == 16
+    assert plan(_args(shape=shape, feature_map=1, time_splits=4, workspace=far, workspace_bytes=phi)) == -7
+    assert plan(_args(shape=shape, time_splits=4)) == -7

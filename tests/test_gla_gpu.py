@@ -154,3 +154,55 @@ def test_feature_map_pass_matches_in_kernel_map(case):
     yr, hr = oracle_gla(inp, True)
     check("y", y1.float().cpu().double().numpy(), yr, torch.bfloat16)
     check("hT", h1.cpu().double().numpy(), hr, torch.bfloat16)
+
+
+def _planned_splits(d, time_splits, feature_map):
+    y = torch.empty_like(d["v"])  # held until the plan is taken: the workspace must not reuse its memory
+    a = ssm.make_gla_args(*(d[k] for k in TENS), y=y, feature_map=feature_map, time_splits=time_splits)
+    ws = torch.empty(max(ssm.gla_workspace_bytes(a), 1), dtype=torch.uint8, device=DEV)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    return ssm.gla_plan(a)
+
+
+SPLIT_CASES = [
+    (dict(batch=2, nheads=4, ngroups=2, dstate=64, seqlen=64 * 13 + 17), 3),
+    (dict(batch=1, nheads=2, ngroups=1, dstate=256, seqlen=64 * 8 + 1), 9),
+    (dict(batch=1, nheads=4, ngroups=4, dstate=128, seqlen=64 * 11 + 40), 6),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[f"N{c[0]['dstate']}-L{c[0]['seqlen']}-S{c[1]}" for c in SPLIT_CASES])
+@pytest.mark.parametrize("mode", ["gated-h0", "linear", "linear-elu-h0"])
+def test_gla_time_split_all_elements(case, mode):
+    """Time segments against the oracle on every element; with the feature map
+    the summaries sit behind phi(k) and phi(q) in the workspace."""
+    shape, asked = case
+    inp = workloads.make_gla_inputs(GW[0], gated=mode.startswith("gated"), with_h0=mode.endswith("h0"),
+                                    seed_extra=(34,), **shape)
+    fm = "elu" in mode
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    assert _planned_splits(d, asked, fm) == asked
+    y, hT = ssm.gla_fwd(*(d[k] for k in TENS), feature_map=fm, return_final_state=True, time_splits=asked)
+    torch.cuda.synchronize()
+    yr, hr = oracle_gla(inp, fm)
+    check("y", y.float().cpu().double().numpy(), yr, torch.bfloat16)
+    check("hT", hT.cpu().double().numpy(), hr, torch.bfloat16)
+
+
+def test_gla_longctx_full_size_sampled_heads():
+    """mLSTM gates over one 32768-token sequence (B1 H64 P64 N128): 4 time
+    segments chosen by the library, as the bench launches it; three heads
+    against the oracle."""
+    w = workloads.GLA_BY_NAME["mlstm_longctx_B1_L32768_H64_P64_N128"]
+    inp = workloads.make_gla_inputs(w, with_h0=True)
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    assert _planned_splits(d, 0, w.feature_map) == 4
+    y, hT = gpu_gla(inp, w.feature_map)
+    for hsel in (0, 41, 63):
+        hi = torch.tensor([hsel])
+        sub = dict(inp, v=inp["v"].index_select(2, hi).contiguous(), h0=inp["h0"].index_select(1, hi).contiguous())
+        for k in ("log_f", "in_gate"):
+            sub[k] = inp[k].index_select(2, hi).contiguous()
+        yr, hr = oracle_gla(sub, w.feature_map)
+        check(f"y head {hsel}", y[:, :, hsel:hsel + 1], yr, torch.bfloat16)
+        check(f"hT head {hsel}", hT[:, hsel:hsel + 1], hr, torch.bfloat16)

@@ -123,3 +123,79 @@ def test_ssd_mamba2_full_size_sampled_heads():
         yr, hr = oracle.ssd(sub["x"], sub["dt"], sub["A"], inp["B"], inp["C"], D=sub["D"], dt_bias=sub["dt_bias"])
         check(f"y head {hsel}", y[:, :, hsel:hsel + 1], yr, torch.bfloat16)
         check(f"hT head {hsel}", hT[:, hsel:hsel + 1], hr, torch.bfloat16)
+
+
+def _planned_splits(d, time_splits):
+    """Segments the library runs for these device inputs (with the workspace it asks for)."""
+    y = torch.empty_like(d["x"])  # held until the plan is taken: the workspace must not reuse its memory
+    a = ssm.make_ssd_args(*(d[k] for k in TENS), y=y, time_splits=time_splits)
+    ws = torch.empty(max(ssm.ssd_workspace_bytes(a), 1), dtype=torch.uint8, device=DEV)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    return ssm.ssd_plan(a)
+
+
+# (shape, asked segments, segments run): ragged last chunks, one chunk per
+# segment, a last segment of one token
+SPLIT_CASES = [
+    (dict(batch=2, nheads=4, ngroups=2, dstate=64, seqlen=64 * 13 + 17), 3, 3),
+    (dict(batch=1, nheads=2, ngroups=1, dstate=128, seqlen=64 * 9), 9, 9),
+    (dict(batch=1, nheads=2, ngroups=1, dstate=256, seqlen=64 * 8 + 1), 9, 9),
+    (dict(batch=2, nheads=4, ngroups=2, dstate=128, seqlen=64 * 20 + 5), 7, 7),
+    (dict(batch=1, nheads=3, ngroups=1, dstate=64, seqlen=64 * 10), 4, 4),  # 10 chunks: 3, 3, 3, 1
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[f"N{c[0]['dstate']}-L{c[0]['seqlen']}-S{c[1]}" for c in SPLIT_CASES])
+@pytest.mark.parametrize("with_h0", [False, True], ids=["zero-state", "h0"])
+def test_ssd_time_split_all_elements(case, with_h0):
+    """Time segments (state-only pass, then the full pass folding the summaries)
+    against the oracle on every element of y and the final state."""
+    shape, asked, runs = case
+    inp = workloads.make_ssd_inputs(SW[0], with_h0=with_h0, seed_extra=(31,), **shape)
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    assert _planned_splits(d, asked) == runs
+    y, hT = ssm.ssd_fwd(*(d[k] for k in TENS), return_final_state=True, time_splits=asked)
+    torch.cuda.synchronize()
+    yr, hr = oracle_ssd(inp)
+    check("y", y.float().cpu().double().numpy(), yr, torch.bfloat16)
+    check("hT", hT.cpu().double().numpy(), hr, torch.bfloat16)
+
+
+def test_ssd_time_split_reuses_workspace():
+    """Two split calls in a row through one workspace, the second shorter: the
+    summaries of the first leave nothing behind."""
+    big = workloads.make_ssd_inputs(SW[0], batch=1, nheads=2, ngroups=1, dstate=128, seqlen=64 * 12, seed_extra=(32,))
+    small = workloads.make_ssd_inputs(SW[0], batch=1, nheads=2, ngroups=1, dstate=128, seqlen=64 * 5 + 9,
+                                      with_h0=True, seed_extra=(33,))
+    db = {k: (v.to(DEV) if v is not None else None) for k, v in big.items()}
+    ds = {k: (v.to(DEV) if v is not None else None) for k, v in small.items()}
+    y1 = torch.empty_like(db["x"])
+    a = ssm.make_ssd_args(*(db[k] for k in TENS), y=y1, time_splits=6)
+    ws = torch.empty(ssm.ssd_workspace_bytes(a), dtype=torch.uint8, device=DEV)
+    y1, h1 = ssm.ssd_fwd(*(db[k] for k in TENS), return_final_state=True, time_splits=6, workspace=ws, out=y1)
+    y2, h2 = ssm.ssd_fwd(*(ds[k] for k in TENS), return_final_state=True, time_splits=3, workspace=ws)
+    torch.cuda.synchronize()
+    for (y, h), inp in (((y1, h1), big), ((y2, h2), small)):
+        yr, hr = oracle_ssd(inp)
+        check("y", y.float().cpu().double().numpy(), yr, torch.bfloat16)
+        check("hT", h.cpu().double().numpy(), hr, torch.bfloat16)
+
+
+def test_ssd_longctx_full_size_sampled_heads():
+    """One sequence of 32768 tokens (B1 H64 P64 N128): 64 (b, h) pairs, so the
+    library cuts it into 4 time segments; as the bench launches it.  Three heads
+    checked against the oracle on every token."""
+    w = workloads.SSD_BY_NAME["mamba2_longctx_B1_L32768_H64_P64_N128"]
+    inp = workloads.make_ssd_inputs(w, with_h0=True)
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    assert _planned_splits(d, 0) == 4
+    y, hT = ssm.ssd_fwd(*(d[k] for k in TENS), return_final_state=True)
+    torch.cuda.synchronize()
+    y, hT = y.float().cpu().double().numpy(), hT.cpu().double().numpy()
+    for hsel in (0, 37, 63):
+        hi = torch.tensor([hsel])
+        yr, hr = oracle.ssd(inp["x"].index_select(2, hi).contiguous(), inp["dt"].index_select(2, hi).contiguous(),
+                            inp["A"].index_select(0, hi), inp["B"], inp["C"], D=inp["D"].index_select(0, hi),
+                            dt_bias=inp["dt_bias"].index_select(0, hi), s0=inp["h0"].index_select(1, hi))
+        check(f"y head {hsel}", y[:, :, hsel:hsel + 1], yr, torch.bfloat16)
+        check(f"hT head {hsel}", hT[:, hsel:hsel + 1], hr, torch.bfloat16)

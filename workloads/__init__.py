@@ -244,6 +244,8 @@ class SsdWorkload:
 SSD_WORKLOADS = [
     SsdWorkload(100, "ssd_small_B2_L200_H4_P64_G2_N64", 2, 200, 4, 64, 2, 64),
     SsdWorkload(101, "mamba2_B4_L8192_H64_P64_N128", 4, 8192, 64, 64, 1, 128),
+    # one long sequence: 64 (b, h) pairs for 256 compute units, the time-split case
+    SsdWorkload(102, "mamba2_longctx_B1_L32768_H64_P64_N128", 1, 32768, 64, 64, 1, 128),
 ]
 SSD_BY_NAME = {w.name: w for w in SSD_WORKLOADS}
 
@@ -310,6 +312,7 @@ GLA_WORKLOADS = [
     GlaWorkload(110, "gla_small_B2_L200_H4_P64_G2_N64", 2, 200, 4, 64, 2, 64, True, False),
     GlaWorkload(111, "mlstm_B4_L8192_H64_P64_N128", 4, 8192, 64, 64, 1, 128, True, False),
     GlaWorkload(112, "linattn_elu_B4_L8192_H64_P64_N128", 4, 8192, 64, 64, 1, 128, False, True),
+    GlaWorkload(113, "mlstm_longctx_B1_L32768_H64_P64_N128", 1, 32768, 64, 64, 1, 128, True, False),
 ]
 GLA_BY_NAME = {w.name: w for w in GLA_WORKLOADS}
 
