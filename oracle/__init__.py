@@ -96,6 +96,8 @@ class Oracle:
         self._lib.oracle_assoc_scan_f64.restype = ctypes.c_int
         self._lib.oracle_scan_bwd_f64.argtypes = [ctypes.POINTER(_Args), ctypes.POINTER(_Grads)]
         self._lib.oracle_scan_bwd_f64.restype = ctypes.c_int
+        self._lib.oracle_scan_bwd_zoh_f64.argtypes = [ctypes.POINTER(_Args), ctypes.POINTER(_Grads)]
+        self._lib.oracle_scan_bwd_zoh_f64.restype = ctypes.c_int
         i64 = ctypes.c_int64
         self._lib.oracle_ssd_f64.argtypes = [ctypes.POINTER(_SsdArgs)]
         self._lib.oracle_ssd_f64.restype = ctypes.c_int
@@ -168,11 +170,13 @@ class Oracle:
         del keep
         return y, hT
 
-    def scan_bwd(self, x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *, dy, dhT=None):
+    def scan_bwd(self, x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *, dy, dhT=None,
+                 zoh: bool = False):
         """Gradients of the scalar loss sum(dy * y) + sum(dhT * hT) with respect
         to every input, as a dict of float64 numpy arrays (keys x, delta, A, B,
         C, D, z, delta_bias, h0; an absent optional input has no entry, except
-        h0, whose gradient is always returned)."""
+        h0, whose gradient is always returned).  zoh=True differentiates the
+        zero-order-hold forward."""
         args, keep, _, _ = self._pack(x, delta, A, B, C, D, z, delta_bias, h0, False)
         xx, dd, AA, BB, CC, DD, zz, bb, hh = keep[:9]
         dy = self._f64(dy)
@@ -190,7 +194,8 @@ class Oracle:
         p = self._ptr
         g = _Grads(p(dy), p(dhT), p(out["x"]), p(out["delta"]), p(out["A"]), p(out["B"]), p(out["C"]),
                    p(out.get("D")), p(out.get("z")), p(out.get("delta_bias")), p(out["h0"]))
-        rc = self._lib.oracle_scan_bwd_f64(ctypes.byref(args), ctypes.byref(g))
+        fn = self._lib.oracle_scan_bwd_zoh_f64 if zoh else self._lib.oracle_scan_bwd_f64
+        rc = fn(ctypes.byref(args), ctypes.byref(g))
         if rc != 0:
             raise RuntimeError("oracle_scan_bwd_f64 failed")
         del keep

@@ -304,11 +304,22 @@ int oracle_assoc_scan_f64(const oracle_args *a) {
  *            carry_n = a_n lambda_n;
  *            after t = 0: dh0_n = carry_n.
  * SiLU'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))); softplus' = sigmoid.
+ * Zero-order hold (section 2.2; oracle_scan_bwd_zoh_f64): the input term is
+ * c_n B_t,n x with c_n = (a_n - 1) / A_n (delta where A_n = 0) in place of
+ * u B_t,n, so in the reverse step
+ *            dB_t,n += lambda_n c_n x,  dx = gy0 D + sum_n lambda_n c_n B_t,n,
+ *            gdelta = sum_n ga_n a_n A_n + x sum_n lambda_n B_t,n a_n
+ *                     (dc_n/ddelta = a_n),
+ *            dA_n += ga_n a_n delta + lambda_n B_t,n x dc_n/dA_n,
+ *            dc_n/dA_n = (delta a_n - c_n) / A_n, or near delta A_n = 0 (where
+ *            that difference cancels) its series delta^2 (1/2 + z/3 + z^2/8 +
+ *            z^3/30 + z^4/144), z = delta A_n.
  * Sums over b, t and d run in increasing index order.  Single-threaded: the
  * reductions over channels (dB, dC) and over batch rows (dA, dD, dbias)
  * would otherwise need merging; inputs here are small.
  * Pinned in tests/test_oracle_bwd.py by central finite differences of
- * oracle_scan_f64 (an independent computation) on every input element. */
+ * oracle_scan_f64 and oracle_scan_zoh_f64 (independent computations) on every
+ * input element. */
 typedef struct {
   const double *dy;   /* (B, L, D) required           */
   const double *dhT;  /* (B, D, N) or NULL (zero)      */
@@ -317,7 +328,28 @@ typedef struct {
 
 static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
 
-int oracle_scan_bwd_f64(const oracle_args *a, const oracle_grads *g) {
+/* d/dA_n of zoh_coef: (delta exp(delta A_n) - zoh_coef) / A_n, by its Taylor
+ * series in z = delta A_n where |z| < 1e-3 (the truncation is below z^5 / 840
+ * relative; the closed form would lose about 1e-16 / z to cancellation). */
+static double zoh_coef_dA(double dt, double An) {
+  const double z = dt * An;
+#if ORACLE_MUTANT == 28
+  (void)z;
+  return 0.0; /* the hold's own dependence on A left out */
+#else
+  if (fabs(z) < 1e-3) return dt * dt * (0.5 + z * (1.0 / 3.0 + z * (1.0 / 8.0 + z * (1.0 / 30.0 + z / 144.0))));
+  return (dt * exp(z) - expm1(z) / An) / An;
+#endif
+}
+
+static int scan_bwd(const oracle_args *a, const oracle_grads *g, int zoh);
+
+int oracle_scan_bwd_f64(const oracle_args *a, const oracle_grads *g) { return scan_bwd(a, g, 0); }
+
+/* The same gradients through the zero-order-hold forward (oracle_scan_zoh_f64). */
+int oracle_scan_bwd_zoh_f64(const oracle_args *a, const oracle_grads *g) { return scan_bwd(a, g, 1); }
+
+static int scan_bwd(const oracle_args *a, const oracle_grads *g, int zoh) {
   if (!a || !g || !a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !g->dy) return -1;
   if (a->batch < 0 || a->seqlen < 0 || a->dim < 0 || a->dstate <= 0) return -1;
   const int64_t Bn = a->batch, L = a->seqlen, D = a->dim, N = a->dstate;
@@ -341,7 +373,8 @@ int oracle_scan_bwd_f64(const oracle_args *a, const oracle_grads *g) {
         dl[t] = oracle_softplus(a->delta[i] + bias);
         for (int64_t n = 0; n < N; ++n) {
           const double hp = t > 0 ? hs[(t - 1) * N + n] : (a->h0 ? a->h0[(b * D + d) * N + n] : 0.0);
-          hs[t * N + n] = exp(dl[t] * a->A[d * N + n]) * hp + dl[t] * a->x[i] * a->Bm[(b * L + t) * N + n];
+          const double cn = zoh ? zoh_coef(dl[t], a->A[d * N + n]) : dl[t];
+          hs[t * N + n] = exp(dl[t] * a->A[d * N + n]) * hp + cn * a->x[i] * a->Bm[(b * L + t) * N + n];
         }
       }
       /* reverse */
@@ -363,21 +396,29 @@ int oracle_scan_bwd_f64(const oracle_args *a, const oracle_grads *g) {
         }
         const double gy0 = g->dy[i] * gate;
         if (g->dD) g->dD[d] += gy0 * xv;
-        double gu = 0.0, gdel = 0.0;
+        double gx = 0.0, gin = 0.0, gdel = 0.0;
         for (int64_t n = 0; n < N; ++n) {
           const int64_t bn = (b * L + t) * N + n;
           const double An = a->A[d * N + n], an = exp(dt * An);
           const double hp = t > 0 ? hs[(t - 1) * N + n] : (a->h0 ? a->h0[(b * D + d) * N + n] : 0.0);
           const double lam = gy0 * a->Cm[bn] + carry[n];
           const double ga = lam * hp;
-          if (g->dA) g->dA[d * N + n] += ga * an * dt;
+          /* input coefficient c_n and its derivatives in delta and A_n (Euler: delta, 1, 0) */
+          const double cn = zoh ? zoh_coef(dt, An) : dt;
+#if ORACLE_MUTANT == 29
+          const double dc_ddelta = 1.0; /* the Euler term's derivative kept under the hold */
+#else
+          const double dc_ddelta = zoh ? an : 1.0;
+#endif
+          if (g->dA) g->dA[d * N + n] += ga * an * dt + (zoh ? lam * a->Bm[bn] * xv * zoh_coef_dA(dt, An) : 0.0);
 #if ORACLE_MUTANT == 16
           gdel -= ga * an * An; /* sign of the decay term */
 #else
           gdel += ga * an * An;
 #endif
-          gu += lam * a->Bm[bn];
-          if (g->dB) g->dB[bn] += lam * dt * xv;
+          gx += lam * a->Bm[bn] * cn;
+          gin += lam * a->Bm[bn] * dc_ddelta;
+          if (g->dB) g->dB[bn] += lam * cn * xv;
           if (g->dC) g->dC[bn] += gy0 * hs[t * N + n];
 #if ORACLE_MUTANT == 15
           carry[n] = lam; /* decay missing from the carried adjoint */
@@ -385,8 +426,8 @@ int oracle_scan_bwd_f64(const oracle_args *a, const oracle_grads *g) {
           carry[n] = an * lam;
 #endif
         }
-        gdel += gu * xv;
-        if (g->dx) g->dx[i] = gy0 * Dd + gu * dt;
+        gdel += gin * xv;
+        if (g->dx) g->dx[i] = gy0 * Dd + gx;
 #if ORACLE_MUTANT == 18
         const double graw = gdel; /* softplus derivative missing */
 #else
