@@ -363,7 +363,8 @@ def bench_backward(w, args, ssm, torch):
     names = ("x", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0")
     grads = {k: torch.empty_like(d[k]) for k in names if k != "h0" and d[k] is not None}
     grads["h0"] = torch.empty(w.batch, w.dim, w.dstate, dtype=torch.float32, device=dev)
-    a0 = ssm.make_bwd_args(*(d[k] for k in names), dy=dy, dhT=dhT, grads=grads, time_splits=args.time_splits)
+    a0 = ssm.make_bwd_args(*(d[k] for k in names), dy=dy, dhT=dhT, grads=grads, time_splits=args.time_splits,
+                           generic_a=args.generic_a, zoh=args.zoh)
     nbytes = ssm.bwd_workspace_bytes(a0)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     a0.workspace, a0.workspace_bytes = ws.data_ptr(), nbytes
@@ -406,7 +407,8 @@ def bench_backward(w, args, ssm, torch):
         "scaling": "weak", "vs_baseline": None, "dtype": io_dtype(w), "state_dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "pass": "backward", "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "dstate": w.dstate, "io_dtype": str(w.dtype).replace("torch.", ""), "gate": w.gate,
-                   "time_splits": splits, "workspace_bytes": nbytes},
+                   "time_splits": splits, "workspace_bytes": nbytes,
+                   "input_term": "zero-order hold" if args.zoh else "Euler"},
         "roofline": _roofline(alg, call_s, "ssm_scan_bwd (local, combine, main, two reductions)"),
     }
     if not args.no_cpu_baseline:
@@ -427,7 +429,7 @@ def bench_backward(w, args, ssm, torch):
         dhs = cot["dhT"][:1, :nd] if w.final_state else None
         log(f"cpu baseline (oracle backward, batch row 0, {nd} channels) ...")
         t = time.perf_counter()
-        oracle.scan_bwd(*(sub[k] for k in names), dy=dys, dhT=dhs)
+        oracle.scan_bwd(*(sub[k] for k in names), dy=dys, dhT=dhs, zoh=args.zoh)
         sec = time.perf_counter() - t
         el = w.seqlen * nd * w.dstate
         out["cpu_baseline"] = {

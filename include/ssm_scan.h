@@ -68,7 +68,9 @@ enum ssm_flags {
   /* Zero-order-hold input term (section 2.2: Bbar = (delta A)^-1
    * (exp(delta A) - I) delta B) instead of the Euler term delta B: state n
    * receives (exp(delta A[d,n]) - 1) / A[d,n] * B[n] * x (delta * B[n] * x where
-   * A[d,n] == 0).  Forward only: ssm_scan_bwd rejects it (SSM_ERR_VARIANT). */
+   * A[d,n] == 0).  ssm_scan_bwd takes it too and differentiates that
+   * forward (dc/ddelta = exp(delta A), dc/dA = (delta exp(delta A) - c) / A
+   * for c the coefficient above). */
   SSM_FLAG_ZOH = 2,
   /* Time-split calls only: compose the segments' summaries with a
    * wave-level associative scan in one extra launch (DPP row shifts and
@@ -165,7 +167,7 @@ int64_t ssm_scan_plan(const ssm_scan_args *args);
 typedef struct ssm_scan_bwd_args {
   int64_t batch, seqlen, dim, dstate; /* as ssm_scan_args; N <= 64           */
   int32_t dtype;                      /* ssm_dtype of x, delta, B, C, z, dy and the (B, L, .) gradients */
-  int32_t flags;                      /* ssm_flags: SSM_FLAG_GENERIC_A as for the forward */
+  int32_t flags;                      /* ssm_flags: SSM_FLAG_GENERIC_A, SSM_FLAG_ZOH as for the forward */
   const void *x;           /* (B, L, D)                                        required */
   const void *delta;       /* (B, L, D) raw step size                          required */
   const float *A;          /* (D, N)                                           required */

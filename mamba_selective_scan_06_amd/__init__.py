@@ -281,10 +281,10 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
 
 
 def make_bwd_args(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *, dy, dhT=None,
-                  grads=None, workspace=None, time_splits=0, generic_a=False) -> ScanBwdArgs:
+                  grads=None, workspace=None, time_splits=0, generic_a=False, zoh=False) -> ScanBwdArgs:
     """Check shapes/dtypes/devices and fill an ssm_scan_bwd_args.  `grads` maps
     input names (x, delta, A, B, C, D, z, delta_bias, h0) to output tensors."""
-    fa = make_args(x, delta, A, B, C, D, z, delta_bias, h0, generic_a=generic_a)
+    fa = make_args(x, delta, A, B, C, D, z, delta_bias, h0, generic_a=generic_a, zoh=zoh)
     bsz, L, dim = x.shape
     N = A.shape[1]
     io, dev, f32 = x.dtype, x.device, torch.float32
@@ -327,11 +327,11 @@ def bwd_plan(args: ScanBwdArgs) -> int:
 
 
 def scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *, dy, dhT=None,
-             wanted=None, workspace=None, time_splits=0, generic_a=False):
+             wanted=None, workspace=None, time_splits=0, generic_a=False, zoh=False):
     """Backward selective scan on the GPU: gradients of sum(dy * y) + sum(dhT * hT)
     with respect to the inputs, as a dict keyed like the inputs (x, delta, A, B,
     C, h0 always; D, z, delta_bias when given).  `wanted` restricts the outputs
-    to those names.  Launches on torch's current HIP stream and does not
+    to those names; zoh=True differentiates the zero-order-hold forward.  Launches on torch's current HIP stream and does not
     synchronise."""
     if not x.is_cuda:
         raise ValueError("scan_bwd runs on the GPU only: move the tensors to a HIP device")
@@ -349,7 +349,7 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *, dy,
         else:
             grads[k] = torch.empty_like(given[k])
     args = make_bwd_args(x, delta, A, B, C, D, z, delta_bias, h0, dy=dy, dhT=dhT, grads=grads,
-                         time_splits=time_splits, generic_a=generic_a)
+                         time_splits=time_splits, generic_a=generic_a, zoh=zoh)
     if workspace is None:
         nbytes = L_.ssm_scan_bwd_workspace_bytes(ctypes.byref(args))
         if nbytes < 0:

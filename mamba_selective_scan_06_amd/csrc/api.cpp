@@ -197,7 +197,7 @@ int validate_bwd(const ssm_scan_bwd_args* a) {
   if (a->dstate < 1 || a->dstate > ssm::kBwdMaxState) return SSM_ERR_DSTATE;
   if (a->dtype != SSM_DTYPE_F32 && a->dtype != SSM_DTYPE_BF16) return SSM_ERR_DTYPE;
   if (a->batch > 65535) return SSM_ERR_SHAPE;
-  if (a->flags & ~static_cast<int32_t>(SSM_FLAG_GENERIC_A)) return SSM_ERR_VARIANT;
+  if (a->flags & ~static_cast<int32_t>(SSM_FLAG_GENERIC_A | SSM_FLAG_ZOH)) return SSM_ERR_VARIANT;
   if (a->time_splits < 0 || a->reserved != 0) return SSM_ERR_VARIANT;
   int64_t bl, bld, bln, bd, bdn, dn, tmp;
   if (!mul_ok(a->batch, a->seqlen, &bl) || !mul_ok(bl, a->dim, &bld) || !mul_ok(bl, a->dstate, &bln) ||

@@ -13,6 +13,12 @@
 //   gdelta = sum_n ga_n a_n A_n + x sum_n lam_n B_t,n,
 //   dx = gy0 D + delta sum_n lam_n B_t,n,  draw = gdelta sigmoid(v),
 //   dbias += draw,  g_n = a_n lam_n;  dh0 = g after t = 0.
+// Under the zero-order hold (section 2.2) the input term is c_n B_t,n x with
+// c_n = (a_n - 1) / A_n in place of u B_t,n, which changes four lines:
+//   dB_t,n += lam_n c_n x,  dx = gy0 D + sum_n lam_n c_n B_t,n,
+//   gdelta = sum_n ga_n a_n A_n + x sum_n lam_n B_t,n a_n   (dc_n/ddelta = a_n),
+//   dA_n += ga_n a_n delta + lam_n B_t,n x dc_n/dA_n;
+// the decays, the adjoint's recurrence and the segment fix-ups are the same.
 //
 // Parallel layout.  G = ceil(N / 8) adjacent lanes share one channel (b, d),
 // each owning K = 8 consecutive states (K = 4 when N <= 4), so one wave holds
@@ -47,6 +53,30 @@ namespace ssm {
 namespace {
 
 __device__ __forceinline__ float sigmoid_f32(float v) { return fast_rcp(1.0f + fast_exp2(-v * kLog2e)); }
+
+// d/dA_n of the hold's input coefficient c = (a - 1) / A_n, a = exp(z),
+// z = delta A_n: (delta a - c) / A_n.  That difference cancels as z -> 0, so
+// for |z| < 1/2 the series delta^2 sum_{k>=1} k z^(k-1) / (k+1)! is taken
+// through z^7 (truncation below 3e-8 relative).  One v_cmp + v_cndmask picks
+// the branch after both are computed (A_n = 0: z = 0, the series; the closed
+// form's 0 * inf is discarded).
+__device__ __forceinline__ float zoh_coef_dA(float dt, float inv_An, float a, float c, float z) {
+  float p = __builtin_fmaf(z, 1.0f / 45360.0f, 1.0f / 5760.0f);
+  p = __builtin_fmaf(z, p, 1.0f / 840.0f);
+  p = __builtin_fmaf(z, p, 1.0f / 144.0f);
+  p = __builtin_fmaf(z, p, 1.0f / 30.0f);
+  p = __builtin_fmaf(z, p, 1.0f / 8.0f);
+  p = __builtin_fmaf(z, p, 1.0f / 3.0f);
+  p = __builtin_fmaf(z, p, 0.5f);
+  const float series = dt * dt * p;
+  const float closed = __builtin_fmaf(dt, a, -c) * inv_An;
+  float r;
+  asm("v_cmp_gt_f32_e64 vcc, %4, |%1|\n\tv_cndmask_b32_e32 %0, %3, %2, vcc"
+      : "=v"(r)
+      : "v"(z), "v"(series), "v"(closed), "s"(0.5f)
+      : "vcc");
+  return r;
+}
 
 template <bool B>
 struct Tag {
@@ -440,7 +470,7 @@ struct RevStage {
 // ---- 1. per-segment local passes ---------------------------------------------------
 // Chunks of T tokens are unrolled with all their loads issued first, so that
 // they are in flight together.
-template <typename S, int K, int G, bool FULL, bool GATE>
+template <typename S, int K, int G, bool FULL, bool GATE, bool ZOH>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2, 4))) void bwd_local_kernel(
     const S* __restrict__ x, const S* __restrict__ dl, const float* __restrict__ A, const S* __restrict__ Bm,
     const S* __restrict__ Cm, const S* __restrict__ z, const float* __restrict__ bias, const S* __restrict__ dy,
@@ -449,10 +479,11 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2, 4))) 
   constexpr int T = bwd_chunk_len(K);
   const Chain<G> c = chain_of<K, G>(D, L, seg_len);
   const Seg<S> sg(c, x, dl, Bm, Cm, z, dy, L, D, N);
-  float A2[K], h[K];
+  float A2[K], h[K], iA[ZOH ? K : 1];  // iA: 1 / A_n for the hold's coefficient
   load_vec<FULL, K>(A + c.d * N, c.n0, N, A2);
 #pragma unroll
   for (int k = 0; k < K; ++k) {
+    if constexpr (ZOH) iA[k] = 1.0f / A2[k];
     A2[k] *= kLog2e;
     h[k] = 0.0f;
   }
@@ -490,13 +521,19 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2, 4))) 
     for (int j = 0; j < T; ++j) {
       if (!RAGGED || t0 + j < c.t_end) {
         const float dt = softplus_f32(bits_to_f32<S>(st.dl[j]) + bs);
-        const float u = dt * bits_to_f32<S>(st.x[j]);
+        const float xv = bits_to_f32<S>(st.x[j]);
+        const float u = dt * xv;
         ds += dt;
         float Bv[K], an[K];
         st.b[j].unpack(Bv, c.n0, N);
         decays<decltype(structs)::value>(dt, A2, A2r, an);
 #pragma unroll
-        for (int k = 0; k < K; ++k) h[k] = __builtin_fmaf(an[k], h[k], u * Bv[k]);
+        for (int k = 0; k < K; ++k) {
+          if constexpr (ZOH)
+            h[k] = __builtin_fmaf(an[k], h[k], (zoh_coef(dt, A2[k] * kLn2, iA[k], an[k]) * xv) * Bv[k]);
+          else
+            h[k] = __builtin_fmaf(an[k], h[k], u * Bv[k]);
+        }
       }
     }
   };
@@ -574,7 +611,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2, 4))) 
 }
 
 // ---- 3. the adjoint walk ------------------------------------------------------------------
-template <typename S, int K, int G, bool FULL, bool GATE>
+template <typename S, int K, int G, bool FULL, bool GATE, bool ZOH>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(FULL ? 2 : 1, 2))) void bwd_main_kernel(
     const S* __restrict__ x, const S* __restrict__ dl, const float* __restrict__ A, const S* __restrict__ Bm,
     const S* __restrict__ Cm, const float* __restrict__ Dsk, const S* __restrict__ z,
@@ -603,11 +640,13 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(FULL ? 2
   const Rsrc rpC = make_buf(pC + (c.b * L + c.t_begin) * nblk * N, static_cast<uint32_t>(c.t_end - c.t_begin) * prow);
 
   float A2[K], g[K], gA[K], hin[K];  // hin: true state entering the segment
+  float iA[ZOH ? K : 1];              // 1 / A_n for the hold's coefficient
   load_vec<FULL, K>(A + c.d * N, c.n0, N, A2);
   load_vec<FULL, K>(segc + si * N, c.n0, N, g);
   load_vec<FULL, K>(segh + si * N, c.n0, N, hin);
 #pragma unroll
   for (int k = 0; k < K; ++k) {
+    if constexpr (ZOH) iA[k] = 1.0f / A2[k];
     A2[k] *= kLog2e;
     gA[k] = 0.0f;
   }
@@ -680,7 +719,13 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(FULL ? 2
         rb[j].unpack(Bv, c.n0, N);
         decays<STRUCT>(dts[j], A2, A2r, an);
 #pragma unroll
-        for (int k = 0; k < K; ++k) hs[j + 1][k] = __builtin_fmaf(an[k], hs[j][k], u * Bv[k]);
+        for (int k = 0; k < K; ++k) {
+          if constexpr (ZOH)
+            hs[j + 1][k] =
+                __builtin_fmaf(an[k], hs[j][k], (zoh_coef(dts[j], A2[k] * kLn2, iA[k], an[k]) * xv[j]) * Bv[k]);
+          else
+            hs[j + 1][k] = __builtin_fmaf(an[k], hs[j][k], u * Bv[k]);
+        }
       }
     }
 #pragma unroll
@@ -714,8 +759,11 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(FULL ? 2
       gDacc = __builtin_fmaf(gy0, x_t, gDacc);
       // inactive lanes add nothing to the channel sums
       const float u_act = c.active ? u : 0.0f;
+      const float x_act = c.active ? x_t : 0.0f;
       const float gy_act = c.active ? gy0 : 0.0f;
-      float gu = 0.0f, gdel = 0.0f;
+      // gu: sum_n lam_n B_n dc_n/ddelta (Euler: dc/ddelta = 1; hold: a_n);
+      // gx: the hold's sum_n lam_n B_n c_n for dx (Euler: delta gu)
+      float gu = 0.0f, gdel = 0.0f, gx = 0.0f;
       float vb[K], vc[K], an[K];
       decays<STRUCT>(dt, A2, A2r, an);
 #pragma unroll
@@ -725,8 +773,18 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(FULL ? 2
         const float gaa = g[k] * hs[j][k];  // lam a_n h_{t-1}: the decay's share
         gA[k] = __builtin_fmaf(gaa, dt, gA[k]);
         gdel = __builtin_fmaf(gaa, A2[k], gdel);  // A scaled by log2 e; undone below
-        gu = __builtin_fmaf(lam, Bv[k], gu);
-        vb[k] = lam * u_act;
+        if constexpr (ZOH) {
+          const float Ak = A2[k] * kLn2;
+          const float ck = zoh_coef(dt, Ak, iA[k], an[k]);
+          const float lb = lam * Bv[k];
+          gA[k] = __builtin_fmaf(lb * x_t, zoh_coef_dA(dt, iA[k], an[k], ck, dt * Ak), gA[k]);
+          gu = __builtin_fmaf(lb, an[k], gu);
+          gx = __builtin_fmaf(lb, ck, gx);
+          vb[k] = lam * (ck * x_act);
+        } else {
+          gu = __builtin_fmaf(lam, Bv[k], gu);
+          vb[k] = lam * u_act;
+        }
         vc[k] = gy_act * hs[j + 1][k];
       }
       gu = group_sum<G>(gu);
@@ -734,7 +792,10 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(FULL ? 2
       // softplus' = sigmoid, taken as exp(v - softplus(v)), exact in both tails
       const float graw = gdel * fast_exp2(lsg[j] * kLog2e);
       gbacc += graw;
-      st1<S>(rgx, vst, so, __builtin_fmaf(gy0, Dd, gu * dt));
+      if constexpr (ZOH)
+        st1<S>(rgx, vst, so, __builtin_fmaf(gy0, Dd, group_sum<G>(gx)));
+      else
+        st1<S>(rgx, vst, so, __builtin_fmaf(gy0, Dd, gu * dt));
       st1<S>(rgdl, vst, so, graw);
       channel_sum<K, G>(vb, c.lane);
       channel_sum<K, G>(vc, c.lane);
@@ -782,7 +843,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
 
 unsigned blocks256(int64_t n) { return static_cast<unsigned>((n + 255) / 256); }
 
-template <typename S, int K, int G, bool FULL, bool GATE>
+template <typename S, int K, int G, bool FULL, bool GATE, bool ZOH>
 hipError_t launch_bwd_t(const BwdProblem& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.nblk / G), static_cast<unsigned>(p.batch), static_cast<unsigned>(p.splits));
   const dim3 block(64 * G);
@@ -793,14 +854,14 @@ hipError_t launch_bwd_t(const BwdProblem& p, hipStream_t stream) {
   const auto* Cm = static_cast<const S*>(p.C);
   const auto* z = static_cast<const S*>(p.z);
   const auto* dy = static_cast<const S*>(p.dy);
-  hipLaunchKernelGGL((bwd_local_kernel<S, K, G, FULL, GATE>), grid, block, 0, stream, x, dl, p.A, Bm, Cm, z, p.delta_bias,
+  hipLaunchKernelGGL((bwd_local_kernel<S, K, G, FULL, GATE, ZOH>), grid, block, 0, stream, x, dl, p.A, Bm, Cm, z, p.delta_bias,
                      dy, p.ck, p.ckds, p.segh, p.segc, p.segds, p.seqlen, p.dim, N, p.seg_len, p.nck,
                      static_cast<int64_t>(p.splits), p.flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = bwd::launch_combine(p, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_main_kernel<S, K, G, FULL, GATE>), grid, block, 0, stream, x, dl, p.A, Bm, Cm, p.D, z,
+  hipLaunchKernelGGL((bwd_main_kernel<S, K, G, FULL, GATE, ZOH>), grid, block, 0, stream, x, dl, p.A, Bm, Cm, p.D, z,
                      p.delta_bias, dy, p.ck, p.ckds, p.segh, p.segc, static_cast<S*>(p.dx),
                      static_cast<S*>(p.ddelta), static_cast<S*>(p.dz), p.dh0, p.pB, p.pC, p.pA, p.pD, p.pbias,
                      p.seqlen, p.dim, N, p.seg_len, p.nck, static_cast<int64_t>(p.splits), p.flags);
@@ -817,9 +878,15 @@ hipError_t launch_bwd_t(const BwdProblem& p, hipStream_t stream) {
   return e;
 }
 
+template <typename S, int K, int G, bool FULL, bool GATE>
+hipError_t launch_bwd_z(const BwdProblem& p, hipStream_t stream) {
+  return (p.flags & kFlagZoh) ? launch_bwd_t<S, K, G, FULL, GATE, true>(p, stream)
+                              : launch_bwd_t<S, K, G, FULL, GATE, false>(p, stream);
+}
+
 template <typename S, int K, int G, bool FULL>
 hipError_t launch_bwd_f(const BwdProblem& p, hipStream_t stream) {
-  return p.z ? launch_bwd_t<S, K, G, FULL, true>(p, stream) : launch_bwd_t<S, K, G, FULL, false>(p, stream);
+  return p.z ? launch_bwd_z<S, K, G, FULL, true>(p, stream) : launch_bwd_z<S, K, G, FULL, false>(p, stream);
 }
 
 template <typename S, int K, int G>

@@ -40,8 +40,7 @@ def _bwd(a):
     (dict(x=0), -1), (dict(delta=0), -1), (dict(A=0), -1), (dict(B=0), -1), (dict(C=0), -1), (dict(dy=0), -1),
     (dict(z=0), -1),  # dz is given, so z is needed
     (dict(dx=FAKE + 4), -5), (dict(dhT=FAKE + 8), -5), (dict(workspace=FAKE + 2), -5),
-    (dict(flags=2), -9),  # the zero-order hold is forward only
-    (dict(flags=4), -9), (dict(time_splits=-1), -9), (dict(reserved=1), -9),
+    (dict(flags=4), -9), (dict(flags=8), -9),  # the carry scan is forward only; 8 is no flag (dict(time_splits=-1), -9), (dict(reserved=1), -9),
     (dict(workspace=0), -7),
     (dict(workspace_bytes=16), -7),
 ])
@@ -104,3 +103,12 @@ def test_dstate_limit_and_lane_layout():
     L = ssm.lib()
     for n in (1, 3, 4, 5, 8, 12, 16, 17, 32, 33, 64):
         assert L.ssm_scan_bwd_plan(ctypes.byref(_args(shape=(1, 64, 64, n)))) >= 1
+
+
+def test_zero_order_hold_passes_host_checks():
+    """SSM_FLAG_ZOH (and with GENERIC_A) is a valid backward flag: the host
+    checks get as far as the workspace, and the plan and size queries accept it."""
+    for flags in (2, 3):
+        assert _bwd(_args(flags=flags, workspace=0)) == -7
+        assert ssm.lib().ssm_scan_bwd_plan(ctypes.byref(_args(flags=flags))) >= 1
+        assert ssm.lib().ssm_scan_bwd_workspace_bytes(ctypes.byref(_args(flags=flags))) > 0
