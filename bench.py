@@ -348,6 +348,22 @@ def bench_decode(w, args, ssm, torch):
     return out
 
 
+def time_calls(fn, torch, dev, args):
+    """Mean seconds per call of fn on torch's current stream (HIP events), after warmup."""
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(max(args.warmup, 1)):
+        fn()
+    torch.cuda.synchronize()
+    n = max(args.steps, 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+
+
 def bench_backward(w, args, ssm, torch):
     """One step = one ssm_scan_bwd over the workload: every gradient (x, delta,
     z, A, B, C, D, delta_bias, h0) from dy (and dhT when the workload returns
@@ -363,8 +379,20 @@ def bench_backward(w, args, ssm, torch):
     names = ("x", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0")
     grads = {k: torch.empty_like(d[k]) for k in names if k != "h0" and d[k] is not None}
     grads["h0"] = torch.empty(w.batch, w.dim, w.dstate, dtype=torch.float32, device=dev)
+    ck, fwd_ck = None, None
+    if args.checkpoints:
+        # the training forward: y plus the states the backward starts its chunks from
+        ck = torch.empty(ssm.checkpoint_shape(w.batch, w.seqlen, w.dim, w.dstate), dtype=torch.float32, device=dev)
+        y = torch.empty_like(d["x"])
+        fwd_ck = time_calls(lambda: ssm.scan_fwd(*(d[k] for k in names), out=y, checkpoints=ck,
+                                                 generic_a=args.generic_a, zoh=args.zoh), torch, dev, args)
+        fwd_plain = time_calls(lambda: ssm.scan_fwd(*(d[k] for k in names), out=y, generic_a=args.generic_a,
+                                                    zoh=args.zoh), torch, dev, args)
+        ssm.scan_fwd(*(d[k] for k in names), out=y, checkpoints=ck, generic_a=args.generic_a, zoh=args.zoh)
+        torch.cuda.synchronize()
+        log(f"forward with checkpoints {fwd_ck * 1e3:.3f} ms, without {fwd_plain * 1e3:.3f} ms")
     a0 = ssm.make_bwd_args(*(d[k] for k in names), dy=dy, dhT=dhT, grads=grads, time_splits=args.time_splits,
-                           generic_a=args.generic_a, zoh=args.zoh)
+                           generic_a=args.generic_a, zoh=args.zoh, checkpoints=ck)
     nbytes = ssm.bwd_workspace_bytes(a0)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     a0.workspace, a0.workspace_bytes = ws.data_ptr(), nbytes
@@ -399,6 +427,8 @@ def bench_backward(w, args, ssm, torch):
     alg += 4 * bln * es  # B, C read; dB, dC written
     alg += 2 * w.dim * w.dstate * 4 + 4 * w.dim * 4  # A read, dA written; D, bias read, dD, dbias written
     alg += bdn * 4 * (2 if w.final_state else 1) + (bdn * 4 if w.h0_std > 0 else 0)  # dhT, dh0, h0
+    if ck is not None:
+        alg += ck.numel() * 4  # the checkpoints read back
     ms_per_step = elapsed * 1e3 / steps
     out = {
         "metric": "backward scan GElem/s (B*L*D*N) + % HBM roofline",
@@ -408,9 +438,14 @@ def bench_backward(w, args, ssm, torch):
         "config": {"workload": w.name, "pass": "backward", "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "dstate": w.dstate, "io_dtype": str(w.dtype).replace("torch.", ""), "gate": w.gate,
                    "time_splits": splits, "workspace_bytes": nbytes,
-                   "input_term": "zero-order hold" if args.zoh else "Euler"},
+                   "input_term": "zero-order hold" if args.zoh else "Euler",
+                   "states": "from the forward's checkpoints" if ck is not None else "recomputed"},
         "roofline": _roofline(alg, call_s, "ssm_scan_bwd (local, combine, main, two reductions)"),
     }
+    if ck is not None:
+        out["forward_with_checkpoints_ms"] = round(fwd_ck * 1e3, 4)
+        out["forward_without_checkpoints_ms"] = round(fwd_plain * 1e3, 4)
+        out["checkpoint_bytes"] = ck.numel() * 4
     if not args.no_cpu_baseline:
         import oracle
         nd = min(w.dim, 512)
@@ -661,6 +696,9 @@ def main():
                     help="time-split calls compose segment summaries with the wave-level scan launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true", help="time ssm_scan_bwd (all gradients) instead")
+    ap.add_argument("--checkpoints", action="store_true",
+                    help="with --backward: the backward starts from the forward's checkpoints (the forward writing "
+                         "them is timed on its own and reported beside)")
     ap.add_argument("--prologue", action="store_true", help="time the conv1d + SiLU prologue on x instead")
     ap.add_argument("--ssd", nargs="?", const="mamba2_B4_L8192_H64_P64_N128", default=None, metavar="WORKLOAD",
                     help="time the Mamba-2 SSD layer instead")

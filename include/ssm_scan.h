@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 3
+#define SSM_SCAN_ABI_VERSION 4
 
 /* Element type of x, delta, B, C, z and y.  A, D, delta_bias, h0, hT are
  * always fp32, and all arithmetic (state, accumulation) is fp32. */
@@ -104,7 +104,23 @@ typedef struct ssm_scan_args {
   int64_t workspace_bytes; /* size of workspace in bytes                               */
   int32_t variant;         /* ssm_variant; 0 = automatic                               */
   int32_t time_splits;     /* segments per sequence: 0 = automatic, 1 = none, >1 = that many (NSPLIT only) */
+  float *checkpoints;      /* states for ssm_scan_bwd, or NULL (see below)              */
 } ssm_scan_args;
+
+/* Checkpoints.  A training forward can hand the backward the states it
+ * passes through, so that ssm_scan_bwd does not run the forward recurrence
+ * again (section 3.3's recomputation is then limited to the few tokens
+ * inside each chunk).  With T = 8 tokens per chunk (16 when N <= 4), entry
+ * i of `checkpoints` holds the state after token (i + 1) T - 1, i.e. the
+ * state entering chunk i + 1; the state entering chunk 0 is h0.  The states
+ * of an entry are cut into four quarters of M = ceil(N / 4): state n of
+ * channel d sits at [b][i][n / M][d][n % M] of a (B, ceil(L / T) - 1, 4, D, M)
+ * fp32 array (the layout in which the forward's four state-holding waves each
+ * write one contiguous block), ssm_scan_checkpoint_bytes bytes, 16-byte
+ * aligned, not overlapping any other tensor.  Every position of a state
+ * n < N is written.  The states are the ones the forward computes for y (time
+ * splitting included), in the discretisation its flags select. */
+int64_t ssm_scan_checkpoint_bytes(const ssm_scan_args *args);
 
 /* Forward selective scan, y (and optionally hT) from the inputs above.
  * With seqlen == 0, y is empty and hT (if given) receives h0 (or zeros).
@@ -192,6 +208,9 @@ typedef struct ssm_scan_bwd_args {
   int64_t workspace_bytes; /* its size                                                  */
   int32_t time_splits;     /* segments per sequence: 0 = automatic, >= 1 = that many    */
   int32_t reserved;        /* must be 0                                                 */
+  const float *checkpoints; /* NULL, or the checkpoints ssm_scan_fwd wrote for these same
+                               inputs and flags (h0 included): the forward recurrence is
+                               then not run again, and the workspace is smaller          */
 } ssm_scan_bwd_args;
 
 /* Backward scan.  Errors as for ssm_scan_fwd, plus: SSM_ERR_NULL when a
@@ -199,7 +218,8 @@ typedef struct ssm_scan_bwd_args {
  * gradient overlaps an input or another gradient; SSM_ERR_WORKSPACE when the
  * workspace is NULL or smaller than ssm_scan_bwd_workspace_bytes (required
  * whenever B * L * D > 0); SSM_ERR_VARIANT for unknown flags, a negative
- * time_splits or reserved != 0.  The workspace is overwritten; its contents
+ * time_splits or reserved != 0; SSM_ERR_ALIGN / SSM_ERR_ALIAS for checkpoints
+ * as for an input.  The workspace is overwritten; its contents
  * on entry do not matter.  Problems with L == 0 give dh0 = dhT (or zeros) and
  * zero dA, dD, ddelta_bias; with B == 0 or D == 0 every non-empty gradient is
  * zero. */

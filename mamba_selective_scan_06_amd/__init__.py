@@ -31,10 +31,11 @@ VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 FLAG_GENERIC_A = 1
 FLAG_ZOH = 2
 FLAG_CARRY_SCAN = 4
-ABI_VERSION = 3  # SSM_SCAN_ABI_VERSION of include/ssm_scan.h
+ABI_VERSION = 4  # SSM_SCAN_ABI_VERSION of include/ssm_scan.h
 
 # Exported symbols the header declares (checked by the tests).
-EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_noalloc", "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_scan_bwd",
+EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_noalloc", "ssm_scan_workspace_bytes", "ssm_scan_plan",
+           "ssm_scan_checkpoint_bytes", "ssm_scan_bwd",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd_plan", "ssm_conv1d_silu_fwd", "ssm_ssd_fwd",
            "ssm_ssd_workspace_bytes", "ssm_ssd_plan", "ssm_gla_fwd", "ssm_gla_workspace_bytes", "ssm_gla_plan",
            "ssm_scan_strerror", "ssm_scan_abi_version")
@@ -50,7 +51,7 @@ class ScanArgs(ctypes.Structure):
         ("z", ctypes.c_void_p), ("delta_bias", ctypes.c_void_p), ("h0", ctypes.c_void_p),
         ("hT", ctypes.c_void_p), ("y", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_int64), ("variant", ctypes.c_int32),
-        ("time_splits", ctypes.c_int32),
+        ("time_splits", ctypes.c_int32), ("checkpoints", ctypes.c_void_p),
     ]
 
 
@@ -68,6 +69,7 @@ class ScanBwdArgs(ctypes.Structure):
         ("dz", ctypes.c_void_p), ("ddelta_bias", ctypes.c_void_p), ("dh0", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
         ("time_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("checkpoints", ctypes.c_void_p),
     ]
 
 
@@ -132,6 +134,8 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_workspace_bytes.restype = ctypes.c_int64
         L.ssm_scan_plan.argtypes = [P]
         L.ssm_scan_plan.restype = ctypes.c_int64
+        L.ssm_scan_checkpoint_bytes.argtypes = [P]
+        L.ssm_scan_checkpoint_bytes.restype = ctypes.c_int64
         PB = ctypes.POINTER(ScanBwdArgs)
         L.ssm_scan_bwd.argtypes = [PB, ctypes.c_void_p]
         L.ssm_scan_bwd.restype = ctypes.c_int
@@ -188,9 +192,10 @@ def _check(name, t, shape, dtype, device):
 
 def make_args(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, hT=None, y=None,
               workspace=None, variant="auto", time_splits=0, generic_a=False, zoh=False,
-              carry_scan=False) -> ScanArgs:
+              carry_scan=False, checkpoints=None) -> ScanArgs:
     """Check shapes/dtypes/devices of torch tensors and fill an ssm_scan_args
-    (zoh: zero-order-hold input term instead of the Euler one)."""
+    (zoh: zero-order-hold input term instead of the Euler one; checkpoints: a
+    float32 tensor of checkpoint_shape(...) for the backward, or None)."""
     if x.dim() != 3:
         raise ValueError("x must be (B, L, D)")
     bsz, L, dim = x.shape
@@ -213,6 +218,7 @@ def make_args(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, hT=No
     _check("h0", h0, (bsz, dim, N), f32, dev)
     _check("hT", hT, (bsz, dim, N), f32, dev)
     _check("y", y, (bsz, L, dim), io, dev)
+    _check("checkpoints", checkpoints, checkpoint_shape(bsz, L, dim, N), f32, dev)
     if variant not in VARIANTS:
         raise ValueError(f"variant must be one of {sorted(VARIANTS)}")
     a = ScanArgs()
@@ -225,7 +231,27 @@ def make_args(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, hT=No
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.variant = VARIANTS[variant]
     a.time_splits = int(time_splits)
+    a.checkpoints = _ptr(checkpoints)
     return a
+
+
+def checkpoint_tokens(dstate: int) -> int:
+    """Tokens between the checkpoints a forward writes for the backward."""
+    return 16 if dstate <= 4 else 8
+
+
+def checkpoint_shape(batch: int, seqlen: int, dim: int, dstate: int):
+    """Shape of the checkpoints of one call: (B, ceil(L / T) - 1, 4, D, M),
+    M = ceil(N / 4); entry i is the state after token (i + 1) T - 1, state n
+    of channel d at [.., i, n // M, d, n % M]."""
+    T = checkpoint_tokens(dstate)
+    return (batch, max((seqlen + T - 1) // T - 1, 0), 4, dim, (dstate + 3) // 4)
+
+
+def checkpoint_states(ck, dstate: int):
+    """The states of checkpoints `ck` as a (B, entries, D, N) tensor."""
+    b, e, _, dim, m = ck.shape
+    return ck.permute(0, 1, 3, 2, 4).reshape(b, e, dim, 4 * m)[..., :dstate]
 
 
 def plan(args: ScanArgs):
@@ -245,14 +271,16 @@ def workspace_bytes(args: ScanArgs) -> int:
 
 def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
              return_final_state=False, out=None, final_state_out=None, workspace=None,
-             variant="auto", time_splits=0, generic_a=False, zoh=False, carry_scan=False):
+             variant="auto", time_splits=0, generic_a=False, zoh=False, carry_scan=False, checkpoints=None):
     """Selective scan forward on the GPU.  Returns y, or (y, hT) with
     return_final_state=True.  `final_state_out` may be h0 itself (in-place state
     update).  zoh=True discretises the input term with the zero-order hold,
     (exp(delta A) - 1) / A * B x, instead of delta B x.  carry_scan=True makes a
     time-split call compose the segment summaries with the wave-level
-    associative scan launch instead of folding them serially in each block.  Launches on torch's
-    current HIP stream and does not synchronise."""
+    associative scan launch instead of folding them serially in each block.
+    `checkpoints` (a float32 tensor of checkpoint_shape(...)) receives the
+    states the backward can start from (scan_bwd(..., checkpoints=...)).
+    Launches on torch's current HIP stream and does not synchronise."""
     if not x.is_cuda:
         raise ValueError("scan_fwd runs on the GPU only: move the tensors to a HIP device")
     L_ = lib()
@@ -261,7 +289,7 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
     if hT is None and return_final_state:
         hT = torch.empty((x.shape[0], x.shape[2], A.shape[1]), dtype=torch.float32, device=x.device)
     args = make_args(x, delta, A, B, C, D, z, delta_bias, h0, hT, y, None, variant, time_splits, generic_a, zoh,
-                     carry_scan)
+                     carry_scan, checkpoints)
     if workspace is None:
         nbytes = L_.ssm_scan_workspace_bytes(ctypes.byref(args))
         if nbytes < 0:
@@ -281,10 +309,11 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
 
 
 def make_bwd_args(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *, dy, dhT=None,
-                  grads=None, workspace=None, time_splits=0, generic_a=False, zoh=False) -> ScanBwdArgs:
+                  grads=None, workspace=None, time_splits=0, generic_a=False, zoh=False,
+                  checkpoints=None) -> ScanBwdArgs:
     """Check shapes/dtypes/devices and fill an ssm_scan_bwd_args.  `grads` maps
     input names (x, delta, A, B, C, D, z, delta_bias, h0) to output tensors."""
-    fa = make_args(x, delta, A, B, C, D, z, delta_bias, h0, generic_a=generic_a, zoh=zoh)
+    fa = make_args(x, delta, A, B, C, D, z, delta_bias, h0, generic_a=generic_a, zoh=zoh, checkpoints=checkpoints)
     bsz, L, dim = x.shape
     N = A.shape[1]
     io, dev, f32 = x.dtype, x.device, torch.float32
@@ -297,6 +326,7 @@ def make_bwd_args(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *
     a = ScanBwdArgs()
     for f, _ in ScanArgs._fields_:
         if f in dict(ScanBwdArgs._fields_) and f not in ("workspace", "workspace_bytes", "time_splits"):
+            # (checkpoints: the forward's, passed through as an input here)
             setattr(a, f, getattr(fa, f))
     a.dy, a.dhT = _ptr(dy), _ptr(dhT)
     for k, t in grads.items():
@@ -327,11 +357,13 @@ def bwd_plan(args: ScanBwdArgs) -> int:
 
 
 def scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *, dy, dhT=None,
-             wanted=None, workspace=None, time_splits=0, generic_a=False, zoh=False):
+             wanted=None, workspace=None, time_splits=0, generic_a=False, zoh=False, checkpoints=None):
     """Backward selective scan on the GPU: gradients of sum(dy * y) + sum(dhT * hT)
     with respect to the inputs, as a dict keyed like the inputs (x, delta, A, B,
     C, h0 always; D, z, delta_bias when given).  `wanted` restricts the outputs
-    to those names; zoh=True differentiates the zero-order-hold forward.  Launches on torch's current HIP stream and does not
+    to those names; zoh=True differentiates the zero-order-hold forward;
+    `checkpoints` are those a scan_fwd call on the same inputs wrote (the
+    forward recurrence is then not run again).  Launches on torch's current HIP stream and does not
     synchronise."""
     if not x.is_cuda:
         raise ValueError("scan_bwd runs on the GPU only: move the tensors to a HIP device")
@@ -349,7 +381,7 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *, dy,
         else:
             grads[k] = torch.empty_like(given[k])
     args = make_bwd_args(x, delta, A, B, C, D, z, delta_bias, h0, dy=dy, dhT=dhT, grads=grads,
-                         time_splits=time_splits, generic_a=generic_a, zoh=zoh)
+                         time_splits=time_splits, generic_a=generic_a, zoh=zoh, checkpoints=checkpoints)
     if workspace is None:
         nbytes = L_.ssm_scan_bwd_workspace_bytes(ctypes.byref(args))
         if nbytes < 0:
@@ -560,4 +592,4 @@ def gla_fwd(q, k, v, log_f=None, in_gate=None, h0=None, *, feature_map=False, re
 
 
 __all__ = ["scan_fwd", "scan_bwd", "conv1d_silu", "ssd_fwd", "gla_fwd", "make_gla_args", "GlaArgs", "gla_workspace_bytes", "gla_plan", "make_ssd_args", "SsdArgs", "ssd_workspace_bytes", "ssd_plan", "make_conv_args", "ConvArgs", "make_args", "make_bwd_args", "plan", "bwd_plan", "workspace_bytes",
-           "bwd_workspace_bytes", "lib", "strerror", "ScanArgs", "ScanBwdArgs", "EXPORTS"]
+           "bwd_workspace_bytes", "checkpoint_shape", "checkpoint_states", "checkpoint_tokens", "lib", "strerror", "ScanArgs", "ScanBwdArgs", "EXPORTS"]

@@ -64,6 +64,19 @@ struct Plan {
 
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
+// Bytes of the forward's checkpoints for the backward: (B, ceil(L / T) - 1, 4,
+// D, ceil(N / 4)) fp32 with T = ssm::ckpt_tokens(N); -1 when the count
+// overflows.
+int64_t ckpt_bytes(int64_t B, int64_t L, int64_t D, int64_t N) {
+  const int64_t T = ssm::ckpt_tokens(N);
+  const int64_t entries = L > 0 ? (L + T - 1) / T - 1 : 0;
+  int64_t v;
+  if (!mul_ok(B, entries, &v) || !mul_ok(v, 4 * ssm::ckpt_quarter(N), &v) || !mul_ok(v, D, &v) ||
+      !mul_ok(v, 4, &v))
+    return -1;
+  return v;
+}
+
 // Element counts and the checks that need no device access.
 int validate(const ssm_scan_args* a, int64_t* n_bld, int64_t* n_bln, int64_t* n_bdn) {
   if (!a) return SSM_ERR_NULL;
@@ -88,9 +101,12 @@ int validate(const ssm_scan_args* a, int64_t* n_bld, int64_t* n_bln, int64_t* n_
   if (empty) return SSM_OK;  // nothing will be read or written
   const bool has_tokens = bld > 0;
   if (has_tokens && (!a->x || !a->delta || !a->A || !a->B || !a->C || !a->y)) return SSM_ERR_NULL;
-  const void* ptrs[] = {a->x, a->delta, a->A, a->B, a->C, a->D, a->z, a->delta_bias, a->h0, a->hT, a->y, a->workspace};
+  const void* ptrs[] = {a->x, a->delta, a->A, a->B, a->C, a->D, a->z, a->delta_bias, a->h0, a->hT, a->y, a->workspace,
+                        a->checkpoints};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SSM_ERR_ALIGN;
+  const int64_t ckb = ckpt_bytes(a->batch, a->seqlen, a->dim, a->dstate);
+  if (ckb < 0) return SSM_ERR_SHAPE;
   // Aliasing: y must not touch any input; hT may coincide with h0 exactly but
   // must not touch any other input, nor y.
   const int64_t xb = bld * es, nb = bln * es, sb = bdn * 4, db = a->dim * 4, ab = dn * 4;
@@ -106,6 +122,12 @@ int validate(const ssm_scan_args* a, int64_t* n_bld, int64_t* n_bln, int64_t* n_
     for (int i = 0; i < 8; ++i)
       if (overlaps(a->hT, sb, ins[i], insz[i])) return SSM_ERR_ALIAS;
     if (a->h0 && a->h0 != a->hT && overlaps(a->hT, sb, a->h0, sb)) return SSM_ERR_ALIAS;
+  }
+  if (a->checkpoints && ckb > 0) {  // an output: touches no input and no other output
+    const void* others[] = {a->x, a->delta, a->B, a->C, a->z, a->A, a->D, a->delta_bias, a->h0, a->hT, a->y};
+    const int64_t osz[] = {xb, xb, nb, nb, xb, ab, db, db, sb, sb, xb};
+    for (int i = 0; i < 11; ++i)
+      if (overlaps(a->checkpoints, ckb, others[i], osz[i])) return SSM_ERR_ALIAS;
   }
   return SSM_OK;
 }
@@ -212,17 +234,20 @@ int validate_bwd(const ssm_scan_bwd_args* a) {
   if (a->dz && !a->z) return SSM_ERR_NULL;
   const void* ptrs[] = {a->x,  a->delta, a->A,  a->B,      a->C,  a->D,  a->z,           a->delta_bias,
                         a->h0, a->dy,    a->dhT, a->dx,    a->ddelta, a->dA, a->dB,      a->dC,
-                        a->dD, a->dz,    a->ddelta_bias,   a->dh0, a->workspace};
+                        a->dD, a->dz,    a->ddelta_bias,   a->dh0, a->workspace, a->checkpoints};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SSM_ERR_ALIGN;
+  const int64_t ckb = ckpt_bytes(a->batch, a->seqlen, a->dim, a->dstate);
+  if (ckb < 0) return SSM_ERR_SHAPE;
   const int64_t es = a->dtype == SSM_DTYPE_F32 ? 4 : 2;
   const int64_t xb = bld * es, nb = bln * es, sb = bdn * 4, db = a->dim * 4, ab = dn * 4;
-  const void* ins[] = {a->x, a->delta, a->A, a->B, a->C, a->D, a->z, a->delta_bias, a->h0, a->dy, a->dhT};
-  const int64_t insz[] = {xb, xb, ab, nb, nb, db, xb, db, sb, xb, sb};
+  const void* ins[] = {a->x, a->delta, a->A, a->B, a->C, a->D, a->z, a->delta_bias, a->h0, a->dy, a->dhT,
+                       a->checkpoints};
+  const int64_t insz[] = {xb, xb, ab, nb, nb, db, xb, db, sb, xb, sb, ckb};
   const void* outs[] = {a->dx, a->ddelta, a->dA, a->dB, a->dC, a->dD, a->dz, a->ddelta_bias, a->dh0};
   const int64_t outsz[] = {xb, xb, ab, nb, nb, db, xb, db, sb};
   for (int i = 0; i < 9; ++i) {
-    for (int j = 0; j < 11; ++j)
+    for (int j = 0; j < 12; ++j)
       if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return SSM_ERR_ALIAS;
     for (int j = 0; j < i; ++j)
       if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return SSM_ERR_ALIAS;
@@ -269,9 +294,12 @@ int make_bwd_plan(const ssm_scan_bwd_args* a, BwdPlan* pl) {
     off += round_up(floats * 4, 256);
     return o;
   };
-  pl->off_ck = take(B * pl->nck * D * N);
-  pl->off_ckds = take(B * pl->nck * D);
-  pl->off_segh = take(B * S * D * N);
+  // with the forward's checkpoints the local pass writes none of its own, and
+  // the states entering segments are not combined
+  const bool own_ck = a->checkpoints == nullptr;
+  pl->off_ck = take(own_ck ? B * pl->nck * D * N : 0);
+  pl->off_ckds = take(own_ck ? B * pl->nck * D : 0);
+  pl->off_segh = take(own_ck ? B * S * D * N : 0);
   pl->off_segc = take(B * S * D * N);
   pl->off_segds = take(B * S * D);
   pl->off_pA = take(B * S * D * N);
@@ -527,6 +555,7 @@ int run_fwd(const ssm_scan_args* a, const Plan& pl, void* ws, void* stream) {
   p.windowed = pl.variant == SSM_VARIANT_NSPLIT && nsplit_windowed(a);
   p.ws_state = pl.splits > 1 ? static_cast<float*>(ws) : nullptr;
   p.ws_dsum = pl.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + pl.ws_state_bytes) : nullptr;
+  p.checkpoints = ckpt_bytes(a->batch, a->seqlen, a->dim, a->dstate) > 0 ? a->checkpoints : nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -542,6 +571,13 @@ int run_fwd(const ssm_scan_args* a, const Plan& pl, void* ws, void* stream) {
 }
 
 }  // namespace
+
+int64_t ssm_scan_checkpoint_bytes(const ssm_scan_args* a) {
+  int64_t bld, bln, bdn;
+  const int rc = validate(a, &bld, &bln, &bdn);
+  if (rc != SSM_OK) return rc;
+  return ckpt_bytes(a->batch, a->seqlen, a->dim, a->dstate);
+}
 
 int ssm_scan_fwd(const ssm_scan_args* a, void* stream) {
   int64_t bld, bln, bdn;
@@ -655,6 +691,7 @@ int ssm_scan_bwd(const ssm_scan_bwd_args* a, void* stream) {
   p.pbias = reg(pl.off_pbias);
   p.pB = reg(pl.off_pB);
   p.pC = reg(pl.off_pC);
+  p.ck_in = a->checkpoints;
   e = ssm::launch_bwd(p, s);
   return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }

@@ -9,27 +9,31 @@ namespace ssm {
 namespace {
 
 // ---- 2. combine the segment summaries ------------------------------------------------
+// states: combine the forward summaries too (no checkpoints from the forward).
 __global__ __launch_bounds__(256) void bwd_combine_kernel(const float* __restrict__ A, const float* __restrict__ h0,
                                                           const float* __restrict__ dhT, float* __restrict__ segh,
                                                           float* __restrict__ segc, const float* __restrict__ segds,
-                                                          int64_t Bsz, int64_t D, int N, int64_t nseg) {
+                                                          int64_t Bsz, int64_t D, int N, int64_t nseg, bool states) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // (b, d, n)
   if (i >= Bsz * D * N) return;
   const int64_t dn = i % (D * N), b = i / (D * N), d = dn / N, n = dn % N;
   const float a2 = A[dn] * kLog2e;
-  float h = h0 ? h0[i] : 0.0f;
-  for (int64_t s = 0; s < nseg; ++s) {
-    const int64_t si = (b * nseg + s) * D + d;
-    const float e = segh[si * N + n];
-    segh[si * N + n] = h;
-    h = __builtin_fmaf(fast_exp2(a2 * segds[si]), h, e);
+  if (states) {
+    float h = h0 ? h0[i] : 0.0f;
+    for (int64_t s = 0; s < nseg; ++s) {
+      const int64_t si = (b * nseg + s) * D + d;
+      const float e = segh[si * N + n];
+      segh[si * N + n] = h;
+      h = __builtin_fmaf(fast_exp2(a2 * segds[si]), h, e);
+    }
   }
+  // the adjoint leaving each segment's end; segment 0's own decay is not needed
   float g = dhT ? dhT[i] : 0.0f;
   for (int64_t s = nseg - 1; s >= 0; --s) {
     const int64_t si = (b * nseg + s) * D + d;
-    const float e = s > 0 ? segc[si * N + n] : 0.0f;
+    const float e = s > 0 ? segc[si * N + n] : 0.0f;  // the segment's adjoint from zero
     segc[si * N + n] = g;
-    g = __builtin_fmaf(fast_exp2(a2 * segds[si]), g, e);
+    if (s > 0) g = __builtin_fmaf(fast_exp2(a2 * segds[si]), g, e);
   }
 }
 
@@ -82,7 +86,8 @@ namespace bwd {
 hipError_t launch_combine(const BwdProblem& p, hipStream_t stream) {
   const int64_t bdn = p.batch * p.dim * p.dstate;
   hipLaunchKernelGGL(bwd_combine_kernel, dim3(blocks256(bdn)), dim3(256), 0, stream, p.A, p.h0, p.dhT, p.segh,
-                     p.segc, p.segds, p.batch, p.dim, static_cast<int>(p.dstate), static_cast<int64_t>(p.splits));
+                     p.segc, p.segds, p.batch, p.dim, static_cast<int>(p.dstate), static_cast<int64_t>(p.splits),
+                     p.ck_in == nullptr);
   return hipGetLastError();
 }
 

@@ -43,6 +43,9 @@
 //               segments.  Kernel 3 writes per-wave and per-segment partials
 //               and kernel 4 adds them in a fixed order, so every result is
 //               independent of scheduling.
+// Given the forward's checkpoints (true states after every chunk), pass 1
+// runs only the adjoint, pass 2 only combines the adjoint, and pass 3 starts
+// each chunk from its checkpoint as it is.
 #pragma once
 
 #include "buffer_io.hpp"
@@ -213,6 +216,30 @@ __device__ __forceinline__ void load_vec(const float* row, int n0, int N, float 
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const float v = row[min(n0 + k, N - 1)];
+      o[k] = n0 + k < N ? v : 0.0f;
+    }
+  }
+}
+
+// The lane's K states n0 .. n0 + K - 1 of channel d from one checkpoint entry
+// laid out in quarters (4, D, M), M = ceil(N / 4): state n at [n / M][d][n % M].
+// Runs of 4 states that stay inside a quarter (M a multiple of 4, n0 too)
+// are one 16-byte load; otherwise state by state, missing states 0.
+template <bool FULL, int K>
+__device__ __forceinline__ void load_ckpt(const float* entry, int64_t d, int64_t D, int n0, int N, float (&o)[K]) {
+  const int M = ckpt_quarter(N);
+  if (FULL && (M & 3) == 0) {
+#pragma unroll
+    for (int k = 0; k < K; k += 4) {
+      const int n = n0 + k;
+      const float4 v = *reinterpret_cast<const float4*>(entry + ((n / M) * D + d) * M + n % M);
+      o[k] = v.x, o[k + 1] = v.y, o[k + 2] = v.z, o[k + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int n = min(n0 + k, N - 1);
+      const float v = entry[((n / M) * D + d) * M + n % M];
       o[k] = n0 + k < N ? v : 0.0f;
     }
   }
@@ -475,7 +502,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2, 4))) 
     const S* __restrict__ x, const S* __restrict__ dl, const float* __restrict__ A, const S* __restrict__ Bm,
     const S* __restrict__ Cm, const S* __restrict__ z, const float* __restrict__ bias, const S* __restrict__ dy,
     float* __restrict__ ck, float* __restrict__ ckds, float* __restrict__ segh, float* __restrict__ segc,
-    float* __restrict__ segds, int64_t L, int64_t D, int N, int64_t seg_len, int64_t nck, int64_t nseg, int flags) {
+    float* __restrict__ segds, const float* __restrict__ ck_in, int64_t L, int64_t D, int N, int64_t seg_len,
+    int64_t nck, int64_t nseg, int flags) {
   constexpr int T = bwd_chunk_len(K);
   const Chain<G> c = chain_of<K, G>(D, L, seg_len);
   const Seg<S> sg(c, x, dl, Bm, Cm, z, dy, L, D, N);
@@ -538,6 +566,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2, 4))) 
     }
   };
   const int64_t t_tail = c.t_begin + (c.t_end - c.t_begin) / T * T;  // seg_len is a multiple of T
+  const int64_t si = (c.b * nseg + c.s) * D + c.d;
   auto fwd_pass = [&](auto structs) {
     pipelined<FS>(
         c.t_begin, T, (t_tail - c.t_begin) / T, [&](FS& st, int64_t t0) { fwd_load(st, t0, Tag<false>{}); },
@@ -548,16 +577,19 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2, 4))) 
       fwd_steps(st, t_tail, Tag<true>{}, structs);
     }
   };
-  if (structured)
-    fwd_pass(Tag<true>{});
-  else
-    fwd_pass(Tag<false>{});
-  const int64_t si = (c.b * nseg + c.s) * D + c.d;
-  if (c.active) {
-    if (c.q == 0) segds[si] = ds;
-    store_states<FULL, K>(segh + si * N, c.n0, N, h);
+  const bool own_ck = ck_in == nullptr;  // else the forward's checkpoints hold the states
+  if (own_ck) {
+    if (structured)
+      fwd_pass(Tag<true>{});
+    else
+      fwd_pass(Tag<false>{});
+    if (c.active) {
+      if (c.q == 0) segds[si] = ds;
+      store_states<FULL, K>(segh + si * N, c.n0, N, h);
+    }
   }
   if (nseg == 1 || c.s == 0) return;  // the adjoint entering segment 0 from the left is never needed
+  ds = 0.0f;  // the adjoint pass sums delta again (the combine's decay over the segment)
   float g[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) g[k] = 0.0f;
@@ -583,6 +615,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2, 4))) 
     for (int j = T - 1; j >= 0; --j) {
       if (!RAGGED || t0 + j < c.t_end) {
         const float dt = softplus_f32(bits_to_f32<S>(st.dl[j]) + bs);
+        ds += dt;
         float gy0 = bits_to_f32<S>(st.dy[j]);
         if constexpr (GATE) gy0 *= silu_f32(bits_to_f32<S>(st.z[j]));
         float Cv[K], an[K];
@@ -607,7 +640,10 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2, 4))) 
     rev_pass(Tag<true>{});
   else
     rev_pass(Tag<false>{});
-  if (c.active) store_states<FULL, K>(segc + si * N, c.n0, N, g);
+  if (c.active) {
+    store_states<FULL, K>(segc + si * N, c.n0, N, g);
+    if (!own_ck && c.q == 0) segds[si] = ds;
+  }
 }
 
 // ---- 3. the adjoint walk ------------------------------------------------------------------
@@ -617,9 +653,10 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(FULL ? 2
     const S* __restrict__ Cm, const float* __restrict__ Dsk, const S* __restrict__ z,
     const float* __restrict__ bias, const S* __restrict__ dy, const float* __restrict__ ck,
     const float* __restrict__ ckds, const float* __restrict__ segh, const float* __restrict__ segc,
-    S* __restrict__ gx, S* __restrict__ gdl, S* __restrict__ gz, float* __restrict__ gh0, float* __restrict__ pB,
-    float* __restrict__ pC, float* __restrict__ pA, float* __restrict__ pD, float* __restrict__ pbias, int64_t L,
-    int64_t D, int N, int64_t seg_len, int64_t nck, int64_t nseg, int flags) {
+    const float* __restrict__ ck_in, const float* __restrict__ h0, S* __restrict__ gx, S* __restrict__ gdl,
+    S* __restrict__ gz, float* __restrict__ gh0, float* __restrict__ pB, float* __restrict__ pC,
+    float* __restrict__ pA, float* __restrict__ pD, float* __restrict__ pbias, int64_t L, int64_t D, int N,
+    int64_t seg_len, int64_t nck, int64_t nseg, int flags) {
   constexpr int T = bwd_chunk_len(K);
   constexpr int LGK = log2i<K>();
   const Chain<G> c = chain_of<K, G>(D, L, seg_len);
@@ -643,7 +680,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(FULL ? 2
   float iA[ZOH ? K : 1];              // 1 / A_n for the hold's coefficient
   load_vec<FULL, K>(A + c.d * N, c.n0, N, A2);
   load_vec<FULL, K>(segc + si * N, c.n0, N, g);
-  load_vec<FULL, K>(segh + si * N, c.n0, N, hin);
+  if (ck_in == nullptr) load_vec<FULL, K>(segh + si * N, c.n0, N, hin);
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     if constexpr (ZOH) iA[k] = 1.0f / A2[k];
@@ -700,7 +737,16 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(FULL ? 2
     // dts: softplus of the chunk's raw steps
     // dts: softplus of the chunk's raw steps; lsg: v - softplus(v); xv: x
     float hs[T + 1][K], dts[T], lsg[T], xv[T];
-    {
+    if (ck_in) {  // the forward's state entering the chunk (h0 for the first)
+      if (cc > 0) {
+        load_ckpt<FULL, K>(ck_in + (c.b * (nck - 1) + cc - 1) * 4 * D * ckpt_quarter(N), c.d, D, c.n0, N, hs[0]);
+      } else if (h0) {
+        load_vec<FULL, K>(h0 + (c.b * D + c.d) * N, c.n0, N, hs[0]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) hs[0][k] = 0.0f;
+      }
+    } else {
       const int64_t ci = (c.b * nck + cc) * D + c.d;
       const float ds0 = ckds[ci];
       load_vec<FULL, K>(ck + ci * N, c.n0, N, hs[0]);
@@ -855,14 +901,14 @@ hipError_t launch_bwd_t(const BwdProblem& p, hipStream_t stream) {
   const auto* z = static_cast<const S*>(p.z);
   const auto* dy = static_cast<const S*>(p.dy);
   hipLaunchKernelGGL((bwd_local_kernel<S, K, G, FULL, GATE, ZOH>), grid, block, 0, stream, x, dl, p.A, Bm, Cm, z, p.delta_bias,
-                     dy, p.ck, p.ckds, p.segh, p.segc, p.segds, p.seqlen, p.dim, N, p.seg_len, p.nck,
+                     dy, p.ck, p.ckds, p.segh, p.segc, p.segds, p.ck_in, p.seqlen, p.dim, N, p.seg_len, p.nck,
                      static_cast<int64_t>(p.splits), p.flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = bwd::launch_combine(p, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_main_kernel<S, K, G, FULL, GATE, ZOH>), grid, block, 0, stream, x, dl, p.A, Bm, Cm, p.D, z,
-                     p.delta_bias, dy, p.ck, p.ckds, p.segh, p.segc, static_cast<S*>(p.dx),
+                     p.delta_bias, dy, p.ck, p.ckds, p.segh, p.segc, p.ck_in, p.h0, static_cast<S*>(p.dx),
                      static_cast<S*>(p.ddelta), static_cast<S*>(p.dz), p.dh0, p.pB, p.pC, p.pA, p.pD, p.pbias,
                      p.seqlen, p.dim, N, p.seg_len, p.nck, static_cast<int64_t>(p.splits), p.flags);
   e = hipGetLastError();

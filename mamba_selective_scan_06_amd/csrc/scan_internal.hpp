@@ -28,6 +28,9 @@ struct Problem {
   float* ws_state;   // (B, splits, D, N) segment end states from a zero start
   float* ws_dsum;    // (B, splits, D) sum of softplus(delta) over each segment
   bool windowed;     // a row of x or B spans 2 GiB or more: move the descriptors along it
+  // (B, ceil(L / T) - 1, 4, D, ceil(N / 4)): the state after every T-th token
+  // (T = ckpt_tokens(N)) for the backward, or nullptr
+  float* checkpoints = nullptr;
 };
 
 constexpr int kFlagGenericA = 1;
@@ -71,6 +74,11 @@ constexpr int bwd_lanes_per_channel(int64_t dstate) {
 // Tokens per checkpoint chunk: the chunk's recomputed states live in
 // registers, (T + 1) * K of them per lane.
 constexpr int bwd_chunk_len(int64_t dstate) { return bwd_lane_states(dstate) == 4 ? 16 : 8; }
+// Spacing of the checkpoints a forward writes for the backward: its chunk.
+constexpr int ckpt_tokens(int64_t dstate) { return bwd_chunk_len(dstate); }
+// States per quarter of a checkpoint entry, laid out (4, D, M): state n of
+// channel d at [n / M][d][n % M].
+constexpr int ckpt_quarter(int64_t dstate) { return static_cast<int>((dstate + 3) / 4); }
 
 struct BwdProblem {
   int64_t batch, seqlen, dim, dstate;
@@ -111,6 +119,11 @@ struct BwdProblem {
   float* pbias;  // (B, S, D) partial d delta_bias
   float* pB;     // (B, L, nblk, N) partial dB, one row per wave (64 / G channels)
   float* pC;     // (B, L, nblk, N) partial dC
+  // The forward's checkpoints ((B, nck - 1, 4, D, ceil(N / 4)), true states
+  // after every chunk but the last), or nullptr.  With them the local pass skips the
+  // forward recurrence, the combine its forward half, and ck, ckds and segh
+  // are not used.
+  const float* ck_in = nullptr;
 };
 
 hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream);

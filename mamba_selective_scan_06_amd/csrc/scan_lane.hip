@@ -20,7 +20,7 @@ __global__ __launch_bounds__(64) void scan_lane_kernel(
     const S* __restrict__ x, const S* __restrict__ dl, const float* __restrict__ A,
     const S* __restrict__ Bm, const S* __restrict__ Cm, const float* __restrict__ Dsk,
     const S* __restrict__ z, const float* __restrict__ bias, const float* h0, float* hT,
-    S* __restrict__ y, int64_t L, int64_t D, int N) {
+    S* __restrict__ y, float* __restrict__ ck, int64_t L, int64_t D, int N) {
   const int64_t b = blockIdx.y;
   const int64_t d0 = static_cast<int64_t>(blockIdx.x) * 64;
   const int lane = threadIdx.x;
@@ -64,6 +64,15 @@ __global__ __launch_bounds__(64) void scan_lane_kernel(
     if (has_d) acc = __builtin_fmaf(Dd, xv, acc);
     if (has_z) acc *= silu_f32(to_f32(z[row + lo]));
     if (active) store_elem(y + row + lane, acc);
+    // the backward's checkpoint after every T-th token but the last chunk's
+    const int64_t T = ckpt_tokens(N);
+    if (ck && (t + 1) % T == 0 && t + 1 < L && active) {  // quarters (4, D, M): [n / M][d][n % M]
+      const int M = ckpt_quarter(N);
+      float* dst = ck + ((b * ((L + T - 1) / T - 1) + (t + 1) / T - 1) * 4 * D + d) * M;
+#pragma unroll
+      for (int n = 0; n < NMAX; ++n)
+        if (n < N) dst[(n / M) * D * M + n % M] = h[n];
+    }
   }
   if (hT && active) {
 #pragma unroll
@@ -79,7 +88,7 @@ hipError_t launch_lane_z(const Problem& p, hipStream_t stream) {
                      static_cast<const S*>(p.x), static_cast<const S*>(p.delta), p.A,
                      static_cast<const S*>(p.B), static_cast<const S*>(p.C), p.D,
                      static_cast<const S*>(p.z), p.delta_bias, p.h0, p.hT, static_cast<S*>(p.y),
-                     p.seqlen, p.dim, static_cast<int>(p.dstate));
+                     p.checkpoints, p.seqlen, p.dim, static_cast<int>(p.dstate));
   return hipGetLastError();
 }
 

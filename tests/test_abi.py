@@ -38,7 +38,7 @@ def test_library_loads_and_exports_header_symbols():
     assert set(declared) == set(ssm.EXPORTS), declared
     for name in declared:
         assert hasattr(L, name), f"{name} not exported"
-    assert L.ssm_scan_abi_version() == ssm.ABI_VERSION == 3
+    assert L.ssm_scan_abi_version() == ssm.ABI_VERSION == 4
 
 
 def test_strerror_covers_codes():
@@ -186,3 +186,30 @@ def test_zoh_flag_accepted():
     for f in (2, 3, 4, 7):  # SSM_FLAG_CARRY_SCAN (4) as well
         assert _fwd(_args(shape=(0, 8, 8, 16), flags=f)) == 0
         assert ssm.lib().ssm_scan_plan(ctypes.byref(_args(flags=f))) >= 0
+
+
+def _ck_bytes(a):
+    return ssm.lib().ssm_scan_checkpoint_bytes(ctypes.byref(a))
+
+
+def test_checkpoint_bytes_query():
+    """(B, ceil(L / T) - 1, 4, D, ceil(N / 4)) fp32, T = 8 tokens (16 when N <= 4)."""
+    assert _ck_bytes(_args(shape=(2, 64, 128, 16))) == 2 * 7 * 128 * 16 * 4
+    assert _ck_bytes(_args(shape=(2, 65, 128, 16))) == 2 * 8 * 128 * 16 * 4
+    assert _ck_bytes(_args(shape=(1, 64, 8, 4))) == 1 * 3 * 8 * 4 * 4     # T = 16
+    assert _ck_bytes(_args(shape=(1, 8, 8, 16))) == 0                     # one chunk: nothing to keep
+    assert _ck_bytes(_args(shape=(1, 0, 8, 16))) == 0
+    assert _ck_bytes(_args(shape=(1, 1, 8, 16))) == 0
+    assert ssm.checkpoint_shape(2, 65, 128, 16) == (2, 8, 4, 128, 4)
+    assert ssm.checkpoint_shape(1, 64, 8, 4) == (1, 3, 4, 8, 1)
+    assert ssm.checkpoint_shape(1, 64, 8, 5) == (1, 7, 4, 8, 2)           # quarters of 2, three slots unused
+    assert _ck_bytes(_args(shape=(1, 64, 8, 5))) == 7 * 4 * 8 * 2 * 4
+    assert _ck_bytes(_args(shape=(1, 64, 8, 65))) == -3
+
+
+def test_checkpoints_checked_on_host():
+    far = FAKE + (40 << 32)
+    assert _fwd(_args(checkpoints=far + 4)) == -5                      # misaligned
+    assert _fwd(_args(checkpoints=FAKE)) == -6                         # over x
+    assert _fwd(_args(checkpoints=FAKE + (10 << 32) - 64)) == -6       # runs into y
+    assert _fwd(_args(checkpoints=FAKE + (9 << 32))) == -6             # over hT

@@ -112,3 +112,19 @@ def test_zero_order_hold_passes_host_checks():
         assert _bwd(_args(flags=flags, workspace=0)) == -7
         assert ssm.lib().ssm_scan_bwd_plan(ctypes.byref(_args(flags=flags))) >= 1
         assert ssm.lib().ssm_scan_bwd_workspace_bytes(ctypes.byref(_args(flags=flags))) > 0
+
+
+def test_checkpoints_shrink_the_workspace_and_are_checked():
+    """With the forward's checkpoints the backward keeps none of its own
+    (nor the segment states), so it asks for less workspace; the checkpoints
+    are an input for the alias checks."""
+    far = FAKE + (40 << 32)
+    ws = ssm.lib().ssm_scan_bwd_workspace_bytes
+    plain = ws(ctypes.byref(_args()))
+    with_ck = ws(ctypes.byref(_args(checkpoints=far)))
+    B, L, D, N = 2, 64, 128, 16
+    S = ssm.lib().ssm_scan_bwd_plan(ctypes.byref(_args()))
+    up = lambda n: (n + 255) // 256 * 256
+    assert plain - with_ck == up(B * (L // 8) * D * N * 4) + up(B * (L // 8) * D * 4) + up(B * S * D * N * 4)
+    assert _bwd(_args(checkpoints=far + 4)) == -5
+    assert _bwd(_args(checkpoints=FAKE + (11 << 32))) == -6   # under dx
