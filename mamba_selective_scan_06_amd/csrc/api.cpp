@@ -266,9 +266,14 @@ int make_bwd_plan(const ssm_scan_bwd_args* a, BwdPlan* pl) {
     // Split until there are 4096 waves (4 per SIMD), keeping segments at least
     // 64 tokens long.  The split's extra cost, an adjoint-only pass, does not
     // grow with the number of segments.
+    // From the forward's checkpoints the local pass is the adjoint alone,
+    // latency-bound at 84 VGPRs: it gains from more waves (measured at B4
+    // L8192 D4096 on one box: 32 segments 2.523 ms, 16 segments 2.549, 8
+    // segments 2.611 on another, 4 segments 2.679).
     const int64_t waves = nblk * a->batch;
+    const int64_t target = a->checkpoints ? 16384 : 4096;
     S = 1;
-    while (waves * S < 4096 && L / (2 * S) >= 64 && S < 1024) S *= 2;
+    while (waves * S < target && L / (2 * S) >= 64 && S < 1024) S *= 2;
   }
   if (S > L) S = L;
   int64_t seg_len = round_up((L + S - 1) / S, T);
@@ -360,8 +365,9 @@ int validate_ssd(const ssm_ssd_args* a, bool check_workspace = true) {
 struct SsdPlan {
   int splits = 1;
   int64_t seg_chunks = 0;
-  int64_t ws_state = 0;  // (B, S-1, H, P, N) fp32, rounded up to 256 bytes
-  int64_t ws_la = 0;     // (B, S-1, H) fp32, rounded up to 256 bytes
+  int64_t sub_chunks = 0;  // chunks per state-only sub-segment, a divisor of seg_chunks
+  int64_t ws_state = 0;    // (B, R, H, P, N) fp32, R = (S-1) seg_chunks / sub_chunks, rounded up to 256 bytes
+  int64_t ws_la = 0;       // (B, R, H) fp32, rounded up to 256 bytes
   int64_t bytes() const { return ws_state + ws_la; }
 };
 
@@ -370,7 +376,10 @@ struct SsdPlan {
 // pass over all but the last segment; it pays while every segment's workgroup
 // still finds a compute unit of its own, so the automatic choice takes the most
 // segments for which B H S fits the 256 compute units, with at least 4 chunks
-// per segment and at most 64 segments.
+// per segment and at most 64 segments.  The state-only pass needs under half
+// the LDS, so two of its workgroups fit a compute unit: each segment before the
+// last is cut into m sub-segments, the most for which (S - 1) m B H fits 512
+// workgroups with m dividing the segment's chunks and at least 4 chunks each.
 int ssd_plan(int64_t B, int64_t L, int64_t H, int64_t N, int32_t time_splits, SsdPlan* pl) {
   constexpr int64_t kComputeUnits = 256;
   const int64_t nch = (L + 63) / 64;
@@ -391,10 +400,14 @@ int ssd_plan(int64_t B, int64_t L, int64_t H, int64_t N, int32_t time_splits, Ss
   const int64_t segc = (nch + S - 1) / S;
   S = (nch + segc - 1) / segc;  // no empty segment
   if (S < 2) return SSM_OK;
+  int64_t m = 1;
+  for (int64_t c = 2; c <= segc / 4 && c <= 2 * kComputeUnits; ++c)  // (bounds the products below)
+    if (segc % c == 0 && (S - 1) * c * B * H <= 2 * kComputeUnits) m = c;
   int64_t bs, st, tmp;
-  if (!mul_ok(B, S - 1, &bs) || !mul_ok(bs, H, &tmp) || !mul_ok(tmp, 64 * N * 4, &st)) return SSM_ERR_SHAPE;
+  if (!mul_ok(B, (S - 1) * m, &bs) || !mul_ok(bs, H, &tmp) || !mul_ok(tmp, 64 * N * 4, &st)) return SSM_ERR_SHAPE;
   pl->splits = static_cast<int>(S);
   pl->seg_chunks = segc;
+  pl->sub_chunks = segc / m;
   pl->ws_state = round_up(st, 256);
   pl->ws_la = round_up(tmp * 4, 256);
   return SSM_OK;
@@ -722,6 +735,7 @@ namespace {
 void set_segments(ssm::SsdProblem* p, const SsdPlan& pl, void* ws) {
   p->splits = pl.splits;
   p->seg_chunks = pl.seg_chunks;
+  p->sub_chunks = pl.sub_chunks;
   if (pl.splits > 1) {
     p->ws_state = static_cast<float*>(ws);
     p->ws_la = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.ws_state);

@@ -45,10 +45,12 @@ __global__ __launch_bounds__(256) void bwd_reduce_d_kernel(const float* __restri
   if (i >= D * N) return;
   const int64_t d = i / N;
   float sa = 0.0f;
-  for (int64_t r = 0; r < rows; ++r) sa += pA[r * D * N + i];  // r = (b, s)
+#pragma unroll 8
+  for (int64_t r = 0; r < rows; ++r) sa += pA[r * D * N + i];  // r = (b, s), loads in flight eight at a time
   if (gA) gA[i] = sa;
   if (i % N == 0) {
     float sd = 0.0f, sbias = 0.0f;
+#pragma unroll 8
     for (int64_t r = 0; r < rows; ++r) {
       sd += pD[r * D + d];
       sbias += pbias[r * D + d];

@@ -177,10 +177,13 @@ struct SsdProblem {
   float* hT;
   void* y;
   // time segments: splits > 1 runs a state-only pass over the first splits - 1
-  // segments of seg_chunks 64-token chunks into ws_state (B, splits-1, H, P, N)
-  // and ws_la (B, splits-1, H), then the full pass
+  // segments of seg_chunks 64-token chunks, cut into sub-segments of
+  // sub_chunks (a divisor of seg_chunks), into ws_state (B, R, H, P, N) and
+  // ws_la (B, R, H) with R = (splits - 1) seg_chunks / sub_chunks, then the
+  // full pass
   int splits = 1;
   int64_t seg_chunks = 0;
+  int64_t sub_chunks = 0;
   float* ws_state = nullptr;
   float* ws_la = nullptr;
 };

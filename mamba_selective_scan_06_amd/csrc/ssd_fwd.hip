@@ -44,13 +44,16 @@
 // the state unchanged.
 //
 // Time segments (when B H workgroups leave most compute units idle): segment s
-// owns the chunks [s SC, (s + 1) SC).  The state recurrence over a segment is
-// affine in the state entering it, S_out = exp(la) S_in + S_seg, with la the
-// sum of the segment's log decays and S_seg its end state from zero.  A
-// state-only launch (no M, no C H^T, no y: per chunk only the scalars, B^T,
-// x o w and the state update) writes S_seg and la for every segment but the
-// last; the full launch starts segment s from h0 and folds the summaries of
-// segments 0 .. s-1 into it in order, then runs the chunks as above.
+// owns the chunks [s SC, (s + 1) SC).  The state recurrence over a run of
+// chunks is affine in the state entering it, S_out = exp(la) S_in + S_run,
+// with la the sum of the run's log decays and S_run its end state from zero.
+// A state-only launch (no M, no C H^T, no y: per chunk only the scalars, B^T,
+// x o w and the state update) writes S_run and la for the sub-segments of SC
+// / m chunks that cover every segment but the last; it needs under half the
+// full kernel's LDS, so two of its workgroups share a compute unit, and the
+// planner picks m to fill them.  The full launch starts segment s from h0 and
+// folds the summaries of sub-segments 0 .. s m - 1 into it in order, then runs
+// the chunks as above.
 #include <type_traits>
 
 #include "buffer_io.hpp"
@@ -141,6 +144,17 @@ struct alignas(16) SsdSmem {
   float4 xch[NW > 4 ? NW : 1][2][64];  // halves of C H^T handed to the slice's other wave
 };
 
+// The state-only pass's part of it (same names, same layouts).
+template <int N, int NW>
+struct alignas(16) SsdSmemState {
+  static constexpr int NB = kSsdStageBufs<N>;
+  uint16_t xw[2][kQ / 8][kP][8];
+  uint16_t bt[NB][N][kQ + kPad];
+  float dl[NB][kQ];
+  float cs[NB][kQ];
+  float ww[NB][kQ];
+};
+
 struct KArgs {
   const uint16_t* x;
   const uint16_t* dt;
@@ -154,11 +168,13 @@ struct KArgs {
   const float* h0;
   float* hT;
   uint16_t* y;
-  float* ws_state;   // (B, S-1, H, P, N) end state of each segment but the last, from zero
-  float* ws_la;      // (B, S-1, H) sum of the log decays over each of those segments
+  float* ws_state;   // (B, R, H, P, N) end state of each state-only sub-segment, from zero
+  float* ws_la;      // (B, R, H) sum of the log decays over each of them
   int64_t L;
   int64_t seg_chunks;  // chunks per segment (all of them when S = 1)
+  int64_t sub_chunks;  // chunks per state-only sub-segment (seg_chunks / m)
   int H, G, S;
+  int R;               // state-only sub-segments: (S - 1) m
 };
 
 // ST: the state-only pass of a time-split call (see the top of the file).
@@ -171,7 +187,7 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
   constexpr int NMK = N / 32 / NK;    // 32-wide k steps over the wave's n part
   constexpr int NJK = N / 16 / NK;    // 16-row state tiles per wave
   static_assert(TPT >= 1 && NMK >= 1, "unsupported state size for this wave count");
-  __shared__ SsdSmem<N, NW> sm;
+  __shared__ std::conditional_t<ST, SsdSmemState<N, NW>, SsdSmem<N, NW>> sm;
   const int tid = threadIdx.x, lane = tid & 63, wi = wave_id();
   const int w = wi & 3, k = wi >> 2;  // channel slice, n part
   const int lr = lane & 15, lg = lane >> 4;
@@ -212,16 +228,17 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
   float Hs[NJK][4];
   const int64_t spart = (16 * w + lr) * N + 16 * k * NJK + 4 * lg;  // offset inside one (P, N) state
   const int64_t sbase = (b * a.H + h) * kP * N + spart;
-  // summary j of this (b, h): state at ((b (S-1) + j) H + h) P N, log decay at (b (S-1) + j) H + h
-  auto summary = [&](int64_t j) { return (b * (a.S - 1) + j) * a.H + h; };
+  // summary j of this (b, h): state at ((b R + j) H + h) P N, log decay at (b R + j) H + h
+  auto summary = [&](int64_t j) { return (b * a.R + j) * a.H + h; };
 #pragma unroll
   for (int j = 0; j < NJK; ++j) {
     float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (!ST && a.h0) v = *reinterpret_cast<const float4*>(a.h0 + sbase + 16 * j);
     Hs[j][0] = v.x, Hs[j][1] = v.y, Hs[j][2] = v.z, Hs[j][3] = v.w;
   }
-  if constexpr (!ST) {  // the state entering this segment: earlier segments' summaries, in order
-    for (int64_t sj = 0; sj < seg; ++sj) {
+  if constexpr (!ST) {  // the state entering this segment: earlier sub-segments' summaries, in order
+    const int64_t runs = a.S > 1 ? seg * (a.seg_chunks / a.sub_chunks) : 0;
+    for (int64_t sj = 0; sj < runs; ++sj) {
       const float dec = fast_exp2(a.ws_la[summary(sj)] * kLog2e);
       const float* src = a.ws_state + summary(sj) * kP * N + spart;
 #pragma unroll
@@ -270,8 +287,9 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
   };
 
   const int64_t nchunks = (L + kQ - 1) / kQ;
-  const int64_t c_begin = seg * a.seg_chunks;
-  const int64_t c_end = c_begin + a.seg_chunks < nchunks ? c_begin + a.seg_chunks : nchunks;
+  const int64_t run = ST ? a.sub_chunks : a.seg_chunks;  // chunks this workgroup walks
+  const int64_t c_begin = seg * run;
+  const int64_t c_end = c_begin + run < nchunks ? c_begin + run : nchunks;
   load_bc(c_begin * kQ);
   load_tok(c_begin * kQ);
   load_x(c_begin * kQ);
@@ -541,12 +559,14 @@ hipError_t launch_ssd_n(const SsdProblem& p, hipStream_t stream) {
   k.ws_la = p.ws_la;
   k.L = p.seqlen;
   k.seg_chunks = p.splits > 1 ? p.seg_chunks : (p.seqlen + kQ - 1) / kQ;
+  k.sub_chunks = p.splits > 1 ? p.sub_chunks : k.seg_chunks;
   k.H = static_cast<int>(p.nheads);
   k.G = static_cast<int>(p.ngroups);
   k.S = p.splits > 1 ? p.splits : 1;
+  k.R = p.splits > 1 ? static_cast<int>((p.splits - 1) * (p.seg_chunks / p.sub_chunks)) : 0;
   const unsigned gh = static_cast<unsigned>(p.nheads), gb = static_cast<unsigned>(p.batch);
-  if (k.S > 1) {  // summaries of every segment but the last, then the full pass
-    hipLaunchKernelGGL((ssd_fwd_kernel<N, MODE, NW, true>), dim3(gh, gb, static_cast<unsigned>(k.S - 1)), dim3(64 * NW),
+  if (k.S > 1) {  // summaries of the sub-segments before the last segment, then the full pass
+    hipLaunchKernelGGL((ssd_fwd_kernel<N, MODE, NW, true>), dim3(gh, gb, static_cast<unsigned>(k.R)), dim3(64 * NW),
                        0, stream, k);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -73,16 +73,19 @@ def _plan(a):
 FAR = FAKE + (40 << 32)  # a workspace address clear of every fake tensor
 
 
-def _summary_bytes(B, S, H, N):
+def _summary_bytes(B, S, H, N, m=1):
+    """Summaries of the (S - 1) m state-only sub-segments."""
     up = lambda n: (n + 255) // 256 * 256
-    return up(B * (S - 1) * H * 64 * N * 4) + up(B * (S - 1) * H * 4)
+    return up(B * (S - 1) * m * H * 64 * N * 4) + up(B * (S - 1) * m * H * 4)
 
 
 def test_time_split_plan_small_batch():
     """B*H = 64 heads leave 3/4 of 256 compute units idle: 4 segments of 128
-    chunks, when the workspace holds their summaries."""
+    chunks, when the workspace holds their summaries.  The state-only pass
+    fits two workgroups per compute unit, so the 3 segments before the last
+    are cut in 2 sub-segments each (3 * 2 * 64 = 384 <= 512 workgroups)."""
     shape = (1, 32768, 64, 64, 1, 128)
-    need = _summary_bytes(1, 4, 64, 128)
+    need = _summary_bytes(1, 4, 64, 128, m=2)
     assert _ws(_args(shape=shape)) == need
     assert _plan(_args(shape=shape)) == 1                                      # no workspace: one segment
     assert _plan(_args(shape=shape, workspace=FAR, workspace_bytes=need - 1)) == 1
@@ -118,3 +121,14 @@ def test_workspace_checked_on_host():
     assert _ssd(_args(workspace=FAR, workspace_bytes=-1)) == -5
     assert _ssd(_args(workspace=FAKE + (1 << 32), workspace_bytes=big)) == -6   # dt
     assert _ssd(_args(workspace=FAKE + (9 << 32), workspace_bytes=big)) == -6   # y
+
+
+def test_state_only_sub_segments():
+    """m: the largest divisor of the segment's chunks with (S - 1) m B H <= 512
+    and at least 4 chunks per sub-segment."""
+    # 48 chunks, 3 segments of 16: (3 - 1) m 2 <= 512 and m <= 4 -> m = 4
+    assert _ws(_args(shape=(1, 64 * 48, 2, 64, 1, 64), time_splits=3)) == _summary_bytes(1, 3, 2, 64, m=4)
+    # 60 chunks, 6 segments of 10: m <= 2 -> 2
+    assert _ws(_args(shape=(1, 64 * 60, 2, 64, 1, 64), time_splits=6)) == _summary_bytes(1, 6, 2, 64, m=2)
+    # B H = 128: 2 automatic segments of 64 chunks, 1 * m * 128 <= 512 -> m = 4
+    assert _ws(_args(shape=(2, 8192, 64, 64, 1, 128))) == _summary_bytes(2, 2, 64, 128, m=4)

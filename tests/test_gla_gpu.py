@@ -206,3 +206,18 @@ def test_gla_longctx_full_size_sampled_heads():
         yr, hr = oracle_gla(sub, w.feature_map)
         check(f"y head {hsel}", y[:, :, hsel:hsel + 1], yr, torch.bfloat16)
         check(f"hT head {hsel}", hT[:, hsel:hsel + 1], hr, torch.bfloat16)
+
+
+@pytest.mark.parametrize("mode", ["gated-h0", "linear-elu"])
+def test_gla_time_split_state_only_sub_segments(mode):
+    """Segments of 16 chunks, state-only sub-segments of 4: every element."""
+    inp = workloads.make_gla_inputs(GW[0], batch=1, nheads=2, ngroups=1, dstate=64, seqlen=64 * 48 - 5,
+                                    gated=mode.startswith("gated"), with_h0=mode.endswith("h0"), seed_extra=(36,))
+    fm = "elu" in mode
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    assert _planned_splits(d, 3, fm) == 3
+    y, hT = ssm.gla_fwd(*(d[k] for k in TENS), feature_map=fm, return_final_state=True, time_splits=3)
+    torch.cuda.synchronize()
+    yr, hr = oracle_gla(inp, fm)
+    check("y", y.float().cpu().double().numpy(), yr, torch.bfloat16)
+    check("hT", hT.cpu().double().numpy(), hr, torch.bfloat16)

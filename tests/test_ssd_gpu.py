@@ -199,3 +199,17 @@ def test_ssd_longctx_full_size_sampled_heads():
                             dt_bias=inp["dt_bias"].index_select(0, hi), s0=inp["h0"].index_select(1, hi))
         check(f"y head {hsel}", y[:, :, hsel:hsel + 1], yr, torch.bfloat16)
         check(f"hT head {hsel}", hT[:, hsel:hsel + 1], hr, torch.bfloat16)
+
+
+def test_ssd_time_split_state_only_sub_segments():
+    """Segments of 16 chunks whose state-only pass runs in sub-segments of 4
+    (the planner's choice for B1 H2 with 3 segments): every element."""
+    inp = workloads.make_ssd_inputs(SW[0], batch=1, nheads=2, ngroups=1, dstate=128, seqlen=64 * 48 - 13,
+                                    with_h0=True, seed_extra=(35,))
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    assert _planned_splits(d, 3) == 3
+    y, hT = ssm.ssd_fwd(*(d[k] for k in TENS), return_final_state=True, time_splits=3)
+    torch.cuda.synchronize()
+    yr, hr = oracle_ssd(inp)
+    check("y", y.float().cpu().double().numpy(), yr, torch.bfloat16)
+    check("hT", hT.cpu().double().numpy(), hr, torch.bfloat16)
