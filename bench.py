@@ -61,18 +61,24 @@ FORWARD_SOURCES = ("buffer_io.hpp", "device_common.hpp", "nsplit_dispatch.cpp", 
                    "scan_decode.hip", "scan_lane.hip", "scan_nsplit_impl.hpp")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the forward kernels' HIP sources, so stored traffic counters can
-    be matched to the kernel build they were measured on."""
+# the sources of the chunked matrix-form kernel (SSD and gated attention lines)
+SSD_SOURCES = ("buffer_io.hpp", "device_common.hpp", "ssd_fwd.hip")
+# the sources of the backward kernels (with the forward's, whose checkpoints they read)
+BACKWARD_SOURCES = FORWARD_SOURCES + ("scan_bwd.hip", "scan_bwd_impl.hpp", "scan_bwd_inst.hip")
+
+
+def kernel_source_hash(sources=FORWARD_SOURCES) -> str:
+    """Hash of the kernels' HIP sources, so stored traffic counters can be
+    matched to the kernel build they were measured on."""
     csrc = os.path.join(HERE, "mamba_selective_scan_06_amd", "csrc")
     h = hashlib.sha256()
-    for f in FORWARD_SOURCES:
+    for f in sources:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload_name: str):
+def stored_traffic(workload_name: str, sources=FORWARD_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None.  The summary is a text
     file of `key: value` lines."""
@@ -85,7 +91,7 @@ def stored_traffic(workload_name: str):
             if ":" in line and not line.lstrip().startswith("#"):
                 k, v = line.split(":", 1)
                 rec[k.strip()] = v.strip()
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
     try:
         return int(rec["bytes_per_launch"])
@@ -440,7 +446,9 @@ def bench_backward(w, args, ssm, torch):
                    "time_splits": splits, "workspace_bytes": nbytes,
                    "input_term": "zero-order hold" if args.zoh else "Euler",
                    "states": "from the forward's checkpoints" if ck is not None else "recomputed"},
-        "roofline": _roofline(alg, call_s, "ssm_scan_bwd (local, combine, main, two reductions)"),
+        "roofline": dict(_roofline(alg, call_s, "ssm_scan_bwd (local, combine, main, two reductions)"),
+                         traffic=stored_traffic(w.name + ("_bwd_zoh" if args.zoh else "_bwd")
+                                                + ("_checkpoints" if ck is not None else ""), BACKWARD_SOURCES)),
     }
     if ck is not None:
         out["forward_with_checkpoints_ms"] = round(fwd_ck * 1e3, 4)
@@ -576,6 +584,7 @@ def bench_ssd(args, ssm, torch):
     chunked_flops = toks * 2 * (Q * N + Q * P + 2 * N * P)
     ms = elapsed * 1e3 / steps
     roof = _roofline(alg, kern_s, "ssd_fwd_kernel" if splits == 1 else "ssd_fwd_kernel, state-only + full pass")
+    roof["traffic"] = stored_traffic(w.name, SSD_SOURCES)
     roof["method_tflops"] = round(method_flops / kern_s / 1e12, 2)
     roof["method_frac_bf16_dense"] = round(method_flops / kern_s / 2.5e15, 4)
     roof["chunked_form_tflops"] = round(chunked_flops / kern_s / 1e12, 2)
@@ -653,6 +662,7 @@ def bench_gla(args, ssm, torch):
     chunked_flops = toks * 2 * (Q * N + Q * P + 2 * N * P)
     ms = elapsed * 1e3 / steps
     roof = _roofline(alg, kern_s, "ssd_fwd_kernel" if splits == 1 else "ssd_fwd_kernel, state-only + full pass")
+    roof["traffic"] = stored_traffic(w.name, SSD_SOURCES)
     roof["method_tflops"] = round(method_flops / kern_s / 1e12, 2)
     roof["method_frac_bf16_dense"] = round(method_flops / kern_s / 2.5e15, 4)
     roof["chunked_form_tflops"] = round(chunked_flops / kern_s / 1e12, 2)
