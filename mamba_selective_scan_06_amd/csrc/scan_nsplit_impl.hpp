@@ -823,6 +823,10 @@ __device__ __forceinline__ void scan_loop(Smem& sm, const S* Brow, const S* Crow
         hv[k] = h[k];
       }
       if constexpr (SAVE && (j + 1) % kCkT == 0) {  // a chunk ends: its state for the backward
+        // The store's branch stays between the state update and the readout
+        // (scheduling barriers), followed by two wait states: the readout's
+        // DPP is inline asm, which the compiler does not pad after the join.
+        __builtin_amdgcn_sched_barrier(0);
         // (a segment's padded tiles run past its end, into the next segment's
         // tokens, with its end state held: those positions are the next one's)
         const int32_t done = t0 + j + 1;
@@ -832,6 +836,8 @@ __device__ __forceinline__ void scan_loop(Smem& sm, const S* Brow, const S* Crow
           for (int k = 0; k < K; ++k) v[k] = (STRUCT && ZOH) ? hv[k] * ck.scale[k] : hv[k];
           store_ck<K>(ck.lane + static_cast<int64_t>(done / kCkT - 1) * ck.stride, v);
         }
+        asm volatile("s_nop 1");
+        __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (!STATE_ONLY) {
         auto csrc = [&](int k) { return BL::odd_half(k) ? Chi[q] : Clo[q]; };
