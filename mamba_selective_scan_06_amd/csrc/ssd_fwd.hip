@@ -37,7 +37,7 @@
 // descriptor covers the chunk's valid tokens (past L: loads read 0, stores are
 // dropped), and the next chunk's x, B, C and per-token inputs are loaded
 // during the current chunk (the barriers wait on LDS only).  Per chunk:
-//   A. per-token prefix sums (wave 0); x^T, B^T, B, C into LDS; prefetch;
+//   A. per-token prefix sums (wave 0, DPP); x^T, B^T, B, C into LDS; prefetch;
 //   B. x o w into LDS; M = masked G^T tiles (12 16x16 tiles); partial C H^T;
 //   C. y^T for the wave's tiles (M X from LDS), store; state update.
 // Tokens past L are padded with i = 0, a = 0 and x = B = C = 0, which leaves
@@ -99,6 +99,28 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t&
 template <int W>
 __device__ __forceinline__ uint32_t elem(const uint32_t (&v)[W], int e) {
   return (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu);
+}
+
+// v of the lane the DPP control names, 0 where it names none or the row is
+// not in ROW_MASK.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_from(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf,
+                                                                 false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8
+// inside each 16-lane row, then each row's total carried into the rows after
+// it (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3).  Six
+// DPP adds, no LDS round trip.
+__device__ __forceinline__ float wave_prefix_sum(float s) {
+  s += dpp_from<0x111, 0xf>(s);
+  s += dpp_from<0x112, 0xf>(s);
+  s += dpp_from<0x114, 0xf>(s);
+  s += dpp_from<0x118, 0xf>(s);
+  s += dpp_from<0x142, 0xa>(s);
+  s += dpp_from<0x143, 0xc>(s);
+  return s;
 }
 
 // elu(v) + 1 on 8 packed bf16, rounded back to bf16.
@@ -311,15 +333,10 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
         d = valid ? (a.in_gate ? __uint_as_float(tig) : 1.0f) : 0.0f;
         la = valid ? __uint_as_float(tlf) : 0.0f;
       }
-      float s = la;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(s, off, 64);
-        if (lane >= off) s += o;
-      }
+      const float s = wave_prefix_sum(la);
       sm.dl[cb][lane] = d;
       sm.cs[cb][lane] = s;
-      const float s_end = __shfl(s, kQ - 1, 64);
+      const float s_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), kQ - 1));
       sm.ww[cb][lane] = fast_exp2((s_end - s) * kLog2e) * d;
     }
     if constexpr (!ST) {
