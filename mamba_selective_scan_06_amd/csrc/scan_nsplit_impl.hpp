@@ -197,9 +197,12 @@ struct BCLayout {
 // read a tile's terms into registers while they scan the tile before it: the
 // terms rotate through NS_EB buffers, the partial readouts through two.
 constexpr int NS_EB = 4;
+// U comes first: its reads then fit the 16-bit immediate offsets of one base
+// register and pair into ds_read2st64 (placed after E, whose 64 KB push it past
+// that range, every token's U read needed an address register of its own).
 struct Smem {
-  float E[NS_EB][NS_T][4][64];  // decay terms: chain start per scan wave (structured) or delta in slot 0
   float U[NS_EB][NS_T][64];     // u = delta * x
+  float E[NS_EB][NS_T][4][64];  // decay terms: chain start per scan wave (structured) or delta in slot 0
   float P[2][NS_T][4][64];      // partial readouts per scan wave
 };
 constexpr int kSmemBytes = static_cast<int>(sizeof(Smem));
@@ -739,25 +742,24 @@ __device__ __forceinline__ void scan_loop(Smem& sm, const S* Brow, const S* Crow
   };
 
   // A tile's per-token LDS terms (decay term of this wave's first state or
-  // delta, the ratio r, u), read into registers one tile ahead of their use.
+  // delta, the ratio r, u), read into registers one tile ahead of their use:
+  // token m of the tile in buffer buf into tt[par][m].
   float tt[2][NS_T][3];
-  auto read_terms = [&](auto par_c, int buf) {
+  auto read_token_terms = [&](auto par_c, int buf, int m) {
     constexpr int par = decltype(par_c)::value;
+    tt[par][m][0] = sm.E[buf][m][STRUCT ? c.w : 0][c.lane];
+    tt[par][m][1] = STRUCT ? sm.E[buf][m][0][c.lane] : 0.0f;
+    tt[par][m][2] = sm.U[buf][m][c.lane];
+  };
+  auto read_terms = [&](auto par_c, int buf) {
 #pragma unroll
-    for (int j = 0; j < NS_T; ++j) {
-      tt[par][j][0] = sm.E[buf][j][STRUCT ? c.w : 0][c.lane];
-      tt[par][j][1] = STRUCT ? sm.E[buf][j][0][c.lane] : 0.0f;
-      tt[par][j][2] = sm.U[buf][j][c.lane];
-    }
+    for (int j = 0; j < NS_T; ++j) read_token_terms(par_c, buf, j);
   };
 
   auto scan_tile = [&](auto slot_c, auto buf_c, int32_t t0) {  // t0: the tile's first token
     constexpr int slot = decltype(slot_c)::value;
     constexpr int buf = decltype(buf_c)::value;  // term buffer of this tile (tile % NS_EB)
     constexpr int par = buf & 1;
-    // the next tile's terms (the owners wrote them an iteration ago)
-    read_terms(std::integral_constant<int, par ^ 1>{}, (buf + 1) % NS_EB);
-    __builtin_amdgcn_sched_barrier(0);
     float Blo[NLD], Bhi[NLD], Clo[NLD], Chi[NLD];
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
@@ -770,12 +772,18 @@ __device__ __forceinline__ void scan_loop(Smem& sm, const S* Brow, const S* Crow
         Bhi[q] = BL::kPairs ? __uint_as_float(bw & 0xffff0000u) : 0.0f;
       }
     }
-    // (Reading a token's LDS terms earlier than its use, in bursts or a few
-    // tokens ahead, measured slower on this GPU: the reads stay next to it,
-    // held there by a scheduling barrier after every second token.)
     auto token = [&](auto j_c) {
       constexpr int j = decltype(j_c)::value;
       constexpr int q = BL::load_of(j);
+      // The next tile's terms (the owners wrote them an iteration ago), two
+      // tokens' worth at every second token.  Issued as one burst at the top
+      // of the tile, the reads filled the LDS counter and stalled the wave
+      // there (the 16th outstanding LDS instruction waits for the first); spread
+      // out, each pair lands long before its tile starts.
+      if constexpr (j % 2 == 0) {
+        read_token_terms(std::integral_constant<int, par ^ 1>{}, (buf + 1) % NS_EB, j);
+        read_token_terms(std::integral_constant<int, par ^ 1>{}, (buf + 1) % NS_EB, j + 1);
+      }
       if constexpr (!STATE_ONLY && j % BL::TPL == 0) {
         const uint32_t cw = ring_word(cq[slot][q]);
         if constexpr (BL::kF32) {
@@ -786,6 +794,12 @@ __device__ __forceinline__ void scan_loop(Smem& sm, const S* Brow, const S* Crow
           Chi[q] = BL::kPairs ? __uint_as_float(cw & 0xffff0000u) : 0.0f;
         }
         if constexpr (STRUCT && ZOH) Clo[q] *= cslo, Chi[q] *= cshi;
+        // Pinned: the compiler may not recompute a widened word next to a
+        // later token's readout (a VALU write right before the DPP read).
+        if constexpr (BL::kPairs)
+          asm volatile("" : "+v"(Clo[q]), "+v"(Chi[q]));
+        else
+          asm volatile("" : "+v"(Clo[q]));
       }
       const float u = tt[par][j][2];
       float hv[K];
@@ -864,12 +878,9 @@ __device__ __forceinline__ void scan_loop(Smem& sm, const S* Brow, const S* Crow
         }
         sm.P[par][j][c.w][c.lane] = acc;
       }
-      // keep each pair of tokens' LDS reads, arithmetic and writes together
-      // (pairs share paired LDS instructions): reads grouped further ahead of
-      // their tokens measured slower.  The state-only pass (no readout) is
-      // left to the scheduler (no pinned ring words either), which does
-      // better there.
-      if constexpr (!STATE_ONLY && j % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      // (No scheduling barrier between tokens: pinning each pair of tokens'
+      // reads, arithmetic and writes together measured 6% slower than leaving
+      // the order to the scheduler.)
     };
     [&]<int... js>(std::integer_sequence<int, js...>) {
       (token(std::integral_constant<int, js>{}), ...);

@@ -1,7 +1,7 @@
 // Issue cost of wave64 VALU instructions on one SIMD (gfx950), by operand
 // kind and number of waves per SIMD.  Every kernel runs ITER iterations of 32
-// independent instructions (8 accumulators, registers fixed in asm so the
-// VGPR banks, index mod 4, are known) and the time per instruction per SIMD
+// instructions: independent ones on 8 accumulators (registers fixed in asm so
+// the VGPR banks, index mod 4, are known), or one dependent chain and the time per instruction per SIMD
 // is the launch time over (instructions x waves per SIMD).  Prints one line
 // per case: "<case> <waves per SIMD> <ns per instruction per SIMD>".
 #include <hip/hip_runtime.h>
@@ -46,6 +46,13 @@ __global__ void probe(int* out) {
     if constexpr (KIND == 3) asm volatile(X4(B8("v_fmac_f32_dpp", "v33", "v34", DPP)) ::: CLOB);
     // a two-source multiply
     if constexpr (KIND == 4) asm volatile(X4(B8("v_mul_f32_e32", "v33", "v35", "")) ::: CLOB);
+    // one dependent chain: all 32 FMAs accumulate into v40, so each waits for
+    // the one before (what a lone wave pays for back-to-back dependences)
+    if constexpr (KIND == 6)
+      asm volatile(X4(X4("v_fmac_f32_e32 v40, v33, v34\n v_fmac_f32_e32 v40, v33, v34\n")) ::: CLOB);
+    // the same chain with a DPP row-broadcast first source
+    if constexpr (KIND == 7)
+      asm volatile(X4(X4("v_fmac_f32_dpp v40, v33, v34" DPP "\n v_fmac_f32_dpp v40, v33, v34" DPP "\n")) ::: CLOB);
     // a transcendental (2^x), one source
     if constexpr (KIND == 5)
       asm volatile(X4("v_exp_f32 v40, v33\n v_exp_f32 v44, v33\n v_exp_f32 v48, v33\n v_exp_f32 v52, v33\n"
@@ -83,6 +90,8 @@ int main() {
     run<3>("fma_dpp", w);
     run<4>("mul", w);
     run<5>("exp", w);
+    run<6>("fma_chain", w);
+    run<7>("fma_dpp_chain", w);
   }
   return 0;
 }

@@ -1,8 +1,9 @@
 """The gfx950 rates the forward kernel's design rests on, measured by the
 probes in tests/hw_probes/ (built by __graft_entry__.build()):
 
-- a lone wave issues at most one VALU instruction every ~4 cycles, while a
-  SIMD runs the instructions of two waves in about half that time each;
+- a lone wave issues at most one VALU instruction every ~4 cycles, dependent
+  or not, while a SIMD runs the instructions of two waves in about half that
+  time each;
 - a fused multiply-add whose sources share the accumulator's VGPR bank, or
   takes a scalar (SGPR) or DPP-broadcast operand, costs the SIMD about twice
   a plain one; a transcendental about four times a multiply;
@@ -51,6 +52,10 @@ def test_valu_issue_costs():
         assert r[("fma_sgpr", w)] > 1.4 * base
         assert r[("fma_dpp", w)] > 1.4 * base
         assert r[("exp", w)] > 2.5 * r[("mul", w)]
+    # a lone wave pays nothing for dependences beyond its issue slot: one chain
+    # of dependent FMAs runs at the rate of eight independent ones
+    assert r[("fma_chain", 1)] < 1.2 * fma1
+    assert r[("fma_dpp_chain", 1)] < 1.2 * r[("fma_dpp", 1)]
 
 
 def test_lds_widths():
