@@ -11,6 +11,11 @@ With a chunked workload (the 256K-token sequence run as 32 chained calls) a
 step is the whole chain; with the decode workload a step is its 128
 single-token steps.  Those lines add per-call / per-decode-step times.
 
+Before the W warmup steps, every line runs its step untimed for --settle-ms
+(300 ms) of wall time: the GPU raises its clocks over the first tens of
+milliseconds of sustained load, and a short run would otherwise time the ramp.
+The JSON line reports what that phase ran ("settle").
+
 The metric is scan elements per second, B*L*D*N / step time, in GElem/s.  The
 roofline object reports the algorithmic HBM bytes of one launch (every input
 read once, y and hT written once) over the launch's average duration, timed
@@ -37,6 +42,37 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# What the clock-settling phase did (added to the JSON line as "settle").
+SETTLE = {}
+
+
+def settle(fn, torch, args):
+    """Run fn(i) back to back, untimed, for args.settle_ms of wall time before
+    the warmup steps.  Under this sustained load the GPU raises its clocks over
+    the first tens of milliseconds: with 5 warmup steps of the 1.4B-shaped
+    layer (2.5 ms) the timed launches averaged 498 us, after 100 warmup steps
+    403 us, so without this phase a short run times the clock's ramp rather
+    than the kernel."""
+    if args.settle_ms <= 0:
+        return
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        for _ in range(2):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    SETTLE.update({"ms": round((time.perf_counter() - t0) * 1e3, 1), "calls": n})
+    log(f"clocks settled: {n} untimed calls in {SETTLE['ms']} ms")
+
+
+def emit(out):
+    if SETTLE:
+        out["settle"] = dict(SETTLE, note="untimed calls of the same step before the warmup steps, while the "
+                                          "GPU's clocks ramp up under load")
+    print(json.dumps(out), flush=True)
 
 
 def algorithmic_bytes(w) -> int:
@@ -206,6 +242,7 @@ def bench_chunked(w, args, ssm, torch):
             if events is not None:
                 events[c][1].record(stream)
 
+    settle(lambda i: one_pass(), torch, args)
     for _ in range(args.warmup):
         one_pass()
     torch.cuda.synchronize()
@@ -279,6 +316,7 @@ def bench_decode(w, args, ssm, torch):
             if events is not None:
                 events[t][1].record(stream)
 
+    settle(lambda i: one_pass(), torch, args)
     for _ in range(args.warmup):
         one_pass()
     torch.cuda.synchronize()
@@ -357,6 +395,7 @@ def bench_decode(w, args, ssm, torch):
 def time_calls(fn, torch, dev, args):
     """Mean seconds per call of fn on torch's current stream (HIP events), after warmup."""
     stream = torch.cuda.current_stream(dev)
+    settle(lambda i: fn(), torch, args)
     for _ in range(max(args.warmup, 1)):
         fn()
     torch.cuda.synchronize()
@@ -413,6 +452,7 @@ def bench_backward(w, args, ssm, torch):
         if rc != 0:
             raise RuntimeError(f"ssm_scan_bwd: {ssm.strerror(rc)}")
 
+    settle(lambda i: step(), torch, args)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -495,6 +535,7 @@ def bench_conv(w, args, ssm, torch):
     wt, bs = prm["weight"].to(dev), prm["bias"].to(dev)
     us = [torch.empty_like(xs[0]) for _ in xs]
     stream = torch.cuda.current_stream(dev)
+    settle(lambda i: ssm.conv1d_silu(xs[i % 2], wt, bs, out=us[i % 2]), torch, args)
     for i in range(args.warmup):
         ssm.conv1d_silu(xs[i % 2], wt, bs, out=us[i % 2])
     torch.cuda.synchronize()
@@ -561,6 +602,7 @@ def bench_ssd(args, ssm, torch):
         ssm.ssd_fwd(xs[i % 2], *(d[k] for k in names), None, out=ys[i % 2], final_state_out=hT,
                     time_splits=args.time_splits, workspace=ws)
 
+    settle(step, torch, args)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -639,6 +681,7 @@ def bench_gla(args, ssm, torch):
         ssm.gla_fwd(d["q"], d["k"], vs[i % 2], d["log_f"], d["in_gate"], None, feature_map=w.feature_map,
                     out=ys[i % 2], final_state_out=hT, workspace=ws, time_splits=args.time_splits)
 
+    settle(step, torch, args)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -705,6 +748,8 @@ def main():
     ap.add_argument("--carry-scan", action="store_true",
                     help="time-split calls compose segment summaries with the wave-level scan launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed calls of the step for this long before the warmup steps (clock ramp; 0: none)")
     ap.add_argument("--backward", action="store_true", help="time ssm_scan_bwd (all gradients) instead")
     ap.add_argument("--checkpoints", action="store_true",
                     help="with --backward: the backward starts from the forward's checkpoints (the forward writing "
@@ -742,29 +787,29 @@ def main():
         return
 
     if args.ssd:
-        print(json.dumps(bench_ssd(args, ssm, torch)), flush=True)
+        emit(bench_ssd(args, ssm, torch))
         return
     if args.gla:
-        print(json.dumps(bench_gla(args, ssm, torch)), flush=True)
+        emit(bench_gla(args, ssm, torch))
         return
     w = workloads.BY_NAME[args.workload]
     if args.prologue:
         if w.chunks > 1 or w.steps:
             print("--prologue runs the single-call workloads", file=sys.stderr)
             sys.exit(2)
-        print(json.dumps(bench_conv(w, args, ssm, torch)), flush=True)
+        emit(bench_conv(w, args, ssm, torch))
         return
     if args.backward:
         if w.chunks > 1 or w.steps:
             print("--backward runs the single-call workloads", file=sys.stderr)
             sys.exit(2)
-        print(json.dumps(bench_backward(w, args, ssm, torch)), flush=True)
+        emit(bench_backward(w, args, ssm, torch))
         return
     if w.chunks > 1:
-        print(json.dumps(bench_chunked(w, args, ssm, torch)), flush=True)
+        emit(bench_chunked(w, args, ssm, torch))
         return
     if w.steps:
-        print(json.dumps(bench_decode(w, args, ssm, torch)), flush=True)
+        emit(bench_decode(w, args, ssm, torch))
         return
     dev = torch.device("cuda:0")
     log(f"workload {w.describe()}")
@@ -796,6 +841,7 @@ def main():
                      out=y[i % 2], final_state_out=hT[i % 2], workspace=ws, variant=args.variant,
                      time_splits=args.time_splits, generic_a=args.generic_a, zoh=args.zoh, carry_scan=args.carry_scan)
 
+    settle(step, torch, args)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -856,7 +902,7 @@ def main():
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(w, inp, zoh=args.zoh)
         log(f"cpu baseline {out['cpu_baseline']['value']} GElem/s on {out['cpu_baseline']['cores']} threads")
-    print(json.dumps(out), flush=True)
+    emit(out)
 
 
 if __name__ == "__main__":
