@@ -37,10 +37,10 @@ bool nsplit_ok(int64_t n) { return n == 4 || n == 8 || n == 16 || n == 32 || n =
 
 // The NSPLIT kernels count tokens in 32 bits and address a batch row through
 // buffer descriptors with 32-bit byte offsets.  A row whose accesses (up to
-// 288 tokens past its end, for the prefetch) fit one 2 GiB descriptor uses
+// 320 tokens past its end, for the prefetch) fit one 2 GiB descriptor uses
 // fixed descriptors; a longer row is addressed through windows that move along
-// it, with offsets under 288 tokens from the window start.  So a token of a
-// row must stay below 2 GiB / 288 (D up to about 3.7 million bf16 channels);
+// it, with offsets under 320 tokens from the window start.  So a token of a
+// row must stay below 2 GiB / 320 (D up to about 3.3 million bf16 channels);
 // the row length itself is free.
 int64_t nsplit_token_bytes(const ssm_scan_args* a) {
   const int64_t es = a->dtype == SSM_DTYPE_F32 ? 4 : 2;

@@ -41,7 +41,7 @@ constexpr int kFlagCarryScan = 4;  // time split: compose segment summaries with
 constexpr int kNsplitTile = 16;
 // Tokens past the current position (the end of a row, or the start of a
 // descriptor window) that the NSPLIT kernels' prefetching loads can reach.
-constexpr int64_t kNsplitReach = 288;
+constexpr int64_t kNsplitReach = 320;
 // Tiles per loop turn of the NSPLIT kernels; a segment runs whole turns and
 // at most one half turn, so its padded length is a multiple of half a turn.
 constexpr int kNsplitTurn = 8;

@@ -24,23 +24,24 @@
 //   h_n  <- Abar_n h_n + (delta x) B_t[n]              sections 2.2, 3.3 (Euler input term)
 //   y     = sum_n C_t[n] h_n + D[d] x, y *= SiLU(z)    sections 2.2, 3.4
 //
-// Time is walked in tiles of 16 tokens with one barrier per tile.  In
+// Time is walked in tiles of 16 tokens with one barrier per two tiles.  In
 // iteration k the scan waves consume tile k (its per-token terms already in
 // registers, writing their partial readouts sum_{n in wave} C_t[n] h_n) and
 // read tile k+1's terms from LDS into registers, while the owners compute
-// tile k+2's terms (4 term buffers) and finish tile k-1 from the partials
-// (2 buffers).  So no scan wave waits on LDS data inside a tile.  The loop
-// runs turns of 8 tiles (and at most one half turn), which keeps every ring
-// index a compile-time constant.
+// tile k+3's terms and finish tile k-2 from the partials (4 buffers of each).
+// So no scan wave waits on LDS data inside a tile, and every buffer is
+// written and read on opposite sides of a barrier.  The loop runs turns of 8
+// tiles (and at most one half turn), which keeps every ring index a
+// compile-time constant.
 
 // Memory.  All loads are raw buffer loads with the whole byte offset in the
 // VGPR offset (the part the range check covers), through a descriptor over one
 // batch row, so loads past the row end return 0 (prefetching past the end of
 // the sequence is safe).  Stores of y go through a descriptor that starts a
-// tile before the segment and ends with it, and a lane whose store must not
+// two tiles before the segment and ends with it, and a lane whose store must not
 // happen gets an offset past it.  Offsets are 32-bit: for rows of 2 GiB or
 // more (WIN) the descriptors instead cover windows that start a few tiles
-// behind the accesses and move forward every turn, so offsets stay below 288
+// behind the accesses and move forward every turn, so offsets stay below 320
 // tokens of a row whatever its length.
 // Every input a tile needs is loaded ahead into register rings: x, delta and
 // z of the owners' tokens 8 tiles ahead (4 for one-channel owners: the
@@ -193,17 +194,20 @@ struct BCLayout {
   static constexpr bool odd_half(int k) { return kPairs && (k & 1); }
 };
 
-// The owners compute a tile's terms two tiles ahead of the scan waves, which
-// read a tile's terms into registers while they scan the tile before it: the
-// terms rotate through NS_EB buffers, the partial readouts through two.
+// The owners compute a tile's terms three tiles ahead of the scan waves, which
+// read a tile's terms into registers while they scan the tile before it, and
+// finish a tile two iterations after it was scanned; the workgroup meets at a
+// barrier after every second tile.  Terms and partial readouts each rotate
+// through four buffers (tile m in buffer m % 4).
 constexpr int NS_EB = 4;
+constexpr int NS_PB = 4;
 // U comes first: its reads then fit the 16-bit immediate offsets of one base
 // register and pair into ds_read2st64 (placed after E, whose 64 KB push it past
 // that range, every token's U read needed an address register of its own).
 struct Smem {
   float U[NS_EB][NS_T][64];     // u = delta * x
   float E[NS_EB][NS_T][4][64];  // decay terms: chain start per scan wave (structured) or delta in slot 0
-  float P[2][NS_T][4][64];      // partial readouts per scan wave
+  float P[NS_PB][NS_T][4][64];  // partial readouts per scan wave
 };
 constexpr int kSmemBytes = static_cast<int>(sizeof(Smem));
 
@@ -243,8 +247,8 @@ __device__ __forceinline__ uint32_t ring_word(uint32_t v) {
 // the part shared by the tensors of one layout (byte offset of W, and the
 // bytes to the end capped below 2 GiB at cap_tokens = kMaxRecords / tok_bytes
 // tokens), then one descriptor per tensor.  Every offset the loops use is
-// under 288 tokens from W; the planner keeps that under 2 GiB, so a capped
-// window still covers it.  W may be one tile before the row start (the first
+// under 320 tokens from W; the planner keeps that under 2 GiB, so a capped
+// window still covers it.  W may be two tiles before the row start (the first
 // store window): the base is formed as an integer address, and nothing before
 // the row is accessed.
 struct WinSpan {
@@ -279,13 +283,15 @@ __device__ __forceinline__ void owner_loop(Smem& sm, const S* xrow, const S* dlr
   const uint32_t yo = c.active ? (c.d0 + c.lane) * ES : kPastWindow;
 
   uint32_t xr[NS_PF][NS_OWN], dr[NS_PF][NS_OWN], zr[NS_PF][NS_OWN];
-  float keep_dx[NS_PF][NS_OWN], keep_g[NS_PF][NS_OWN];
+  // D x and the gate of tile m live in slot m % 8 from its terms (three tiles
+  // ahead of the scan) until it is finished (two tiles behind)
+  float keep_x[8][NS_OWN], keep_g[8][NS_OWN];
 
-  // descriptor starts: the loads' at W, the stores' at Wy, a tile before the
-  // segment (that tile's stores are sent out of range).  Windowed (WIN): W
-  // starts with the segment and both move at every turn of the ring (the
-  // loads reach 9 tiles past W, the stores 5 past Wy).
-  int32_t W = WIN ? c.t_begin : 0, Wy = c.t_begin - NS_T;
+  // descriptor starts: the loads' at W, the stores' at Wy, two tiles before
+  // the segment (those tiles' stores are sent out of range).  Windowed (WIN):
+  // W starts with the segment and both move at every turn of the ring (the
+  // loads reach 15 tiles past W, the stores 8 past Wy).
+  int32_t W = WIN ? c.t_begin : 0, Wy = c.t_begin - 2 * NS_T;
   __amdgpu_buffer_rsrc_t bx, bdl, bz, by;
   const uint32_t tok_bytes = c.D * ES;
   const int32_t cap_tokens = static_cast<int32_t>(kMaxRecords / tok_bytes);
@@ -310,22 +316,23 @@ __device__ __forceinline__ void owner_loop(Smem& sm, const S* xrow, const S* dlr
     }
   };
 
-  // shared terms of the tile at t0 (ring slot `slot`) into LDS buffer `buf`
-  auto compute_tile = [&](auto slot_c, int buf, int32_t t0) {
+  // shared terms of the tile at t0 (ring slot `slot`, keep slot `ks`) into LDS buffer `buf`
+  auto compute_tile = [&](auto slot_c, auto ks_c, int buf, int32_t t0) {
     constexpr int slot = decltype(slot_c)::value;
+    constexpr int ks = decltype(ks_c)::value;
 #pragma unroll
     for (int i = 0; i < NS_OWN; ++i) {
       const int j = 4 * i + o;
       float e0 = 1.0f, e1 = 1.0f, e2 = 1.0f, e3 = 1.0f, u = 0.0f;  // neutral step
       if constexpr (!STRUCT || ZOH) e0 = e1 = e2 = e3 = 0.0f;     // delta = 0 / exp(0) - 1 = 0
-      float dx = 0.0f, g = 0.0f;
+      float xk = 0.0f, g = 0.0f;  // x of a token that is finished later (D x is fused there)
       if (t0 + j < c.t_end) {  // wave-uniform
         const float xv = bits_to_f32<S>(xr[slot][i]);
         const float dt = softplus_f32(bits_to_f32<S>(dr[slot][i]) + c.bias_d);
         if constexpr (STATE_ONLY) {
           dsum += dt;
         } else {
-          dx = c.D_d * xv;
+          xk = xv;
           if constexpr (GATE) g = silu_f32(bits_to_f32<S>(zr[slot][i]));
         }
         if constexpr (STRUCT && ZOH) {
@@ -363,8 +370,8 @@ __device__ __forceinline__ void owner_loop(Smem& sm, const S* xrow, const S* dlr
         sm.E[buf][j][3][c.lane] = e3;
       }
       sm.U[buf][j][c.lane] = u;
-      keep_dx[slot][i] = dx;
-      keep_g[slot][i] = g;
+      keep_x[ks][i] = xk;
+      keep_g[ks][i] = g;
     }
   };
 
@@ -377,17 +384,17 @@ __device__ __forceinline__ void owner_loop(Smem& sm, const S* xrow, const S* dlr
 #pragma unroll
       for (int w = 0; w < 4; ++w) pr[i][w] = sm.P[buf][4 * i + o][w][c.lane];
   };
-  // finish the tile at t0 (its keep values in slot `slot`) from the partials in pr
-  auto finish_tile = [&](auto slot_c, int32_t t0) {
-    constexpr int slot = decltype(slot_c)::value;
+  // finish the tile at t0 (its keep values in slot `ks`) from the partials in pr
+  auto finish_tile = [&](auto ks_c, int32_t t0) {
+    constexpr int ks = decltype(ks_c)::value;
 #pragma unroll
     for (int i = 0; i < NS_OWN; ++i) {
       const int j = 4 * i + o;
       float yv = ((pr[i][0] + pr[i][1]) + pr[i][2]) + pr[i][3];
-      yv += keep_dx[slot][i];
-      if constexpr (GATE) yv *= keep_g[slot][i];
-      // by ends with the segment: tokens before it (the tile "before the
-      // first" finished in the first iteration) and lanes past D are sent out
+      yv = __builtin_fmaf(c.D_d, keep_x[ks][i], yv);  // one fused D x term, whatever the schedule
+      if constexpr (GATE) yv *= keep_g[ks][i];
+      // by ends with the segment: tokens before it (the two tiles "before the
+      // first" finished in the first iterations) and lanes past D are sent out
       // of range; tokens after it fail the range check.
       const int32_t tj = t0 + j;
       const uint32_t off = (tj >= c.t_begin ? yo : kPastWindow) + static_cast<uint32_t>(tj - Wy) * c.D * ES;
@@ -395,7 +402,7 @@ __device__ __forceinline__ void owner_loop(Smem& sm, const S* xrow, const S* dlr
     }
   };
 
-  static_assert(NS_PF == 4 && NS_TURN % NS_PF == 0 && NS_EB == 4, "the ring code below is written for 4 slots");
+  static_assert(NS_PF == 4 && NS_TURN == 8 && NS_EB == 4 && NS_PB == 4, "the ring code below is written for these");
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -404,30 +411,35 @@ __device__ __forceinline__ void owner_loop(Smem& sm, const S* xrow, const S* dlr
   load_tile(I1{}, c.t_begin + 1 * NS_T);
   load_tile(I2{}, c.t_begin + 2 * NS_T);
   load_tile(I3{}, c.t_begin + 3 * NS_T);
-  compute_tile(I0{}, 0, c.t_begin);
+  compute_tile(I0{}, I0{}, 0, c.t_begin);
   load_tile(I0{}, c.t_begin + NS_PF * NS_T);
-  compute_tile(I1{}, 1, c.t_begin + NS_T);
+  compute_tile(I1{}, I1{}, 1, c.t_begin + NS_T);
   load_tile(I1{}, c.t_begin + (NS_PF + 1) * NS_T);
+  compute_tile(I2{}, I2{}, 2, c.t_begin + 2 * NS_T);
+  load_tile(I2{}, c.t_begin + (NS_PF + 2) * NS_T);
   __syncthreads();
-  // iteration k (tile k scanned meanwhile): compute tile k+2, finish tile k-1
+  __syncthreads();  // the scan waves have read tile 0's terms (buffer 0 is written again in iteration 1)
+  // iteration k (tile k scanned meanwhile): compute tile k+3, finish tile k-2;
+  // a barrier after every odd k
   int32_t k0 = 0;
   auto turn_start = [&]() {
-    if constexpr (WIN) {  // this turn loads tiles k0+6..k0+13 and stores tiles k0-1..k0+6
+    if constexpr (WIN) {  // this turn loads tiles k0+7..k0+14 and stores tiles k0-2..k0+5
       W = opaque_sgpr(c.t_begin + k0 * NS_T);
-      Wy = W - NS_T;
+      Wy = W - 2 * NS_T;
       set_windows();
     }
   };
-  // ring slot and term buffer of tile m are m % 4; k0 is a multiple of 4
+  // ring slot of tile m is m % 4, keep slot m % 8, term and partial buffers
+  // m % 4; k0 is a multiple of 8
   auto step = [&](auto kc) {
     constexpr int kk = decltype(kc)::value;  // k0 + kk is the tile being scanned
     const int32_t tk = c.t_begin + (k0 + kk) * NS_T;
-    using Ahead = std::integral_constant<int, (kk + 2) % NS_PF>;
-    if constexpr (!STATE_ONLY) read_partials((kk + 1) & 1);
-    compute_tile(Ahead{}, (kk + 2) % NS_EB, tk + 2 * NS_T);
-    load_tile(Ahead{}, tk + 2 * NS_T + NS_PF * NS_T);
-    if constexpr (!STATE_ONLY) finish_tile(std::integral_constant<int, (kk + NS_PF - 1) % NS_PF>{}, tk - NS_T);
-    __syncthreads();
+    using Ahead = std::integral_constant<int, (kk + 3) % NS_PF>;
+    if constexpr (!STATE_ONLY) read_partials((kk + 2) % NS_PB);
+    compute_tile(Ahead{}, std::integral_constant<int, (kk + 3) % 8>{}, (kk + 3) % NS_EB, tk + 3 * NS_T);
+    load_tile(Ahead{}, tk + 3 * NS_T + NS_PF * NS_T);
+    if constexpr (!STATE_ONLY) finish_tile(std::integral_constant<int, (kk + 6) % 8>{}, tk - 2 * NS_T);
+    if constexpr (kk % 2 == 1) __syncthreads();
   };
   for (; k0 + NS_TURN <= c.ntiles; k0 += NS_TURN) {
     turn_start();
@@ -437,10 +449,19 @@ __device__ __forceinline__ void owner_loop(Smem& sm, const S* xrow, const S* dlr
     turn_start();
     static_for<NS_TURN / 2>(step);
   }
-  // the last scanned tile (ntiles-1 has slot 3)
+  // the last two scanned tiles (keep slots 6, 7, or 2, 3 after a half turn)
   if constexpr (!STATE_ONLY) {
-    read_partials((c.ntiles - 1) & 1);
-    finish_tile(I3{}, c.t_begin + (c.ntiles - 1) * NS_T);
+    const bool whole = c.ntiles % 8 == 0;
+    read_partials((c.ntiles - 2) % NS_PB);
+    if (whole)
+      finish_tile(std::integral_constant<int, 6>{}, c.t_begin + (c.ntiles - 2) * NS_T);
+    else
+      finish_tile(std::integral_constant<int, 2>{}, c.t_begin + (c.ntiles - 2) * NS_T);
+    read_partials((c.ntiles - 1) % NS_PB);
+    if (whole)
+      finish_tile(std::integral_constant<int, 7>{}, c.t_begin + (c.ntiles - 1) * NS_T);
+    else
+      finish_tile(std::integral_constant<int, 3>{}, c.t_begin + (c.ntiles - 1) * NS_T);
   }
 }
 
@@ -507,7 +528,7 @@ __device__ __forceinline__ void owner_loop_wide(Smem& sm, const S* xrow, const S
   const uint32_t yo = (c.d0 + cg < c.D) ? xo : kPastWindow;
 
   V xr[NS_PFO], dr[NS_PFO], zr[NS_PFO];
-  float keep_dx[NS_PFO][4], keep_g[NS_PFO][4];
+  float keep_x[NS_PFO][4], keep_g[NS_PFO][4];
   // a ring word, marked as used here: its load's wait stays at the tile that
   // needs it (hoisted to the top of a turn, it would drain the whole ring)
   auto pin = [](V v) {
@@ -520,7 +541,7 @@ __device__ __forceinline__ void owner_loop_wide(Smem& sm, const S* xrow, const S
     return v;
   };
 
-  int32_t W = WIN ? c.t_begin : 0, Wy = c.t_begin - NS_T;
+  int32_t W = WIN ? c.t_begin : 0, Wy = c.t_begin - 2 * NS_T;
   __amdgpu_buffer_rsrc_t bx, bdl, bz, by;
   const uint32_t tok_bytes = c.D * ES;
   const int32_t cap_tokens = static_cast<int32_t>(kMaxRecords / tok_bytes);
@@ -562,7 +583,7 @@ __device__ __forceinline__ void owner_loop_wide(Smem& sm, const S* xrow, const S
       if constexpr (STATE_ONLY) {
         dsum[k] += dt;
       } else {
-        keep_dx[slot][k] = ch.Dd[k] * xv;
+        keep_x[slot][k] = xv;
         if constexpr (GATE) keep_g[slot][k] = silu_f32(WV::get(zw, k));
       }
       if constexpr (STRUCT && ZOH) {
@@ -613,7 +634,7 @@ __device__ __forceinline__ void owner_loop_wide(Smem& sm, const S* xrow, const S
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       yv[k] = ((p0[k] + p1[k]) + p2[k]) + p3[k];
-      yv[k] += keep_dx[slot][k];
+      yv[k] = __builtin_fmaf(ch.Dd[k], keep_x[slot][k], yv[k]);  // one fused D x term, whatever the schedule
       if constexpr (GATE) yv[k] *= keep_g[slot][k];
     }
     const int32_t tj = t0 + jl;
@@ -621,32 +642,36 @@ __device__ __forceinline__ void owner_loop_wide(Smem& sm, const S* xrow, const S
     WV::store(by, off, yv);
   };
 
-  static_assert(NS_TURN % NS_PFO == 0 && NS_TURN % NS_EB == 0, "a turn covers whole rings");
+  static_assert(NS_TURN % NS_PFO == 0 && NS_TURN % NS_EB == 0 && NS_PFO == 8 && NS_PB == 4, "a turn covers whole rings");
   static_for<NS_PFO>([&](auto sc) { load_tile(sc, c.t_begin + decltype(sc)::value * NS_T); });
   compute_tile(std::integral_constant<int, 0>{}, 0, c.t_begin);
   load_tile(std::integral_constant<int, 0>{}, c.t_begin + NS_PFO * NS_T);
   compute_tile(std::integral_constant<int, 1>{}, 1, c.t_begin + NS_T);
   load_tile(std::integral_constant<int, 1>{}, c.t_begin + (NS_PFO + 1) * NS_T);
+  compute_tile(std::integral_constant<int, 2>{}, 2, c.t_begin + 2 * NS_T);
+  load_tile(std::integral_constant<int, 2>{}, c.t_begin + (NS_PFO + 2) * NS_T);
   __syncthreads();
-  // iteration k (tile k scanned meanwhile): compute tile k+2, load tile
-  // k+2+NS_PFO into its slot, finish tile k-1
+  __syncthreads();  // the scan waves have read tile 0's terms (buffer 0 is written again in iteration 1)
+  // iteration k (tile k scanned meanwhile): compute tile k+3, load tile
+  // k+3+NS_PFO into its slot, finish tile k-2; a barrier after every odd k
   int32_t k0 = 0;
   auto turn_start = [&]() {
-    if constexpr (WIN) {  // this turn loads tiles k0+10..k0+17 and stores tiles k0-1..k0+6
+    if constexpr (WIN) {  // this turn loads tiles k0+11..k0+18 and stores tiles k0-2..k0+5
       W = opaque_sgpr(c.t_begin + k0 * NS_T);
-      Wy = W - NS_T;
+      Wy = W - 2 * NS_T;
       set_windows();
     }
   };
+  // ring and keep slot of tile m are m % 8, its term and partial buffers m % 4
   auto step = [&](auto kc) {
     constexpr int kk = decltype(kc)::value;
     const int32_t tk = c.t_begin + (k0 + kk) * NS_T;
-    using Ahead = std::integral_constant<int, (kk + 2) % NS_PFO>;
-    if constexpr (!STATE_ONLY) read_partials((kk + 1) & 1);
-    compute_tile(Ahead{}, (kk + 2) % NS_EB, tk + 2 * NS_T);
-    load_tile(Ahead{}, tk + 2 * NS_T + NS_PFO * NS_T);
-    if constexpr (!STATE_ONLY) finish_tile(std::integral_constant<int, (kk + NS_PFO - 1) % NS_PFO>{}, tk - NS_T);
-    __syncthreads();
+    using Ahead = std::integral_constant<int, (kk + 3) % NS_PFO>;
+    if constexpr (!STATE_ONLY) read_partials((kk + 2) % NS_PB);
+    compute_tile(Ahead{}, (kk + 3) % NS_EB, tk + 3 * NS_T);
+    load_tile(Ahead{}, tk + 3 * NS_T + NS_PFO * NS_T);
+    if constexpr (!STATE_ONLY) finish_tile(std::integral_constant<int, (kk + NS_PFO - 2) % NS_PFO>{}, tk - 2 * NS_T);
+    if constexpr (kk % 2 == 1) __syncthreads();
   };
   for (; k0 + NS_TURN <= c.ntiles; k0 += NS_TURN) {
     turn_start();
@@ -656,9 +681,15 @@ __device__ __forceinline__ void owner_loop_wide(Smem& sm, const S* xrow, const S
     turn_start();
     static_for<NS_TURN / 2>(step);
   }
-  if constexpr (!STATE_ONLY) {  // the last scanned tile has slot NS_PFO - 1, or NS_PFO / 2 - 1 after a half turn
-    read_partials((c.ntiles - 1) & 1);
-    if (c.ntiles % NS_PFO == 0)
+  if constexpr (!STATE_ONLY) {  // the last two scanned tiles: slots 6, 7, or 2, 3 after a half turn
+    const bool whole = c.ntiles % NS_PFO == 0;
+    read_partials((c.ntiles - 2) % NS_PB);
+    if (whole)
+      finish_tile(std::integral_constant<int, NS_PFO - 2>{}, c.t_begin + (c.ntiles - 2) * NS_T);
+    else
+      finish_tile(std::integral_constant<int, NS_PFO / 2 - 2>{}, c.t_begin + (c.ntiles - 2) * NS_T);
+    read_partials((c.ntiles - 1) % NS_PB);
+    if (whole)
       finish_tile(std::integral_constant<int, NS_PFO - 1>{}, c.t_begin + (c.ntiles - 1) * NS_T);
     else
       finish_tile(std::integral_constant<int, NS_PFO / 2 - 1>{}, c.t_begin + (c.ntiles - 1) * NS_T);
@@ -758,8 +789,8 @@ __device__ __forceinline__ void scan_loop(Smem& sm, const S* Brow, const S* Crow
 
   auto scan_tile = [&](auto slot_c, auto buf_c, int32_t t0) {  // t0: the tile's first token
     constexpr int slot = decltype(slot_c)::value;
-    constexpr int buf = decltype(buf_c)::value;  // term buffer of this tile (tile % NS_EB)
-    constexpr int par = buf & 1;
+    constexpr int buf = decltype(buf_c)::value;  // term and partial buffer of this tile (tile % 4)
+    constexpr int par = buf & 1;                 // register set of this tile's terms
     float Blo[NLD], Bhi[NLD], Clo[NLD], Chi[NLD];
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
@@ -876,7 +907,7 @@ __device__ __forceinline__ void scan_loop(Smem& sm, const S* Brow, const S* Crow
           if constexpr (K >= 12) chunk(std::integral_constant<int, 2>{});
           if constexpr (K >= 16) chunk(std::integral_constant<int, 3>{});
         }
-        sm.P[par][j][c.w][c.lane] = acc;
+        sm.P[buf][j][c.w][c.lane] = acc;
       }
       // (No scheduling barrier between tokens: pinning each pair of tokens'
       // reads, arithmetic and writes together measured 6% slower than leaving
@@ -897,6 +928,7 @@ __device__ __forceinline__ void scan_loop(Smem& sm, const S* Brow, const S* Crow
   load_tile(I3{}, c.t_begin + 3 * NS_T);
   __syncthreads();
   read_terms(std::integral_constant<int, 0>{}, 0);
+  __syncthreads();  // tile 0's terms are in registers before the owners reuse buffer 0
   int32_t k0 = 0;
   auto turn_start = [&]() {
     if constexpr (WIN) {  // this turn loads tiles k0+4..k0+11
@@ -904,12 +936,15 @@ __device__ __forceinline__ void scan_loop(Smem& sm, const S* Brow, const S* Crow
       set_windows();
     }
   };
+  // a barrier after every second tile (k0 is a multiple of 8): the owners
+  // work three tiles ahead and finish two behind, so every buffer a tile
+  // touches is written and read on opposite sides of one
   auto step = [&](auto kc) {
     constexpr int kk = decltype(kc)::value;
     using Slot = std::integral_constant<int, kk % NS_PF>;
     scan_tile(Slot{}, std::integral_constant<int, kk % NS_EB>{}, c.t_begin + (k0 + kk) * NS_T);
     load_tile(Slot{}, c.t_begin + (k0 + kk + NS_PF) * NS_T);
-    __syncthreads();
+    if constexpr (kk % 2 == 1) __syncthreads();
   };
   for (; k0 + NS_TURN <= c.ntiles; k0 += NS_TURN) {
     turn_start();

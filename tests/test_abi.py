@@ -173,7 +173,7 @@ def test_plan_long_rows_stay_on_the_main_kernel():
     assert ssm.plan(big((1, 270_008, 4104, 16), 0)) == ("nsplit", 1)   # 4.43 GB fp32 row
     assert ssm.plan(big((1, 2**31 - 1025, 64, 16), 1)) == ("nsplit", 1)
     assert ssm.plan(big((1, 2**31 - 1024, 64, 16), 1)) == ("lane", 1)
-    lim = (2**31 - 1) // 288
+    lim = (2**31 - 1) // 320
     assert ssm.plan(big((1, 64, lim // 2, 16), 1)) == ("nsplit", 1)
     assert ssm.plan(big((1, 64, lim // 2 + 1, 16), 1)) == ("lane", 1)
     assert ssm.plan(big((1, 64, lim // 4, 16), 0)) == ("nsplit", 1)
