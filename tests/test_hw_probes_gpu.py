@@ -8,7 +8,10 @@ probes in tests/hw_probes/ (built by __graft_entry__.build()):
   takes a scalar (SGPR) or DPP-broadcast operand, costs the SIMD about twice
   a plain one; a transcendental about four times a multiply;
 - LDS reads of 16 bytes per lane move about twice the bytes of two-dword
-  reads, and writes move fewer bytes per ns than reads.
+  reads, and writes move fewer bytes per ns than reads;
+- a wave's plain FMA stream keeps its rate when the other wave of its SIMD
+  runs FMAs or transcendentals; a DPP-operand stream loses some of it to a
+  transcendental stream.
 
 Only relations with wide margins are asserted (the absolute rates depend on
 the clock under load); the measured table is printed.
@@ -63,3 +66,10 @@ def test_lds_widths():
     for w in (8, 16):
         assert r[("read_b128", w)] > 1.4 * r[("read_2x_b32", w)]
         assert r[("write_b128", w)] < r[("read_b128", w)]
+
+
+def test_wave_pairs_on_one_simd():
+    r = _run("wave_mix")
+    assert r[("fma_with_fma", 1)] < 1.1 * r[("fma_alone", 1)]
+    assert r[("fma_with_exp", 1)] < 1.1 * r[("fma_alone", 1)]
+    assert r[("dppfma_with_exp", 1)] > 1.04 * r[("dppfma_alone", 1)]
