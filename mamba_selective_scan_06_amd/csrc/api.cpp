@@ -376,10 +376,13 @@ struct SsdPlan {
 // pass over all but the last segment; it pays while every segment's workgroup
 // still finds a compute unit of its own, so the automatic choice takes the most
 // segments for which B H S fits the 256 compute units, with at least 4 chunks
-// per segment and at most 64 segments.  The state-only pass needs under half
-// the LDS, so two of its workgroups fit a compute unit: each segment before the
-// last is cut into m sub-segments, the most for which (S - 1) m B H fits 512
-// workgroups with m dividing the segment's chunks and at least 4 chunks each.
+// per segment and at most 64 segments.  Two of the state-only pass's
+// workgroups fit a compute unit (its LDS would allow three, its VGPRs do not):
+// each segment before the last is cut into m sub-segments, the most for which
+// (S - 1) m B H fits 768 workgroups with m dividing the segment's chunks and at
+// least 4 chunks each.  Past 512 they run as a second, shorter round, which
+// balances the compute units better than sub-segments twice as long (B1 L32768
+// H64 N128: 508 against 520 us per call).
 int ssd_plan(int64_t B, int64_t L, int64_t H, int64_t N, int32_t time_splits, SsdPlan* pl) {
   constexpr int64_t kComputeUnits = 256;
   const int64_t nch = (L + 63) / 64;
@@ -401,8 +404,8 @@ int ssd_plan(int64_t B, int64_t L, int64_t H, int64_t N, int32_t time_splits, Ss
   S = (nch + segc - 1) / segc;  // no empty segment
   if (S < 2) return SSM_OK;
   int64_t m = 1;
-  for (int64_t c = 2; c <= segc / 4 && c <= 2 * kComputeUnits; ++c)  // (bounds the products below)
-    if (segc % c == 0 && (S - 1) * c * B * H <= 2 * kComputeUnits) m = c;
+  for (int64_t c = 2; c <= segc / 4 && c <= 3 * kComputeUnits; ++c)  // (bounds the products below)
+    if (segc % c == 0 && (S - 1) * c * B * H <= 3 * kComputeUnits) m = c;
   int64_t bs, st, tmp;
   if (!mul_ok(B, (S - 1) * m, &bs) || !mul_ok(bs, H, &tmp) || !mul_ok(tmp, 64 * N * 4, &st)) return SSM_ERR_SHAPE;
   pl->splits = static_cast<int>(S);

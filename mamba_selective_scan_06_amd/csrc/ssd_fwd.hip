@@ -49,9 +49,10 @@
 // with la the sum of the run's log decays and S_run its end state from zero.
 // A state-only launch (no M, no C H^T, no y: per chunk only the scalars, B^T,
 // x o w and the state update) writes S_run and la for the sub-segments of SC
-// / m chunks that cover every segment but the last; it needs under half the
-// full kernel's LDS, so two of its workgroups share a compute unit, and the
-// planner picks m to fill them.  The full launch starts segment s from h0 and
+// / m chunks that cover every segment but the last; it needs about a third of
+// the full kernel's LDS (its VGPRs let two of its workgroups share a compute
+// unit), and the planner picks m for up to three workgroups per compute unit:
+// a second, shorter round balances the units better than longer sub-segments.  The full launch starts segment s from h0 and
 // folds the summaries of sub-segments 0 .. s m - 1 into it in order, then runs
 // the chunks as above.
 #include <type_traits>
@@ -166,16 +167,32 @@ struct alignas(16) SsdSmem {
   float4 xch[NW > 4 ? NW : 1][2][64];  // halves of C H^T handed to the slice's other wave
 };
 
-// The state-only pass's part of it (same names, same layouts).
+// The state-only pass's part of it (same names and layouts, but for B^T:
+// unpadded rows whose 16-byte chunks are swizzled, chunk c of row n stored at
+// chunk c ^ ((n / 2) mod 8), so that the 16 rows one MFMA operand read spans
+// still hit 64 distinct banks).  At N = 128 that is 50688 bytes.
 template <int N, int NW>
 struct alignas(16) SsdSmemState {
   static constexpr int NB = kSsdStageBufs<N>;
   uint16_t xw[2][kQ / 8][kP][8];
-  uint16_t bt[NB][N][kQ + kPad];
+  uint16_t bt[NB][N][kQ];
   float dl[NB][kQ];
   float cs[NB][kQ];
   float ww[NB][kQ];
 };
+
+// Element (n, s) of one B^T buffer: padded rows in the full pass, swizzled
+// 16-byte chunks in the state-only pass (a run of up to 8 elements starting at
+// a multiple of its length stays inside one chunk).
+template <bool SWZ, int W>
+__device__ __forceinline__ uint16_t* bt_at(uint16_t (*b)[W], int n, int s) {
+  if constexpr (SWZ) {
+    static_assert(W == kQ, "swizzled rows are unpadded");
+    return &b[n][(((s >> 3) ^ ((n >> 1) & 7)) << 3) | (s & 7)];
+  } else {
+    return &b[n][s];
+  }
+}
 
 struct KArgs {
   const uint16_t* x;
@@ -355,7 +372,7 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      uint16_t* dst = &sm.bt[cb][8 * bng + e][TPT * btq];
+      uint16_t* dst = bt_at<ST>(sm.bt[cb], 8 * bng + e, TPT * btq);
       if constexpr (TPT == 1) {
         *dst = static_cast<uint16_t>(elem(br[0], e));
       } else {
@@ -529,7 +546,7 @@ __global__ __launch_bounds__(64 * NW) void ssd_fwd_kernel(const KArgs a) {
         f32x4 sacc = {};
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 bb = lds8(&sm.bt[cb][16 * (k * NJK + j) + lr][32 * kk + 8 * lg]);
+          const bf16x8 bb = lds8(bt_at<ST>(sm.bt[cb], 16 * (k * NJK + j) + lr, 32 * kk + 8 * lg));
           sacc = mfma(bb, xh[kk], sacc);
           sacc = mfma(bb, xl[kk], sacc);
         }

@@ -82,10 +82,10 @@ def _summary_bytes(B, S, H, N, m=1):
 def test_time_split_plan_small_batch():
     """B*H = 64 heads leave 3/4 of 256 compute units idle: 4 segments of 128
     chunks, when the workspace holds their summaries.  The state-only pass
-    fits two workgroups per compute unit, so the 3 segments before the last
-    are cut in 2 sub-segments each (3 * 2 * 64 = 384 <= 512 workgroups)."""
+    fits three workgroups per compute unit, so the 3 segments before the last
+    are cut in 4 sub-segments each (3 * 4 * 64 = 768 <= 768 workgroups)."""
     shape = (1, 32768, 64, 64, 1, 128)
-    need = _summary_bytes(1, 4, 64, 128, m=2)
+    need = _summary_bytes(1, 4, 64, 128, m=4)
     assert _ws(_args(shape=shape)) == need
     assert _plan(_args(shape=shape)) == 1                                      # no workspace: one segment
     assert _plan(_args(shape=shape, workspace=FAR, workspace_bytes=need - 1)) == 1
@@ -124,11 +124,11 @@ def test_workspace_checked_on_host():
 
 
 def test_state_only_sub_segments():
-    """m: the largest divisor of the segment's chunks with (S - 1) m B H <= 512
+    """m: the largest divisor of the segment's chunks with (S - 1) m B H <= 768
     and at least 4 chunks per sub-segment."""
     # 48 chunks, 3 segments of 16: (3 - 1) m 2 <= 512 and m <= 4 -> m = 4
     assert _ws(_args(shape=(1, 64 * 48, 2, 64, 1, 64), time_splits=3)) == _summary_bytes(1, 3, 2, 64, m=4)
     # 60 chunks, 6 segments of 10: m <= 2 -> 2
     assert _ws(_args(shape=(1, 64 * 60, 2, 64, 1, 64), time_splits=6)) == _summary_bytes(1, 6, 2, 64, m=2)
-    # B H = 128: 2 automatic segments of 64 chunks, 1 * m * 128 <= 512 -> m = 4
+    # B H = 128: 2 automatic segments of 64 chunks, 1 * m * 128 <= 768 and m | 64 -> m = 4
     assert _ws(_args(shape=(2, 8192, 64, 64, 1, 128))) == _summary_bytes(2, 2, 64, 128, m=4)
