@@ -270,8 +270,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const S* row, const Win
 // ---- owner waves (4..7): per-token scalars, loads of x/delta/z, y -----------
 // Owner wave o handles the tokens j = 4i + o (i < NS_OWN) of every tile for all
 // 64 channels.  In the iteration that the scan waves spend on tile k, it
-// computes the shared terms of tile k+1 into the other LDS buffer and finishes
-// tile k-1 from the partial readouts the scan waves left there.
+// computes the shared terms of tile k+3 into that tile's LDS buffer and
+// finishes tile k-2 from the partial readouts the scan waves left there.
 template <typename S, int K, bool STATE_ONLY, bool STRUCT, bool GATE, bool ZOH, bool WIN>
 __device__ __forceinline__ void owner_loop(Smem& sm, const S* xrow, const S* dlrow, const S* zrow, S* yrow,
                                            const SegCtx& c, float& dsum) {
